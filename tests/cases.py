@@ -1,0 +1,118 @@
+"""Shared test scaffolding: seeded scenarios built on the CPU oracle.
+
+A scenario is a workload shape, its seeded factors, sequence lengths, page
+table, per-sequence Keys/Values and queries, and (optionally) the oracle's
+cache with every token written.  GPU tests upload the same host arrays.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+import oracle
+from workloads import synth
+from workloads.configs import BF16, F32, Workload
+
+
+def small(name: str, cfg_id: int, **kw) -> Workload:
+    base = dict(name=name, cfg_id=cfg_id, batch=2, n_q_heads=4, n_kv_heads=2, head_dim=16,
+                page_size=4, rank_v=4, rank_k=2, top_k=3, d_model=24, dtype=F32, ctx=37)
+    base.update(kw)
+    return Workload(**base)
+
+
+@dataclass
+class Scenario:
+    w: Workload
+    fac: synth.Factors
+    rows: List[int]                 # global sequence ids (generator keys) of the local rows
+    lengths: np.ndarray             # tokens per local row after the decode append
+    page_table: np.ndarray
+    num_pages: int
+    K: List[np.ndarray] = field(default_factory=list)   # per row [n][H_kv][d_h] storage dtype
+    V: List[np.ndarray] = field(default_factory=list)
+    q: Optional[np.ndarray] = None  # [rows][H_q][d_h]
+    d: Optional[oracle.Dims] = None
+    cache: Optional[oracle.Cache] = None
+    W_ofT: Optional[np.ndarray] = None
+
+    @property
+    def batch(self) -> int:
+        return len(self.rows)
+
+
+def make_scenario(w: Workload, seed: int = 0, rows: Optional[Sequence[int]] = None,
+                  lengths: Optional[Sequence[int]] = None, permuted: Optional[bool] = None,
+                  write: bool = True, upto_last: bool = False, fill=0) -> Scenario:
+    """Build inputs for `rows` (default: the whole batch).
+
+    With ``write`` the oracle cache holds every token (or all but the last when
+    ``upto_last``: the decode step then appends the last one).
+    """
+    fac = synth.make_factors(w, seed)
+    all_len = synth.make_lengths(w, seed)
+    rows = list(range(w.batch)) if rows is None else list(rows)
+    if lengths is None:
+        lengths = [int(all_len[r]) for r in rows]
+    lengths = np.asarray(lengths, np.int32)
+    pt, total = synth.make_page_table(w, lengths, seed, permuted)
+    sc = Scenario(w=w, fac=fac, rows=rows, lengths=lengths, page_table=pt, num_pages=total)
+    for r, n in zip(rows, lengths):
+        Kf, Vf = synth.make_sequence(w, fac, r, max(int(n), 1), seed)
+        sc.K.append(Kf[:n])
+        sc.V.append(Vf[:n])
+    qall = synth.make_queries(w, seed=seed)
+    sc.q = np.ascontiguousarray(qall[rows])
+    sc.d = oracle.Dims.of(w, batch=len(rows), num_pages=total)
+    if write:
+        sc.cache = oracle.Cache(sc.d, pt, fill)
+        for b, n in enumerate(lengths):
+            m = int(n) - 1 if upto_last else int(n)
+            if m > 0:
+                oracle.write(sc.d, fac, sc.cache, b, 0, sc.K[b][:m], sc.V[b][:m])
+        sc.W_ofT = oracle.fold(sc.d, fac.B, fac.W_O)
+    return sc
+
+
+def all_pages_selection(lengths: Sequence[int], n_kv: int, top_k: int, ps: int):
+    B = len(lengths)
+    sel = np.full((B, n_kv, top_k), -1, np.int32)
+    n_sel = np.zeros((B, n_kv), np.int32)
+    for b, n in enumerate(lengths):
+        npg = -(-int(n) // ps)
+        assert npg <= top_k
+        sel[b, :, :npg] = np.arange(npg)
+        n_sel[b, :] = npg
+    return sel, n_sel
+
+
+def to_f64(x: np.ndarray, dtype: int) -> np.ndarray:
+    return synth.storage_to_f64(x, dtype)
+
+
+def softmax(s: np.ndarray) -> np.ndarray:
+    m = np.max(s)
+    e = np.exp(s - m)
+    return e / e.sum()
+
+
+def brute_topk(scores: np.ndarray, k: int) -> List[int]:
+    """Indices of the k best scores, ties to the smaller index, ascending."""
+    order = sorted(range(len(scores)), key=lambda j: (-float(scores[j]), j))
+    return sorted(order[:k])
+
+
+def check_selection_valid(ref_scores: np.ndarray, chosen: Sequence[int], k: int, rtol: float):
+    """`chosen` is a top-k of ref_scores up to swaps of near-equal scores."""
+    chosen = list(chosen)
+    assert len(chosen) == k == len(set(chosen))
+    assert chosen == sorted(chosen)
+    if k == len(ref_scores) or k == 0:
+        return
+    rest = [j for j in range(len(ref_scores)) if j not in set(chosen)]
+    lo = min(float(ref_scores[j]) for j in chosen)
+    hi = max(float(ref_scores[j]) for j in rest)
+    assert lo >= hi - rtol * max(abs(lo), abs(hi), 1e-30), (lo, hi)
