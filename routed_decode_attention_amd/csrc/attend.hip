@@ -1,0 +1,366 @@
+// Gathered exact-QK split-K decode attention over the routed pages.
+//
+// The router keeps only the top-k pages per (sequence, KV head); their exact
+// Keys are read back to score q.k exactly, and the softmax weights sum the
+// stored Value latents (weekinpapers "BasisKV: Value Latents for
+// Communication and Key Routing", Abstract; kongchang article, coarse routing
+// then exact scoring; softmax(q.k / sqrt(d_h)) from machinelearning.ru
+// "KV-кэширование", "Математическая формализация").
+//
+// Work split: a (sequence, KV head) pair's selected pages are cut into
+// n_wsplit workgroup splits of ATTEND_WAVES waves; each wave owns
+// pages_per_wave consecutive selected pages and keeps an online softmax
+// (running max m, denominator l, latent accumulator) for every query head of
+// the group.  The waves of a workgroup merge through LDS; the workgroup that
+// finishes last for its pair merges every split and writes the normalised
+// latent (counter in the workspace, reset by that workgroup).
+//
+// bf16 storage, d_h in {64,128}, page 32/64, r in {16,32,48,64}: matrix-core
+// kernel.  Per 32-token chunk of a page, S = K.q^T runs as two 16x16x32 bf16
+// MFMAs per 32 dims with the page's tokens as rows and the group's query
+// heads as columns (q is the B operand, loaded once).  Row m of the two
+// tiles a=0,1 is token 32c + 8*(m/4) + 4a + m%4, so each lane ends up holding
+// 8 consecutive tokens (32c + 8*qd + 0..7) of one head: exactly the k-slice
+// it must supply for the transposed latent product Acc^T[r][h] +=
+// Z^T[r][t] . P^T[t][h], whose A operand is the channel-major latent page
+// loaded straight from HBM.  Every softmax statistic of head h then lives in
+// the lanes of column h, so rescaling needs no cross-lane traffic.
+// Everything else (fp32 storage, other shapes): a plain VALU kernel with the
+// same split and merge.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace bkv {
+
+namespace {
+
+constexpr float NEG_INF = -__builtin_huge_valf();
+
+struct WaveState {  // LDS image of one wave's online-softmax state
+  float m[ATTEND_WAVES][MAX_GROUP];
+  float l[ATTEND_WAVES][MAX_GROUP];
+  float acc[ATTEND_WAVES][MAX_GROUP][MAX_RANK];
+};
+
+// Merge the workgroup's waves into one partial; then, if this workgroup is the
+// last of its pair to finish, merge all partials into z_out.
+__device__ void finish_pair(const AttendArgs& a, WaveState& ws, int pair, int split) {
+  const int G = a.s.group, R = a.s.rank_v;
+  const int stride = R + 2;
+  const int tid = threadIdx.x;
+  __syncthreads();
+  float* part = a.partials + ((size_t)pair * a.n_wsplit + split) * G * stride;
+  const bool single = a.n_wsplit == 1;
+  const int b = pair / a.s.n_kv_heads, g = pair % a.s.n_kv_heads;
+  for (int o = tid; o < G * R; o += blockDim.x) {
+    const int h = o / R, r = o % R;
+    float M = NEG_INF;
+    for (int w = 0; w < ATTEND_WAVES; ++w) M = fmaxf(M, ws.m[w][h]);
+    float L = 0.f, A = 0.f;
+    if (M != NEG_INF) {
+      for (int w = 0; w < ATTEND_WAVES; ++w) {
+        const float e = exp2f(ws.m[w][h] - M);
+        L += e * ws.l[w][h];
+        A += e * ws.acc[w][h][r];
+      }
+    }
+    if (single) {
+      a.z_out[((size_t)b * a.s.n_q_heads + g * G + h) * R + r] = L > 0.f ? A / L : 0.f;
+    } else {
+      part[h * stride + 2 + r] = A;
+      if (r == 0) {
+        part[h * stride] = M;
+        part[h * stride + 1] = L;
+      }
+    }
+  }
+  if (single) return;
+
+  __shared__ int s_last;
+  __threadfence();  // release this thread's partial stores at device scope
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(&a.counters[pair], 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (unsigned)(a.n_wsplit - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();  // acquire the other workgroups' partials
+  const float* base = a.partials + (size_t)pair * a.n_wsplit * G * stride;
+  for (int o = tid; o < G * R; o += blockDim.x) {
+    const int h = o / R, r = o % R;
+    float M = NEG_INF;
+    for (int sp = 0; sp < a.n_wsplit; ++sp) M = fmaxf(M, base[((size_t)sp * G + h) * stride]);
+    float L = 0.f, A = 0.f;
+    if (M != NEG_INF) {
+      for (int sp = 0; sp < a.n_wsplit; ++sp) {
+        const float* p = base + ((size_t)sp * G + h) * stride;
+        const float e = exp2f(p[0] - M);
+        L += e * p[1];
+        A += e * p[2 + r];
+      }
+    }
+    a.z_out[((size_t)b * a.s.n_q_heads + g * G + h) * R + r] = L > 0.f ? A / L : 0.f;
+  }
+  if (tid == 0)
+    __hip_atomic_store(&a.counters[pair], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Zero the bf16 elements j of v whose index is >= valid (0 <= valid <= 8).
+__device__ __forceinline__ bf16x8 keep_first(bf16x8 v, int valid) {
+  u32x4 u = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t lo = (2 * e < valid) ? 0x0000ffffu : 0u;
+    const uint32_t hi = (2 * e + 1 < valid) ? 0xffff0000u : 0u;
+    u[e] &= (lo | hi);
+  }
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+template <int D, int PS, int R>
+__global__ __launch_bounds__(256) void attend_mfma_kernel(AttendArgs a) {
+  constexpr int KS = D / 32;   // 32-dim steps of q.k
+  constexpr int NC = PS / 32;  // 32-token chunks per page
+  constexpr int MT = R / 16;   // 16-channel tiles of the latent
+  __shared__ WaveState st;
+
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int pair = wg / a.n_wsplit, split = wg % a.n_wsplit;
+  const int H = a.s.n_kv_heads, G = a.s.group;
+  const int b = pair / H, g = pair % H;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, qd = lane >> 4;
+
+  const int seq_len = a.seq_lens[b];
+  const int nsel = seq_len > 0 ? a.n_sel[pair] : 0;
+  const int first = (split * ATTEND_WAVES + wave) * a.pages_per_wave;
+  const int last = min(first + a.pages_per_wave, nsel);
+
+  const uint16_t* Kp = static_cast<const uint16_t*>(a.K);
+  const uint16_t* Zp = static_cast<const uint16_t*>(a.Z);
+
+  bf16x8 qb[KS];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                         ((size_t)b * a.s.n_q_heads + g * G + (n < G ? n : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qb[s] = n < G ? load_bf16x8(qp + 8 * qd + 32 * s) : zero_bf16x8();
+  }
+
+  float m_run = NEG_INF, l_run = 0.f;
+  f32x4 acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int i = first; i < last; ++i) {
+    const int j = a.sel[(size_t)pair * a.s.top_k + i];
+    const int phys = a.page_table[(size_t)b * a.s.max_pages + j];
+    const int cnt = min(PS, seq_len - j * PS);
+    const uint16_t* kp = Kp + ((size_t)phys * H + g) * PS * D;
+    const uint16_t* zp = Zp + ((size_t)phys * H + g) * R * PS;
+
+    bf16x8 kf[NC][2][KS];
+    bf16x8 zf[NC][MT];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int tok = 32 * c + 8 * (n >> 2) + 4 * t2 + (n & 3);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kf[c][t2][s] = load_bf16x8(kp + tok * D + 8 * qd + 32 * s);
+      }
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) zf[c][t] = load_bf16x8(zp + (16 * t + n) * PS + 32 * c + 8 * qd);
+
+    float sv[NC][8];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c][t2][s], qb[s], s4, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[c][4 * t2 + e] = s4[e] * a.scale_log2;
+      }
+
+    if (cnt < PS) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int valid = min(max(cnt - (32 * c + 8 * qd), 0), 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e >= valid) sv[c][e] = NEG_INF;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) zf[c][t] = keep_first(zf[c][t], valid);
+      }
+    }
+
+    float mx = NEG_INF;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sv[c][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    if (m_new == NEG_INF) continue;  // nothing valid yet
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] *= alpha;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = bf16_to_f32(f32_to_bf16(exp2f(sv[c][e] - m_new)));
+        l_run += p[e];
+      }
+      const bf16x8 pb = pack_bf16x8(p);
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zf[c][t], pb, acc[t], 0, 0, 0);
+    }
+  }
+
+  // this wave's state into LDS: head n lives in lanes n, n+16, n+32, n+48
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (n < G) {
+    if (qd == 0) {
+      st.m[wave][n] = m_run;
+      st.l[wave][n] = l_run;
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st.acc[wave][n][16 * t + 4 * qd + e] = acc[t][e];
+  }
+  finish_pair(a, st, pair, split);
+}
+
+// Plain VALU kernel: one lane per token for q.k, one lane per latent channel
+// for the weighted sum.  Any storage dtype and any supported shape.
+template <typename T>
+__global__ __launch_bounds__(256) void attend_valu_kernel(AttendArgs a) {
+  __shared__ WaveState st;
+  __shared__ float s_q[MAX_GROUP][128];
+  __shared__ float s_p[ATTEND_WAVES][64];
+
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int pair = wg / a.n_wsplit, split = wg % a.n_wsplit;
+  const int H = a.s.n_kv_heads, G = a.s.group, D = a.s.head_dim, R = a.s.rank_v;
+  const int PS = a.s.page_size;
+  const int b = pair / H, g = pair % H;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const T* Kp = static_cast<const T*>(a.K);
+  const T* Zp = static_cast<const T*>(a.Z);
+  const T* qp = static_cast<const T*>(a.q);
+
+  for (int o = threadIdx.x; o < G * D; o += blockDim.x)
+    s_q[o / D][o % D] = ld_elem(qp, ((size_t)b * a.s.n_q_heads + g * G + o / D) * D + o % D);
+  __syncthreads();
+
+  const int seq_len = a.seq_lens[b];
+  const int nsel = seq_len > 0 ? a.n_sel[pair] : 0;
+  const int first = (split * ATTEND_WAVES + wave) * a.pages_per_wave;
+  const int last = min(first + a.pages_per_wave, nsel);
+
+  float m_run[MAX_GROUP], l_run[MAX_GROUP], acc[MAX_GROUP];
+  for (int h = 0; h < MAX_GROUP; ++h) {
+    m_run[h] = NEG_INF;
+    l_run[h] = 0.f;
+    acc[h] = 0.f;
+  }
+  for (int i = first; i < last; ++i) {
+    const int j = a.sel[(size_t)pair * a.s.top_k + i];
+    const int phys = a.page_table[(size_t)b * a.s.max_pages + j];
+    const int cnt = min(PS, seq_len - j * PS);
+    const size_t kbase = ((size_t)phys * H + g) * PS * D;
+    const size_t zbase = ((size_t)phys * H + g) * R * PS;
+    for (int h = 0; h < G; ++h) {
+      float s = NEG_INF;
+      if (lane < cnt) {
+        float d = 0.f;
+        for (int x = 0; x < D; ++x) d += s_q[h][x] * ld_elem(Kp, kbase + (size_t)lane * D + x);
+        s = d * a.scale_log2;
+      }
+      const float mx = wave_max(s);
+      if (mx == NEG_INF) continue;
+      const float m_new = fmaxf(m_run[h], mx);
+      const float alpha = exp2f(m_run[h] - m_new);
+      const float p = lane < cnt ? exp2f(s - m_new) : 0.f;
+      l_run[h] = l_run[h] * alpha + wave_sum(p);
+      m_run[h] = m_new;
+      s_p[wave][lane] = p;
+      __builtin_amdgcn_wave_barrier();
+      float z = 0.f;
+      if (lane < R)
+        for (int t = 0; t < cnt; ++t) z += s_p[wave][t] * ld_elem(Zp, zbase + (size_t)lane * PS + t);
+      acc[h] = acc[h] * alpha + z;
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  for (int h = 0; h < G; ++h) {
+    if (lane == 0) {
+      st.m[wave][h] = m_run[h];
+      st.l[wave][h] = l_run[h];
+    }
+    if (lane < R) st.acc[wave][h][lane] = acc[h];
+  }
+  finish_pair(a, st, pair, split);
+}
+
+}  // namespace
+
+bool attend_mfma_supported(const Shape& s) {
+  return s.dtype == 1 && (s.head_dim == 64 || s.head_dim == 128) &&
+         (s.page_size == 32 || s.page_size == 64) && s.rank_v % 16 == 0 && s.rank_v <= 64 &&
+         s.group <= MAX_GROUP;
+}
+
+AttendPlan plan_attend(const Shape& s) {
+  // About 16 waves per CU over 256 CUs once every page unit is counted.
+  const long units = (long)s.batch * s.n_kv_heads * s.top_k;
+  int ppw = (int)((units + 4095) / 4096);
+  if (ppw < 1) ppw = 1;
+  if (ppw > 8) ppw = 8;
+  const char* env = getenv("BASISKV_PAGES_PER_WAVE");
+  if (env && atoi(env) > 0) ppw = atoi(env);
+  AttendPlan p;
+  p.pages_per_wave = ppw;
+  p.n_wsplit = (s.top_k + ATTEND_WAVES * ppw - 1) / (ATTEND_WAVES * ppw);
+  return p;
+}
+
+hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
+  const int pairs = a.s.batch * a.s.n_kv_heads;
+  const dim3 grid(pairs * a.n_wsplit), block(256);
+  if (attend_mfma_supported(a.s)) {
+    const int key = a.s.head_dim * 10000 + a.s.page_size * 100 + a.s.rank_v;
+    switch (key) {
+#define BKV_CASE(D, PS, R) \
+  case D * 10000 + PS * 100 + R: hipLaunchKernelGGL((attend_mfma_kernel<D, PS, R>), grid, block, 0, st, a); break;
+      BKV_CASE(128, 64, 16) BKV_CASE(128, 64, 32) BKV_CASE(128, 64, 48) BKV_CASE(128, 64, 64)
+      BKV_CASE(128, 32, 16) BKV_CASE(128, 32, 32) BKV_CASE(128, 32, 48) BKV_CASE(128, 32, 64)
+      BKV_CASE(64, 64, 16) BKV_CASE(64, 64, 32) BKV_CASE(64, 64, 48) BKV_CASE(64, 64, 64)
+      BKV_CASE(64, 32, 16) BKV_CASE(64, 32, 32) BKV_CASE(64, 32, 48) BKV_CASE(64, 32, 64)
+#undef BKV_CASE
+      default: return hipErrorInvalidValue;
+    }
+  } else if (a.s.dtype == 0) {
+    hipLaunchKernelGGL((attend_valu_kernel<float>), grid, block, 0, st, a);
+  } else {
+    hipLaunchKernelGGL((attend_valu_kernel<uint16_t>), grid, block, 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bkv

@@ -1,0 +1,359 @@
+// C-ABI host layer: argument validation, workspace planning and kernel
+// launches on the caller's stream.  The library keeps no device state; the
+// only global is the thread-local error text.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <cstdlib>
+
+#include "../../include/basiskv.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(BASISKV_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Validate dims and fill the kernels' shape.  Returns BASISKV_OK or an error.
+int check_dims(const basiskv_dims* d, bkv::Shape* s) {
+  if (!d) return fail(BASISKV_E_NULL, "dims is NULL");
+  if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->head_dim < 1 ||
+      d->rank_v < 1 || d->rank_k < 1 || d->page_size < 1 || d->d_model < 1 || d->top_k < 1 ||
+      d->max_pages_per_seq < 1 || d->num_phys_pages < 1)
+    return fail(BASISKV_E_DIMS, "every dimension must be positive");
+  if (d->n_q_heads % d->n_kv_heads != 0)
+    return fail(BASISKV_E_DIMS, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", d->n_q_heads,
+                d->n_kv_heads);
+  if (d->rank_v > d->head_dim || d->rank_k > d->head_dim)
+    return fail(BASISKV_E_DIMS, "ranks must not exceed head_dim");
+  if (d->top_k > d->max_pages_per_seq)
+    return fail(BASISKV_E_DIMS, "top_k (%d) exceeds max_pages_per_seq (%d)", d->top_k,
+                d->max_pages_per_seq);
+  if (d->dtype != BASISKV_F32 && d->dtype != BASISKV_BF16)
+    return fail(BASISKV_E_DIMS, "unknown dtype %d", d->dtype);
+  if (!(d->softmax_scale >= 0.f) || !isfinite(d->softmax_scale))
+    return fail(BASISKV_E_DIMS, "softmax_scale must be finite and >= 0");
+  const int group = d->n_q_heads / d->n_kv_heads;
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(BASISKV_E_UNSUPPORTED, "head_dim %d (supported: 64, 128)", d->head_dim);
+  if (d->page_size != 16 && d->page_size != 32 && d->page_size != 64)
+    return fail(BASISKV_E_UNSUPPORTED, "page_size %d (supported: 16, 32, 64)", d->page_size);
+  if (d->rank_v % 16 != 0 || d->rank_v > bkv::MAX_RANK)
+    return fail(BASISKV_E_UNSUPPORTED, "rank_v %d (multiple of 16, at most 64)", d->rank_v);
+  if (d->rank_k % 4 != 0 || d->rank_k > bkv::MAX_RESID)
+    return fail(BASISKV_E_UNSUPPORTED, "rank_k %d (multiple of 4, at most 64)", d->rank_k);
+  if (group > bkv::MAX_GROUP)
+    return fail(BASISKV_E_UNSUPPORTED, "%d query heads per KV head (at most 16)", group);
+  if (d->max_pages_per_seq > bkv::MAX_PAGES)
+    return fail(BASISKV_E_UNSUPPORTED, "max_pages_per_seq %d (at most %d)", d->max_pages_per_seq,
+                bkv::MAX_PAGES);
+  s->batch = d->batch;
+  s->n_q_heads = d->n_q_heads;
+  s->n_kv_heads = d->n_kv_heads;
+  s->group = group;
+  s->head_dim = d->head_dim;
+  s->rank_v = d->rank_v;
+  s->rank_k = d->rank_k;
+  s->page_size = d->page_size;
+  s->d_model = d->d_model;
+  s->top_k = d->top_k;
+  s->max_pages = d->max_pages_per_seq;
+  s->num_pages = d->num_phys_pages;
+  s->dtype = d->dtype;
+  s->scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf((float)d->head_dim);
+  return BASISKV_OK;
+}
+
+struct WsLayout {
+  size_t route_cnt, attend_cnt, partials, z, total;
+};
+
+WsLayout ws_layout(const bkv::Shape& s, int max_prefill_tokens) {
+  const size_t pairs = (size_t)s.batch * s.n_kv_heads;
+  const bkv::AttendPlan p = bkv::plan_attend(s);
+  WsLayout L;
+  L.route_cnt = 0;
+  L.attend_cnt = pairs * sizeof(unsigned);
+  L.partials = align256(2 * pairs * sizeof(unsigned));
+  const size_t part_bytes = pairs * p.n_wsplit * s.group * (s.rank_v + 2) * sizeof(float);
+  L.z = L.partials + align256(part_bytes);
+  size_t rows = (size_t)s.batch;
+  if (max_prefill_tokens > 0 && (size_t)max_prefill_tokens > rows) rows = max_prefill_tokens;
+  L.total = L.z + align256(rows * s.n_q_heads * s.rank_v * sizeof(float));
+  return L;
+}
+
+int check_cache(const basiskv_cache* c, bool needs_k, bool needs_z, bool needs_s) {
+  if (!c) return fail(BASISKV_E_NULL, "cache is NULL");
+  if (!c->page_table || !c->summ || (needs_k && !c->K) || (needs_z && !c->Z) || (needs_s && !c->S))
+    return fail(BASISKV_E_NULL, "a cache pointer is NULL");
+  return BASISKV_OK;
+}
+
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int do_attend(const bkv::Shape& s, const basiskv_cache* cache, const int32_t* seq_lens, const void* q,
+              const int32_t* sel, const int32_t* n_sel, void* ws, size_t ws_bytes, float* z_out,
+              void* stream) {
+  const WsLayout L = ws_layout(s, 0);
+  if (ws_bytes < L.partials + (L.z - L.partials))
+    return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, attention needs %zu", ws_bytes,
+                L.z);
+  bkv::AttendArgs a;
+  a.s = s;
+  a.K = cache->K;
+  a.Z = cache->Z;
+  a.page_table = cache->page_table;
+  a.seq_lens = seq_lens;
+  a.q = q;
+  a.sel = sel;
+  a.n_sel = n_sel;
+  char* w = static_cast<char*>(ws);
+  a.partials = reinterpret_cast<float*>(w + L.partials);
+  a.counters = reinterpret_cast<unsigned*>(w + L.attend_cnt);
+  a.z_out = z_out;
+  const bkv::AttendPlan p = bkv::plan_attend(s);
+  a.n_wsplit = p.n_wsplit;
+  a.pages_per_wave = p.pages_per_wave;
+  a.scale_log2 = s.scale * 1.4426950408889634f;
+  const hipError_t e = bkv::launch_attend(a, as_stream(stream));
+  return e == hipSuccess ? BASISKV_OK : hip_fail(e, "attention launch");
+}
+
+int do_project(const bkv::Shape& s, const basiskv_factors* f, const float* z, int rows, float* out,
+               void* stream) {
+  bkv::ProjectArgs a;
+  a.z = z;
+  a.W = f->W_ofT;
+  a.out = out;
+  a.rows = rows;
+  a.kdim = s.n_q_heads * s.rank_v;
+  a.n = s.d_model;
+  a.dtype = s.dtype;
+  const hipError_t e = bkv::launch_project(a, as_stream(stream));
+  return e == hipSuccess ? BASISKV_OK : hip_fail(e, "projection launch");
+}
+
+int do_write(const bkv::Shape& s, const basiskv_factors* f, const basiskv_cache* c, const int32_t* pos,
+             int seq, int start, int n_tok, const void* k, const void* v, void* stream) {
+  bkv::WriteArgs a;
+  a.s = s;
+  a.B = f->B;
+  a.P = f->P;
+  a.R_enc = f->R_enc;
+  a.K = c->K;
+  a.Z = c->Z;
+  a.S = c->S;
+  a.summ = c->summ;
+  a.page_table = c->page_table;
+  a.k = k;
+  a.v = v;
+  a.pos = pos;
+  a.seq = seq;
+  a.start = start;
+  a.n_tok = n_tok;
+  const hipError_t e = bkv::launch_write(a, as_stream(stream));
+  return e == hipSuccess ? BASISKV_OK : hip_fail(e, "writer launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int basiskv_version(void) { return BASISKV_VERSION; }
+
+const char* basiskv_strerror(int code) {
+  switch (code) {
+    case BASISKV_OK: return "ok";
+    case BASISKV_E_NULL: return "a required pointer is NULL";
+    case BASISKV_E_DIMS: return "inconsistent or non-positive dimensions";
+    case BASISKV_E_UNSUPPORTED: return "shape not supported by the kernels";
+    case BASISKV_E_WORKSPACE: return "workspace too small";
+    case BASISKV_E_HIP: return "HIP error";
+    case BASISKV_E_DATA: return "invalid device data";
+    default: return "unknown error";
+  }
+}
+
+const char* basiskv_last_error(void) { return g_err; }
+
+int basiskv_fold_output(const basiskv_dims* dims, const float* B, const void* W_O, void* W_ofT,
+                        void* stream) {
+  bkv::Shape s;
+  int rc = check_dims(dims, &s);
+  if (rc) return rc;
+  if (!B || !W_O || !W_ofT) return fail(BASISKV_E_NULL, "fold: B, W_O and W_ofT are required");
+  const hipError_t e = bkv::launch_fold(s, B, W_O, W_ofT, as_stream(stream));
+  return e == hipSuccess ? BASISKV_OK : hip_fail(e, "fold launch");
+}
+
+int basiskv_write(const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
+                  int32_t seq, int32_t start, int32_t n_tok, const void* k, const void* v,
+                  void* stream) {
+  bkv::Shape s;
+  int rc = check_dims(dims, &s);
+  if (rc) return rc;
+  if (!f || !f->B || !f->P || !f->R_enc) return fail(BASISKV_E_NULL, "write: factors B, P, R_enc required");
+  if ((rc = check_cache(cache, true, true, true))) return rc;
+  if (n_tok < 0 || start < 0 || seq < 0 || seq >= s.batch)
+    return fail(BASISKV_E_DIMS, "write: seq %d, start %d, n_tok %d out of range", seq, start, n_tok);
+  if (n_tok == 0) return BASISKV_OK;
+  if (!k || !v) return fail(BASISKV_E_NULL, "write: k and v are required");
+  if ((int64_t)start + n_tok > (int64_t)s.max_pages * s.page_size)
+    return fail(BASISKV_E_DIMS, "write: tokens beyond max_pages_per_seq * page_size");
+  return do_write(s, f, cache, nullptr, seq, start, n_tok, k, v, stream);
+}
+
+int basiskv_append(const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
+                   const int32_t* pos, const void* k_new, const void* v_new, void* stream) {
+  bkv::Shape s;
+  int rc = check_dims(dims, &s);
+  if (rc) return rc;
+  if (!f || !f->B || !f->P || !f->R_enc) return fail(BASISKV_E_NULL, "append: factors B, P, R_enc required");
+  if ((rc = check_cache(cache, true, true, true))) return rc;
+  if (!pos || !k_new || !v_new) return fail(BASISKV_E_NULL, "append: pos, k_new and v_new are required");
+  return do_write(s, f, cache, pos, 0, 0, 1, k_new, v_new, stream);
+}
+
+int basiskv_route(const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
+                  const int32_t* seq_lens, const void* q, void* ws, size_t ws_bytes, int32_t* sel,
+                  int32_t* n_sel, float* scores, void* stream) {
+  bkv::Shape s;
+  int rc = check_dims(dims, &s);
+  if (rc) return rc;
+  if (!f || !f->P || !f->R_dec) return fail(BASISKV_E_NULL, "route: factors P and R_dec required");
+  if ((rc = check_cache(cache, false, false, false))) return rc;
+  if (!seq_lens || !q || !ws || !sel || !n_sel || !scores)
+    return fail(BASISKV_E_NULL, "route: seq_lens, q, ws, sel, n_sel and scores are required");
+  const WsLayout L = ws_layout(s, 0);
+  if (ws_bytes < L.partials)
+    return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, routing needs %zu", ws_bytes, L.partials);
+  bkv::RouteArgs a;
+  a.s = s;
+  a.P = f->P;
+  a.R_dec = f->R_dec;
+  a.summ = cache->summ;
+  a.page_table = cache->page_table;
+  a.seq_lens = seq_lens;
+  a.q = q;
+  a.sel = sel;
+  a.n_sel = n_sel;
+  a.scores = scores;
+  a.counters = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + L.route_cnt);
+  a.pages_per_wg = bkv::route_pages_per_wg(s);
+  a.n_chunks = (s.max_pages + a.pages_per_wg - 1) / a.pages_per_wg;
+  const hipError_t e = bkv::launch_route(a, as_stream(stream));
+  return e == hipSuccess ? BASISKV_OK : hip_fail(e, "route launch");
+}
+
+size_t basiskv_workspace_bytes(const basiskv_dims* dims, int32_t max_prefill_tokens) {
+  bkv::Shape s;
+  if (check_dims(dims, &s)) return 0;
+  return ws_layout(s, max_prefill_tokens).total;
+}
+
+int basiskv_workspace_init(const basiskv_dims* dims, void* ws, size_t ws_bytes, void* stream) {
+  bkv::Shape s;
+  int rc = check_dims(dims, &s);
+  if (rc) return rc;
+  if (!ws) return fail(BASISKV_E_NULL, "workspace is NULL");
+  const WsLayout L = ws_layout(s, 0);
+  if (ws_bytes < L.partials) return fail(BASISKV_E_WORKSPACE, "workspace too small for its counters");
+  const hipError_t e = bkv::launch_zero_u32(static_cast<unsigned*>(ws), L.partials / sizeof(unsigned),
+                                            as_stream(stream));
+  return e == hipSuccess ? BASISKV_OK : hip_fail(e, "workspace init");
+}
+
+int basiskv_attend(const basiskv_dims* dims, const basiskv_cache* cache, const int32_t* seq_lens,
+                   const void* q, const int32_t* sel, const int32_t* n_sel, void* ws, size_t ws_bytes,
+                   float* z_out, void* stream) {
+  bkv::Shape s;
+  int rc = check_dims(dims, &s);
+  if (rc) return rc;
+  if ((rc = check_cache(cache, true, true, false))) return rc;
+  if (!seq_lens || !q || !sel || !n_sel || !ws || !z_out)
+    return fail(BASISKV_E_NULL, "attend: seq_lens, q, sel, n_sel, ws and z_out are required");
+  return do_attend(s, cache, seq_lens, q, sel, n_sel, ws, ws_bytes, z_out, stream);
+}
+
+int basiskv_project(const basiskv_dims* dims, const basiskv_factors* f, const float* z, int32_t rows,
+                    float* out, void* stream) {
+  bkv::Shape s;
+  int rc = check_dims(dims, &s);
+  if (rc) return rc;
+  if (rows < 0) return fail(BASISKV_E_DIMS, "project: rows %d", rows);
+  if (!f || !f->W_ofT || !z || !out) return fail(BASISKV_E_NULL, "project: W_ofT, z and out are required");
+  return do_project(s, f, z, rows, out, stream);
+}
+
+int basiskv_decode(const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
+                   const int32_t* seq_lens, const void* q, const int32_t* sel, const int32_t* n_sel,
+                   void* ws, size_t ws_bytes, float* z_out, float* out, void* stream) {
+  bkv::Shape s;
+  int rc = check_dims(dims, &s);
+  if (rc) return rc;
+  if ((rc = check_cache(cache, true, true, false))) return rc;
+  if (!f || !f->W_ofT) return fail(BASISKV_E_NULL, "decode: W_ofT is required");
+  if (!seq_lens || !q || !sel || !n_sel || !ws || !out)
+    return fail(BASISKV_E_NULL, "decode: seq_lens, q, sel, n_sel, ws and out are required");
+  const WsLayout L = ws_layout(s, 0);
+  if (ws_bytes < L.total)
+    return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, decode needs %zu", ws_bytes, L.total);
+  float* z = z_out ? z_out : reinterpret_cast<float*>(static_cast<char*>(ws) + L.z);
+  if ((rc = do_attend(s, cache, seq_lens, q, sel, n_sel, ws, ws_bytes, z, stream))) return rc;
+  return do_project(s, f, z, s.batch, out, stream);
+}
+
+int basiskv_prefill(const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
+                    int32_t seq, int32_t start_pos, int32_t n_tok, const void* q, const void* k,
+                    const void* v, void* ws, size_t ws_bytes, float* z_out, float* out, void* stream) {
+  bkv::Shape s;
+  int rc = check_dims(dims, &s);
+  if (rc) return rc;
+  if (!f || !f->B || !f->P || !f->R_enc || !f->W_ofT)
+    return fail(BASISKV_E_NULL, "prefill: factors B, P, R_enc and W_ofT are required");
+  if ((rc = check_cache(cache, true, true, true))) return rc;
+  if (n_tok < 0 || start_pos < 0 || seq < 0 || seq >= s.batch)
+    return fail(BASISKV_E_DIMS, "prefill: seq %d, start %d, n_tok %d out of range", seq, start_pos, n_tok);
+  if ((int64_t)start_pos + n_tok > (int64_t)s.max_pages * s.page_size)
+    return fail(BASISKV_E_DIMS, "prefill: tokens beyond max_pages_per_seq * page_size");
+  if (n_tok == 0) return BASISKV_OK;
+  if (!q || !k || !v || !out || !ws) return fail(BASISKV_E_NULL, "prefill: q, k, v, ws and out are required");
+  const WsLayout L = ws_layout(s, n_tok);
+  if (ws_bytes < L.total)
+    return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, a %d-token prefill needs %zu", ws_bytes,
+                n_tok, L.total);
+  if ((rc = do_write(s, f, cache, nullptr, seq, start_pos, n_tok, k, v, stream))) return rc;
+  float* z = z_out ? z_out : reinterpret_cast<float*>(static_cast<char*>(ws) + L.z);
+  bkv::PrefillArgs a;
+  a.s = s;
+  a.K = cache->K;
+  a.Z = cache->Z;
+  a.page_table = cache->page_table;
+  a.q = q;
+  a.z_out = z;
+  a.seq = seq;
+  a.start = start_pos;
+  a.n_tok = n_tok;
+  a.scale_log2 = s.scale * 1.4426950408889634f;
+  const hipError_t e = bkv::launch_prefill_attend(a, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+  return do_project(s, f, z, n_tok, out, stream);
+}
+
+}  // extern "C"

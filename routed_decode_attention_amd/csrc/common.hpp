@@ -1,0 +1,114 @@
+// Device helpers shared by the gfx950 kernels of the routed latent decode library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bkv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (quiet NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Two fp32 -> packed bf16 pair (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+// Storage element access: T is float (fp32 storage) or uint16_t (bf16 storage).
+__device__ __forceinline__ float ld_elem(const float* p, size_t i) { return p[i]; }
+__device__ __forceinline__ float ld_elem(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+__device__ __forceinline__ float round_store(float* p, size_t i, float x) {
+  p[i] = x;
+  return x;
+}
+__device__ __forceinline__ float round_store(uint16_t* p, size_t i, float x) {
+  uint16_t h = f32_to_bf16(x);
+  p[i] = h;
+  return bf16_to_f32(h);
+}
+__device__ __forceinline__ float round_only(float x, const float*) { return x; }
+__device__ __forceinline__ float round_only(float x, const uint16_t*) {
+  return bf16_to_f32(f32_to_bf16(x));
+}
+
+// 16-byte global load as an MFMA bf16x8 operand.
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
+  u32x4 v = *reinterpret_cast<const u32x4*>(p);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float (&x)[8]) {
+  u32x4 v;
+  v[0] = pack_bf16x2(x[0], x[1]);
+  v[1] = pack_bf16x2(x[2], x[3]);
+  v[2] = pack_bf16x2(x[4], x[5]);
+  v[3] = pack_bf16x2(x[6], x[7]);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  u32x4 v = {0u, 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & (WAVE - 1);
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) {
+    int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Order-preserving map of fp32 onto uint32 (larger float -> larger key);
+// -0 is folded onto +0 so that the two compare equal.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  if (f == 0.0f) f = 0.0f;
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Map a linear workgroup id so that consecutive "logical" ids owned by one
+// unit land on the same XCD: the hardware deals workgroups round-robin over
+// the 8 XCDs, so logical id L is placed at a physical id with the same
+// residue modulo 8 as its unit.  Only used when count % 8 == 0.
+__device__ __forceinline__ int xcd_remap(int phys, int count) {
+  if ((count & 7) != 0) return phys;
+  const int per = count >> 3;
+  return (phys & 7) * per + (phys >> 3);
+}
+
+}  // namespace bkv

@@ -1,0 +1,96 @@
+// Internal launch interface between the C-ABI host layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bkv {
+
+constexpr int MAX_GROUP = 16;      // query heads per KV head handled by one wave
+constexpr int MAX_RANK = 64;       // latent width bound
+constexpr int MAX_RESID = 64;      // residual width bound
+constexpr int MAX_PAGES = 8192;    // page-table columns the router's LDS holds
+constexpr int ATTEND_WAVES = 4;    // waves per attention workgroup
+
+struct Shape {
+  int batch, n_q_heads, n_kv_heads, group, head_dim, rank_v, rank_k, page_size;
+  int d_model, top_k, max_pages, num_pages, dtype;
+  float scale;
+};
+
+struct WriteArgs {
+  Shape s;
+  const float *B, *P, *R_enc;
+  void *K, *Z, *S;
+  float* summ;
+  const int32_t* page_table;
+  const void *k, *v;
+  // append mode: pos != nullptr, one token per row b at pos[b]
+  const int32_t* pos;
+  // chunk mode: row `seq`, tokens [start, start+n_tok)
+  int seq, start, n_tok;
+};
+
+struct RouteArgs {
+  Shape s;
+  const float *P, *R_dec;
+  const float* summ;
+  const int32_t *page_table, *seq_lens;
+  const void* q;
+  int32_t *sel, *n_sel;
+  float* scores;
+  unsigned* counters;       // [batch * n_kv_heads], zero on entry and exit
+  int pages_per_wg, n_chunks;
+};
+
+struct AttendArgs {
+  Shape s;
+  const void *K, *Z;
+  const int32_t *page_table, *seq_lens;
+  const void* q;
+  const int32_t *sel, *n_sel;
+  float* partials;          // [pairs][n_wsplit][group][rank_v + 2]
+  unsigned* counters;       // [pairs], zero on entry and exit
+  float* z_out;             // [batch][n_q_heads][rank_v]
+  int n_wsplit, pages_per_wave;
+  float scale_log2;         // softmax scale * log2(e)
+};
+
+struct ProjectArgs {
+  const float* z;           // [rows][kdim] fp32
+  const void* W;            // [n][kdim] dtype
+  float* out;               // [rows][n]
+  int rows, kdim, n, dtype;
+};
+
+struct PrefillArgs {
+  Shape s;
+  const void *K, *Z;
+  const int32_t* page_table;
+  const void* q;            // [n_tok][n_q_heads][head_dim]
+  float* z_out;             // [n_tok][n_q_heads][rank_v]
+  int seq, start, n_tok;
+  float scale_log2;
+};
+
+// Host-side planning shared by workspace sizing and launches.
+struct AttendPlan {
+  int pages_per_wave, n_wsplit;
+};
+AttendPlan plan_attend(const Shape& s);
+int route_pages_per_wg(const Shape& s);
+
+bool attend_mfma_supported(const Shape& s);
+bool project_mfma_supported(int kdim, int n, int dtype);
+bool prefill_mfma_supported(const Shape& s);
+
+hipError_t launch_fold(const Shape& s, const float* B, const void* W_O, void* W_ofT, hipStream_t st);
+hipError_t launch_write(const WriteArgs& a, hipStream_t st);
+hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
+hipError_t launch_project(const ProjectArgs& a, hipStream_t st);
+hipError_t launch_prefill_attend(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_zero_u32(unsigned* p, size_t n, hipStream_t st);
+
+}  // namespace bkv

@@ -1,0 +1,111 @@
+// Output projection through the folded weights: out = z . W_of, with W_of =
+// B^T.W_O (weekinpapers "BasisKV: Value Latents for Communication and Key
+// Routing", Abstract, observation (ii): Value compression associated with the
+// output projection; kongchang article, same section).  z is the attention
+// output still in latent space, [rows][n_q_heads*r]; W_ofT is stored
+// [d_model][n_q_heads*r], so both MFMA operands are contiguous along the
+// contraction and load straight from memory as 16-byte fragments.
+//
+// bf16: v_mfma_f32_16x16x32_bf16 with z rounded to bf16 on load and fp32
+// accumulation.  A wave computes WM x WN tiles of 16x16; a workgroup holds
+// WAVES_M x WAVES_N waves.  Decode batches use one 16-row tile per wave (the
+// rows are the batch), prefill chunks 64x64 per wave.
+// fp32 (or shapes the matrix cores do not tile): a VALU dot per output.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace bkv {
+
+namespace {
+
+template <int WM, int WN, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void project_mfma_kernel(ProjectArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, qd = lane >> 4;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int tiles_n = a.n / (16 * WN * WAVES_N);
+  const int bid = blockIdx.x;
+  const int row0 = (bid / tiles_n) * (16 * WM * WAVES_M) + wm * 16 * WM;
+  const int col0 = (bid % tiles_n) * (16 * WN * WAVES_N) + wn * 16 * WN;
+  const uint16_t* W = static_cast<const uint16_t*>(a.W);
+
+  f32x4 acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int k0 = 0; k0 < a.kdim; k0 += 32) {
+    bf16x8 af[WM], bfr[WN];
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      const int row = row0 + 16 * i + n;
+      if (row < a.rows) {
+        const float4* zp = reinterpret_cast<const float4*>(a.z + (size_t)row * a.kdim + k0 + 8 * qd);
+        const float4 x0 = zp[0], x1 = zp[1];
+        const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        af[i] = pack_bf16x8(x);
+      } else {
+        af[i] = zero_bf16x8();
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < WN; ++j)
+      bfr[j] = load_bf16x8(W + (size_t)(col0 + 16 * j + n) * a.kdim + k0 + 8 * qd);
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = row0 + 16 * i + 4 * qd + e;
+      if (row < a.rows) {
+#pragma unroll
+        for (int j = 0; j < WN; ++j) a.out[(size_t)row * a.n + col0 + 16 * j + n] = acc[i][j][e];
+      }
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void project_valu_kernel(ProjectArgs a) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int row = blockIdx.y;
+  if (c >= a.n) return;
+  const T* W = static_cast<const T*>(a.W);
+  const float* z = a.z + (size_t)row * a.kdim;
+  float acc = 0.f;
+  for (int x = 0; x < a.kdim; ++x) acc += z[x] * ld_elem(W, (size_t)c * a.kdim + x);
+  a.out[(size_t)row * a.n + c] = acc;
+}
+
+}  // namespace
+
+bool project_mfma_supported(int kdim, int n, int dtype) {
+  return dtype == 1 && kdim % 32 == 0 && n % 64 == 0;
+}
+
+hipError_t launch_project(const ProjectArgs& a, hipStream_t st) {
+  if (a.rows <= 0) return hipSuccess;
+  if (project_mfma_supported(a.kdim, a.n, a.dtype)) {
+    if (a.rows > 64 && a.n % 128 == 0) {
+      // 128x128 per workgroup (2x2 waves of 64x64)
+      const int grid = ((a.rows + 127) / 128) * (a.n / 128);
+      hipLaunchKernelGGL((project_mfma_kernel<4, 4, 2, 2>), dim3(grid), dim3(256), 0, st, a);
+    } else {
+      // 16 rows x 64 columns per workgroup (4 waves of 16x16)
+      const int grid = ((a.rows + 15) / 16) * (a.n / 64);
+      hipLaunchKernelGGL((project_mfma_kernel<1, 1, 1, 4>), dim3(grid), dim3(256), 0, st, a);
+    }
+  } else {
+    const dim3 grid((a.n + 255) / 256, a.rows);
+    if (a.dtype == 0) hipLaunchKernelGGL((project_valu_kernel<float>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((project_valu_kernel<uint16_t>), grid, dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bkv

@@ -1,0 +1,322 @@
+"""GPU parity: every entry point of the C-ABI library against the CPU oracle.
+
+Inputs are the seeded synthetic workloads (tests/cases.py); the oracle never
+receives anything the GPU produced.  Where a test wants identical cache
+contents, the oracle's cache is uploaded to the GPU.  Tolerances: selected
+page sets identical up to swaps of pages whose oracle fp32 scores differ by
+less than 1e-5 relative; outputs within rtol 2e-2 / atol 2e-3 for bf16
+storage (fp32 accumulation) and 1e-4 for fp32 storage.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import cases
+from tests.cases import small
+from workloads import configs, synth
+from workloads.configs import BF16, F32
+
+pytestmark = pytest.mark.gpu
+
+gc = None
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    global gc
+    assert torch.cuda.is_available(), "GPU parity tests need a GPU"
+    from tests import gpu_cases
+    gc = gpu_cases
+    oracle.build(force=False)
+
+
+# Shapes: the headline geometry (d_h 128, pages of 64, r 32, GQA 4:1) at short
+# contexts, wider groups with two KV heads and r 48 (pages of 32), head_dim
+# 64, fp32 storage, and bf16 pages of 16 (plain kernels).  Lengths mix
+# ragged tails, an exactly full page and a single token.
+CASES = {
+    "g4_d128_p64": (configs.get("llama8b_32k").with_(name="g4", cfg_id=201, batch=3, top_k=5,
+                                                     d_model=256), [700, 64, 130]),
+    "g8_2kv_r48_p32": (small("g8", 202, batch=2, n_q_heads=16, n_kv_heads=2, head_dim=128,
+                             page_size=32, rank_v=48, rank_k=16, top_k=7, d_model=192,
+                             dtype=BF16, ctx=513), [513, 200]),
+    "g1_d64": (small("g1", 203, batch=2, n_q_heads=2, n_kv_heads=2, head_dim=64, page_size=64,
+                     rank_v=16, rank_k=8, top_k=3, d_model=128, dtype=BF16, ctx=300), [300, 1]),
+    "tiny_f32": (configs.get("tiny_f32"), [1024]),
+    "f32_p16_g2": (small("f32g2", 204, batch=2, n_q_heads=2, n_kv_heads=1, head_dim=64,
+                         page_size=16, rank_v=16, rank_k=8, top_k=4, d_model=96, dtype=F32, ctx=100),
+                   [100, 33]),
+    "bf16_p16": (small("p16", 205, batch=2, n_q_heads=2, n_kv_heads=1, head_dim=64,
+                       page_size=16, rank_v=16, rank_k=8, top_k=4, d_model=64, dtype=BF16, ctx=100),
+                 [100, 33]),
+    "ragged_permuted": (configs.get("ragged_mix").with_(name="rg", cfg_id=206, batch=5,
+                                                        length_range=(1, 3000), top_k=16,
+                                                        d_model=256),
+                        None),
+}
+
+
+def scenario(name, **kw):
+    w, lengths = CASES[name]
+    return cases.make_scenario(w, lengths=lengths, **kw)
+
+
+def ulp_dist(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    def ordered(u):
+        u = u.astype(np.int64)
+        return np.where(u & 0x8000, -(u & 0x7FFF), u & 0x7FFF)
+    return np.abs(ordered(a) - ordered(b))
+
+
+def _valid_slots(sc):
+    """(page, slot) of every written token."""
+    out = []
+    ps = sc.w.page_size
+    for b, n in enumerate(sc.lengths):
+        for t in range(int(n)):
+            out.append((sc.page_table[b, t // ps], t % ps))
+    return out
+
+
+def compare_written(sc, got, ora):
+    """GPU-written cache against the oracle-written one."""
+    w = sc.w
+    slots = _valid_slots(sc)
+    P = np.array([p for p, _ in slots])
+    T = np.array([t for _, t in slots])
+    # exact Keys, bit for bit
+    assert np.array_equal(got["K"][P, :, T], ora.K[P, :, T])
+    gz, oz = got["Z"][P, :, :, T], ora.Z[P, :, :, T]     # [tokens][H][R]
+    gs, os_ = got["S"][P, :, T], ora.S[P, :, T]           # [tokens][H][RK]
+    if w.dtype == BF16:
+        dz = ulp_dist(gz, oz)
+        assert dz.max() <= 1, "latent more than 1 ulp from the oracle"
+        assert (dz > 0).mean() <= 2e-3
+        same = (dz == 0).all(axis=2)  # tokens whose whole latent matched
+        ds = ulp_dist(gs, os_)
+        assert ds[same].max(initial=0) <= 1
+        assert (ds[same] > 0).mean() <= 2e-3
+    else:
+        np.testing.assert_allclose(gz, oz, rtol=2e-6, atol=1e-6)
+        np.testing.assert_allclose(gs, os_, rtol=1e-5, atol=1e-5)
+    # page sums: the fp32 sum of the GPU's own stored values, in slot order
+    ps = w.page_size
+    R = w.rank_v
+    vz = synth.storage_to_f64(got["Z"], w.dtype)
+    vs = synth.storage_to_f64(got["S"], w.dtype)
+    for b, n in enumerate(sc.lengths):
+        for j in range(-(-int(n) // ps)):
+            p = sc.page_table[b, j]
+            cnt = min(ps, int(n) - j * ps)
+            for g in range(w.n_kv_heads):
+                x = np.concatenate([vz[p, g, :, :cnt].T, vs[p, g, :cnt, :]], axis=1)  # [cnt][R+RK]
+                ref = x.sum(axis=0)
+                bound = cnt * 2.0 ** -23 * np.abs(x).sum(axis=0) + 1e-30
+                assert np.all(np.abs(got["summ"][p, g] - ref) <= bound), (b, j, g)
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_fold_matches_oracle(name):
+    sc = scenario(name)
+    g = gc.upload(sc, cache=True)
+    got = gc.host(g.f.W_ofT)
+    if sc.w.dtype == BF16:
+        d = ulp_dist(got, sc.W_ofT)
+        assert d.max() <= 1 and (d > 0).mean() <= 2e-3
+    else:
+        np.testing.assert_allclose(got, sc.W_ofT, rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_writer_matches_oracle(name):
+    sc = scenario(name)
+    g = gc.upload(sc)
+    gc.write_all(g, sc, chunk=97)  # chunks straddle page boundaries
+    torch.cuda.synchronize()
+    compare_written(sc, gc.cache_host(g), sc.cache)
+
+
+@pytest.mark.parametrize("name", ["g4_d128_p64", "tiny_f32", "ragged_permuted"])
+def test_appends_equal_one_chunk_write(name):
+    sc = scenario(name)
+    a = gc.upload(sc)
+    gc.write_all(a, sc)
+    b = gc.upload(sc)
+    gc.write_all(b, sc, upto_last=True, chunk=50)
+    gc.append_last(b, sc)
+    gc.append_last(b, sc)  # rewriting the same position is idempotent
+    torch.cuda.synchronize()
+    ca, cb = gc.cache_host(a), gc.cache_host(b)
+    for k in ca:
+        assert np.array_equal(ca[k], cb[k]), k
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_route_matches_oracle(name):
+    sc = scenario(name)
+    sel, n_sel, scores = oracle.route(sc.d, sc.fac, sc.cache, sc.lengths, sc.q)
+    g = gc.upload(sc, cache=True)
+    gs, gn, gscores = gc.route(g)
+    assert np.array_equal(gn, n_sel)
+    for b, n in enumerate(sc.lengths):
+        npg = -(-int(n) // sc.w.page_size)
+        for h in range(sc.w.n_kv_heads):
+            k = int(n_sel[b, h])
+            np.testing.assert_allclose(gscores[b, h, :npg], scores[b, h, :npg], rtol=1e-5,
+                                       atol=1e-5 * max(1.0, float(np.abs(scores[b, h, :npg]).max(initial=0))))
+            cases.check_selection_valid(scores[b, h, :npg], gs[b, h, :k], k, 1e-5)
+            assert (gs[b, h, k:] == -1).all()
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_decode_matches_oracle(name):
+    sc = scenario(name)
+    sel, n_sel, _ = oracle.route(sc.d, sc.fac, sc.cache, sc.lengths, sc.q)
+    z_ref, out_ref = oracle.decode(sc.d, sc.W_ofT, sc.cache, sc.lengths, sc.q, sel, n_sel)
+    g = gc.upload(sc, cache=True, W_ofT=sc.W_ofT)
+    z, out = gc.decode(g, sel, n_sel)
+    rtol, atol = gc.tol(sc.w)
+    np.testing.assert_allclose(z, z_ref, rtol=rtol, atol=atol)
+    np.testing.assert_allclose(out, out_ref, rtol=rtol, atol=atol)
+
+
+@pytest.mark.parametrize("name", ["g4_d128_p64", "g8_2kv_r48_p32", "ragged_permuted"])
+def test_decode_with_every_page_selected(name):
+    w, lengths = CASES[name]
+    w = w.with_(top_k=w.max_pages_per_seq)
+    sc = cases.make_scenario(w, lengths=lengths)
+    sel, n_sel = cases.all_pages_selection(sc.lengths, w.n_kv_heads, w.top_k, w.page_size)
+    z_ref, out_ref = oracle.decode(sc.d, sc.W_ofT, sc.cache, sc.lengths, sc.q, sel, n_sel)
+    g = gc.upload(sc, cache=True, W_ofT=sc.W_ofT)
+    z, out = gc.decode(g, sel, n_sel)
+    rtol, atol = gc.tol(w)
+    np.testing.assert_allclose(z, z_ref, rtol=rtol, atol=atol)
+    np.testing.assert_allclose(out, out_ref, rtol=rtol, atol=atol)
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_decode_step_end_to_end(name):
+    """GPU writer + append + route + decode against the oracle's whole step."""
+    sc = scenario(name)
+    sel, n_sel, scores = oracle.route(sc.d, sc.fac, sc.cache, sc.lengths, sc.q)
+    z_ref, out_ref = oracle.decode(sc.d, sc.W_ofT, sc.cache, sc.lengths, sc.q, sel, n_sel)
+    g = gc.upload(sc)
+    gc.write_all(g, sc, upto_last=True, chunk=1000)
+    gc.append_last(g, sc)
+    gs, gn, _ = gc.route(g)
+    z, out = gc.decode(g, gs, gn)
+    rtol, atol = gc.tol(sc.w)
+    for b in range(sc.batch):
+        same = True
+        for h in range(sc.w.n_kv_heads):
+            k = int(n_sel[b, h])
+            cases.check_selection_valid(scores[b, h, :-(-int(sc.lengths[b]) // sc.w.page_size)],
+                                        gs[b, h, :k], k, 1e-5)
+            same &= np.array_equal(gs[b, h], sel[b, h])
+        if same:  # near-tie swaps change the softmax domain; compared via the decode test then
+            np.testing.assert_allclose(out[b], out_ref[b], rtol=rtol, atol=atol)
+            np.testing.assert_allclose(z[b], z_ref[b], rtol=rtol, atol=atol)
+
+
+def _permuted(sc, seed):
+    pt2 = synth.permute_pool(sc.page_table, sc.num_pages, seed)
+    c2 = oracle.Cache(sc.d, pt2)
+    for b in range(sc.page_table.shape[0]):
+        for j in range(sc.page_table.shape[1]):
+            p, p2 = sc.page_table[b, j], pt2[b, j]
+            if p >= 0:
+                c2.K[p2], c2.Z[p2], c2.S[p2], c2.summ[p2] = sc.cache.K[p], sc.cache.Z[p], \
+                    sc.cache.S[p], sc.cache.summ[p]
+    return pt2, c2
+
+
+@pytest.mark.parametrize("name", ["g4_d128_p64", "g8_2kv_r48_p32", "tiny_f32"])
+def test_page_permutation_bit_identical(name):
+    sc = scenario(name)
+    g1 = gc.upload(sc, cache=True, W_ofT=sc.W_ofT)
+    s1 = gc.route(g1)
+    o1 = gc.decode(g1, s1[0], s1[1])
+    pt2, c2 = _permuted(sc, 11)
+    sc.page_table, sc.cache = pt2, c2
+    g2 = gc.upload(sc, cache=True, W_ofT=sc.W_ofT)
+    s2 = gc.route(g2)
+    o2 = gc.decode(g2, s2[0], s2[1])
+    for a, b in zip(s1[:2], s2[:2]):
+        assert np.array_equal(a, b)
+    for a, b in zip(o1, o2):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["g4_d128_p64", "g8_2kv_r48_p32", "bf16_p16", "tiny_f32"])
+def test_poisoned_unused_slots(name):
+    w = CASES[name][0]
+    poison = np.float32(np.nan) if w.dtype == F32 else np.uint16(0x7FC0)
+    clean = scenario(name)
+    dirty = scenario(name, fill=poison)
+    dirty.cache.summ[...] = np.where(clean.cache.summ == 0, np.nan, dirty.cache.summ)
+    r = []
+    for sc in (clean, dirty):
+        g = gc.upload(sc, cache=True, W_ofT=clean.W_ofT)
+        s = gc.route(g)
+        r.append((s, gc.decode(g, s[0], s[1])))
+    assert np.array_equal(r[0][0][0], r[1][0][0])
+    assert np.all(np.isfinite(r[1][1][1]))
+    assert np.array_equal(r[0][1][1], r[1][1][1])
+
+
+def test_run_to_run_deterministic():
+    sc = scenario("g8_2kv_r48_p32")
+    g = gc.upload(sc, cache=True)
+    a = gc.route(g)
+    oa = gc.decode(g, a[0], a[1])
+    for _ in range(3):
+        b = gc.route(g)
+        ob = gc.decode(g, b[0], b[1])
+        assert all(np.array_equal(x, y) for x, y in zip(a, b))
+        assert all(np.array_equal(x, y) for x, y in zip(oa, ob))
+
+
+def test_empty_and_single_token_sequences():
+    w, _ = CASES["g4_d128_p64"]
+    sc = cases.make_scenario(w, lengths=[0, 1, 65])
+    sel, n_sel, _ = oracle.route(sc.d, sc.fac, sc.cache, sc.lengths, sc.q)
+    z_ref, out_ref = oracle.decode(sc.d, sc.W_ofT, sc.cache, sc.lengths, sc.q, sel, n_sel)
+    g = gc.upload(sc, cache=True, W_ofT=sc.W_ofT)
+    gs, gn, _ = gc.route(g)
+    assert gn.tolist() == [[0], [1], [2]]
+    assert (gs[0] == -1).all()
+    z, out = gc.decode(g, gs, gn)
+    assert (out[0] == 0).all() and (z[0] == 0).all()
+    np.testing.assert_allclose(out, out_ref, rtol=2e-2, atol=2e-3)
+
+
+@pytest.mark.parametrize("name,chunks", [("g4_d128_p64", [0, 128, 300]), ("g8_2kv_r48_p32", [0, 77, 513]),
+                                         ("tiny_f32", [0, 64, 200]), ("bf16_p16", [0, 40, 100])])
+def test_prefill_matches_oracle(name, chunks):
+    w, _ = CASES[name]
+    n = chunks[-1]
+    w = w.with_(batch=1)
+    sc = cases.make_scenario(w, lengths=[n], write=False)
+    qp = synth.to_storage(np.random.default_rng(5).standard_normal((n, w.n_q_heads, w.head_dim)), w.dtype)
+    ora = oracle.Cache(sc.d, sc.page_table)
+    W = oracle.fold(sc.d, sc.fac.B, sc.fac.W_O)
+    zr, orr = [], []
+    for a, b in zip(chunks[:-1], chunks[1:]):
+        z, o = oracle.prefill(sc.d, sc.fac, W, ora, 0, a, qp[a:b], sc.K[0][a:b], sc.V[0][a:b])
+        zr.append(z); orr.append(o)
+    z_ref, out_ref = np.concatenate(zr), np.concatenate(orr)
+    g = gc.upload(sc, W_ofT=W, max_prefill=n)
+    zs, outs = [], []
+    for a, b in zip(chunks[:-1], chunks[1:]):
+        z = torch.empty((b - a, w.n_q_heads, w.rank_v), device="cuda")
+        out = torch.empty((b - a, w.d_model), device="cuda")
+        import routed_decode_attention_amd as rda
+        rda.basiskv_prefill(g.d, g.f, g.cache, 0, a, gc.dev(qp[a:b], w.dtype), gc.dev(sc.K[0][a:b], w.dtype),
+                            gc.dev(sc.V[0][a:b], w.dtype), g.ws, out, z_out=z)
+        zs.append(gc.host(z)); outs.append(gc.host(out))
+    torch.cuda.synchronize()
+    rtol, atol = gc.tol(w)
+    np.testing.assert_allclose(np.concatenate(zs), z_ref, rtol=rtol, atol=atol)
+    np.testing.assert_allclose(np.concatenate(outs), out_ref, rtol=rtol, atol=atol)
+    compare_written(sc, gc.cache_host(g), ora)
