@@ -6,9 +6,11 @@
 // [d_model][n_q_heads*r], so both MFMA operands are contiguous along the
 // contraction and load straight from memory as 16-byte fragments.
 //
-// bf16: v_mfma_f32_16x16x32_bf16 with z rounded to bf16 on load and fp32
-// accumulation.  A wave computes WM x WN tiles of 16x16; a workgroup holds
-// WAVES_M x WAVES_N waves.  Decode batches use one 16-row tile per wave (the
+// bf16: v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  z is split on load
+// into a bf16 high part and the bf16 rounding of its remainder, and both are
+// multiplied (two MFMAs): z keeps about 16 significant bits instead of 8, so
+// the only rounding left in the product is the stored weights'.  A wave
+// computes WM x WN tiles of 16x16; a workgroup holds WAVES_M x WAVES_N waves.  Decode batches use one 16-row tile per wave (the
 // rows are the batch), prefill chunks 64x64 per wave.
 // fp32 (or shapes the matrix cores do not tile): a VALU dot per output.
 #include "common.hpp"
@@ -36,7 +38,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void project_mfma_kernel(Pr
     for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int k0 = 0; k0 < a.kdim; k0 += 32) {
-    bf16x8 af[WM], bfr[WN];
+    bf16x8 af[WM], al[WM], bfr[WN];
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
       const int row = row0 + 16 * i + n;
@@ -44,9 +46,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void project_mfma_kernel(Pr
         const float4* zp = reinterpret_cast<const float4*>(a.z + (size_t)row * a.kdim + k0 + 8 * qd);
         const float4 x0 = zp[0], x1 = zp[1];
         const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        float lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lo[e] = x[e] - bf16_to_f32(f32_to_bf16(x[e]));
         af[i] = pack_bf16x8(x);
+        al[i] = pack_bf16x8(lo);
       } else {
         af[i] = zero_bf16x8();
+        al[i] = zero_bf16x8();
       }
     }
 #pragma unroll
@@ -55,8 +62,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void project_mfma_kernel(Pr
 #pragma unroll
     for (int i = 0; i < WM; ++i)
 #pragma unroll
-      for (int j = 0; j < WN; ++j)
+      for (int j = 0; j < WN; ++j) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
   }
 #pragma unroll
   for (int i = 0; i < WM; ++i)
