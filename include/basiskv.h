@@ -164,16 +164,24 @@ int basiskv_append(const basiskv_dims *dims, const basiskv_factors *f,
  *          for j < n_pg; entries j >= n_pg are left unspecified;
  *   sel    [batch][n_kv_heads][top_k] int32 ascending logical pages, -1 padded;
  *   n_sel  [batch][n_kv_heads] int32 = min(top_k, n_pg).
- * ws: the workspace of basiskv_workspace_bytes (its counters are used).
  */
 int basiskv_route(const basiskv_dims *dims, const basiskv_factors *f,
                   const basiskv_cache *cache, const int32_t *seq_lens, const void *q,
-                  void *ws, size_t ws_bytes, int32_t *sel, int32_t *n_sel, float *scores,
-                  void *stream);
+                  int32_t *sel, int32_t *n_sel, float *scores, void *stream);
 
 /*
- * Device workspace, in bytes, that basiskv_route/attend/decode (batch rows)
- * and basiskv_prefill (up to max_prefill_tokens queries) need.  Host function.
+ * basiskv_append followed by basiskv_route, in one launch (the decode step
+ * appends its token before attending).  Arguments as in the two calls; the
+ * factors B, P, R_enc and R_dec are all required.
+ */
+int basiskv_append_route(const basiskv_dims *dims, const basiskv_factors *f,
+                         const basiskv_cache *cache, const int32_t *pos, const void *k_new,
+                         const void *v_new, const int32_t *seq_lens, const void *q,
+                         int32_t *sel, int32_t *n_sel, float *scores, void *stream);
+
+/*
+ * Device workspace, in bytes, that basiskv_attend/decode/decode_step (batch
+ * rows) and basiskv_prefill (up to max_prefill_tokens queries) need.  Host function.
  * Its first bytes hold counters that must be zero before first use: allocate
  * it zero-filled or call basiskv_workspace_init once.  Every call leaves them
  * zero again.  Calls that share a workspace must not overlap in time.
@@ -215,6 +223,17 @@ int basiskv_decode(const basiskv_dims *dims, const basiskv_factors *f,
                    const basiskv_cache *cache, const int32_t *seq_lens, const void *q,
                    const int32_t *sel, const int32_t *n_sel, void *ws, size_t ws_bytes,
                    float *z_out, float *out, void *stream);
+
+/*
+ * The whole decode layer step in three launches: append + route (one kernel),
+ * attend, project.  sel, n_sel and scores are written as by basiskv_route;
+ * z_out may be NULL.
+ */
+int basiskv_decode_step(const basiskv_dims *dims, const basiskv_factors *f,
+                        const basiskv_cache *cache, const int32_t *pos, const void *k_new,
+                        const void *v_new, const int32_t *seq_lens, const void *q,
+                        int32_t *sel, int32_t *n_sel, float *scores, void *ws, size_t ws_bytes,
+                        float *z_out, float *out, void *stream);
 
 /*
  * Prefill chunk of one sequence: basiskv_write of tokens [start_pos,

@@ -26,9 +26,9 @@ OK, E_NULL, E_DIMS, E_UNSUPPORTED, E_WORKSPACE, E_HIP, E_DATA = 0, -1, -2, -3, -
 
 EXPORTS = (
     "basiskv_version", "basiskv_strerror", "basiskv_last_error", "basiskv_fold_output",
-    "basiskv_write", "basiskv_append", "basiskv_route", "basiskv_workspace_bytes",
-    "basiskv_workspace_init", "basiskv_attend", "basiskv_project", "basiskv_decode",
-    "basiskv_prefill",
+    "basiskv_write", "basiskv_append", "basiskv_route", "basiskv_append_route",
+    "basiskv_workspace_bytes", "basiskv_workspace_init", "basiskv_attend", "basiskv_project",
+    "basiskv_decode", "basiskv_decode_step", "basiskv_prefill",
 )
 
 
@@ -69,7 +69,9 @@ def _load() -> C.CDLL:
         "basiskv_fold_output": ([D, p, p, p, p], C.c_int),
         "basiskv_write": ([D, Fp, Cp, i32, i32, i32, p, p, p], C.c_int),
         "basiskv_append": ([D, Fp, Cp, p, p, p, p], C.c_int),
-        "basiskv_route": ([D, Fp, Cp, p, p, p, sz, p, p, p, p], C.c_int),
+        "basiskv_route": ([D, Fp, Cp, p, p, p, p, p, p], C.c_int),
+        "basiskv_append_route": ([D, Fp, Cp, p, p, p, p, p, p, p, p, p], C.c_int),
+        "basiskv_decode_step": ([D, Fp, Cp, p, p, p, p, p, p, p, p, p, sz, p, p, p], C.c_int),
         "basiskv_workspace_bytes": ([D, i32], sz),
         "basiskv_workspace_init": ([D, p, sz, p], C.c_int),
         "basiskv_attend": ([D, Cp, p, p, p, p, p, sz, p, p], C.c_int),
@@ -243,17 +245,48 @@ def basiskv_workspace_init(d: Dims, ws: torch.Tensor, stream=None) -> None:
 
 
 def basiskv_route(d: Dims, f: Factors, cache: Cache, seq_lens: torch.Tensor, q: torch.Tensor,
-                  ws: torch.Tensor, sel: torch.Tensor, n_sel: torch.Tensor, scores: torch.Tensor,
-                  stream=None) -> None:
+                  sel: torch.Tensor, n_sel: torch.Tensor, scores: torch.Tensor, stream=None) -> None:
     pairs = d.batch * d.n_kv_heads
     fc, cc = f.c(d), cache.c(d)
     _check(_lib.basiskv_route(
         C.byref(d.c()), C.byref(fc), C.byref(cc),
         _ptr(seq_lens, "seq_lens", torch.int32, d.batch),
         _ptr(q, "q", d.torch_dtype, d.batch * d.n_q_heads * d.head_dim),
-        _ptr(ws, "ws", torch.uint8), ws.numel(),
         _ptr(sel, "sel", torch.int32, pairs * d.top_k), _ptr(n_sel, "n_sel", torch.int32, pairs),
         _ptr(scores, "scores", torch.float32, pairs * d.max_pages_per_seq), _stream(stream)))
+
+
+def basiskv_append_route(d: Dims, f: Factors, cache: Cache, pos: torch.Tensor, k_new: torch.Tensor,
+                         v_new: torch.Tensor, seq_lens: torch.Tensor, q: torch.Tensor,
+                         sel: torch.Tensor, n_sel: torch.Tensor, scores: torch.Tensor,
+                         stream=None) -> None:
+    pairs = d.batch * d.n_kv_heads
+    need = d.batch * d.n_kv_heads * d.head_dim
+    fc, cc = f.c(d), cache.c(d)
+    _check(_lib.basiskv_append_route(
+        C.byref(d.c()), C.byref(fc), C.byref(cc), _ptr(pos, "pos", torch.int32, d.batch),
+        _ptr(k_new, "k_new", d.torch_dtype, need), _ptr(v_new, "v_new", d.torch_dtype, need),
+        _ptr(seq_lens, "seq_lens", torch.int32, d.batch),
+        _ptr(q, "q", d.torch_dtype, d.batch * d.n_q_heads * d.head_dim),
+        _ptr(sel, "sel", torch.int32, pairs * d.top_k), _ptr(n_sel, "n_sel", torch.int32, pairs),
+        _ptr(scores, "scores", torch.float32, pairs * d.max_pages_per_seq), _stream(stream)))
+
+
+def basiskv_decode_step(d: Dims, f: Factors, cache: Cache, pos, k_new, v_new, seq_lens, q, sel, n_sel,
+                        scores, ws, out, z_out=None, stream=None) -> None:
+    pairs = d.batch * d.n_kv_heads
+    need = d.batch * d.n_kv_heads * d.head_dim
+    fc, cc = f.c(d), cache.c(d)
+    _check(_lib.basiskv_decode_step(
+        C.byref(d.c()), C.byref(fc), C.byref(cc), _ptr(pos, "pos", torch.int32, d.batch),
+        _ptr(k_new, "k_new", d.torch_dtype, need), _ptr(v_new, "v_new", d.torch_dtype, need),
+        _ptr(seq_lens, "seq_lens", torch.int32, d.batch),
+        _ptr(q, "q", d.torch_dtype, d.batch * d.n_q_heads * d.head_dim),
+        _ptr(sel, "sel", torch.int32, pairs * d.top_k), _ptr(n_sel, "n_sel", torch.int32, pairs),
+        _ptr(scores, "scores", torch.float32, pairs * d.max_pages_per_seq),
+        _ptr(ws, "ws", torch.uint8), ws.numel(),
+        _ptr(z_out, "z_out", torch.float32, d.batch * d.n_q_heads * d.rank_v),
+        _ptr(out, "out", torch.float32, d.batch * d.d_model), _stream(stream)))
 
 
 def basiskv_attend(d: Dims, cache: Cache, seq_lens, q, sel, n_sel, ws, z_out, stream=None) -> None:

@@ -14,7 +14,7 @@ BUILD = os.path.join(HERE, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Werror",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Werror",
     "-Wno-unused-result",
     # no packed fp32 arithmetic in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

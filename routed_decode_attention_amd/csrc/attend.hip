@@ -12,8 +12,16 @@
 // pages_per_wave consecutive selected pages and keeps an online softmax
 // (running max m, denominator l, latent accumulator) for every query head of
 // the group.  The waves of a workgroup merge through LDS; the workgroup that
-// finishes last for its pair merges every split and writes the normalised
-// latent (counter in the workspace, reset by that workgroup).
+// finishes last for its pair loads every split's partial into LDS in one
+// round trip, merges them and writes the normalised latent (counter in the
+// workspace, reset by that workgroup).  The partials cross workgroups (and
+// XCDs, whose L2s are not coherent with each other) through device-scope
+// accesses only: they are written with relaxed agent-scope atomic stores
+// (write-through to the device coherence point), each thread waits for its
+// stores to complete before the workgroup barrier, one thread then bumps the
+// counter, and the last workgroup reads them with agent-scope atomic loads.
+// This avoids agent-scope fences, which write back and invalidate a whole
+// L2 and cost far more than the merge itself.
 //
 // bf16 storage, d_h in {64,128}, page 32/64, r in {16,32,48,64}: matrix-core
 // kernel.  Per 32-token chunk of a page, S = K.q^T runs as two 16x16x32 bf16
@@ -24,9 +32,13 @@
 // it must supply for the transposed latent product Acc^T[r][h] +=
 // Z^T[r][t] . P^T[t][h], whose A operand is the channel-major latent page
 // loaded straight from HBM.  Every softmax statistic of head h then lives in
-// the lanes of column h, so rescaling needs no cross-lane traffic.
+// the lanes of column h, so rescaling needs no cross-lane traffic.  A page's
+// 20 16-byte fragments per lane are all issued before its first MFMA, and the
+// next page's while the current one is multiplied.
 // Everything else (fp32 storage, other shapes): a plain VALU kernel with the
 // same split and merge.
+#include <cstdlib>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -42,9 +54,12 @@ struct WaveState {  // LDS image of one wave's online-softmax state
   float acc[ATTEND_WAVES][MAX_GROUP][MAX_RANK];
 };
 
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 // Merge the workgroup's waves into one partial; then, if this workgroup is the
-// last of its pair to finish, merge all partials into z_out.
-__device__ void finish_pair(const AttendArgs& a, WaveState& ws, int pair, int split) {
+// last of its pair to finish, merge all partials into z_out.  s_part: dynamic
+// LDS of n_wsplit * group * (rank_v + 2) floats.
+__device__ void finish_pair(const AttendArgs& a, WaveState& ws, float* s_part, int pair, int split) {
   const int G = a.s.group, R = a.s.rank_v;
   const int stride = R + 2;
   const int tid = threadIdx.x;
@@ -55,9 +70,11 @@ __device__ void finish_pair(const AttendArgs& a, WaveState& ws, int pair, int sp
   for (int o = tid; o < G * R; o += blockDim.x) {
     const int h = o / R, r = o % R;
     float M = NEG_INF;
+#pragma unroll
     for (int w = 0; w < ATTEND_WAVES; ++w) M = fmaxf(M, ws.m[w][h]);
     float L = 0.f, A = 0.f;
     if (M != NEG_INF) {
+#pragma unroll
       for (int w = 0; w < ATTEND_WAVES; ++w) {
         const float e = exp2f(ws.m[w][h] - M);
         L += e * ws.l[w][h];
@@ -67,35 +84,50 @@ __device__ void finish_pair(const AttendArgs& a, WaveState& ws, int pair, int sp
     if (single) {
       a.z_out[((size_t)b * a.s.n_q_heads + g * G + h) * R + r] = L > 0.f ? A / L : 0.f;
     } else {
-      part[h * stride + 2 + r] = A;
+      __hip_atomic_store(&part[h * stride + 2 + r], A, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (r == 0) {
-        part[h * stride] = M;
-        part[h * stride + 1] = L;
+        __hip_atomic_store(&part[h * stride], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&part[h * stride + 1], L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
   if (single) return;
 
   __shared__ int s_last;
-  __threadfence();  // release this thread's partial stores at device scope
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
+  __syncthreads();                // ... and every other thread's of the workgroup
   if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(&a.counters[pair], 1u, __ATOMIC_ACQ_REL,
+    const unsigned prev = __hip_atomic_fetch_add(&a.counters[pair], 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     s_last = prev == (unsigned)(a.n_wsplit - 1);
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();  // acquire the other workgroups' partials
+  // every partial of the pair into LDS, up to 8 device-scope loads in flight per thread
   const float* base = a.partials + (size_t)pair * a.n_wsplit * G * stride;
+  const int total = a.n_wsplit * G * stride;
+  for (int i0 = tid; i0 < total; i0 += blockDim.x * 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * blockDim.x;
+      v[u] = i < total ? __hip_atomic_load(base + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * blockDim.x;
+      if (i < total) s_part[i] = v[u];
+    }
+  }
+  __syncthreads();
   for (int o = tid; o < G * R; o += blockDim.x) {
     const int h = o / R, r = o % R;
     float M = NEG_INF;
-    for (int sp = 0; sp < a.n_wsplit; ++sp) M = fmaxf(M, base[((size_t)sp * G + h) * stride]);
+    for (int sp = 0; sp < a.n_wsplit; ++sp) M = fmaxf(M, s_part[(sp * G + h) * stride]);
     float L = 0.f, A = 0.f;
     if (M != NEG_INF) {
       for (int sp = 0; sp < a.n_wsplit; ++sp) {
-        const float* p = base + ((size_t)sp * G + h) * stride;
+        const float* p = s_part + (sp * G + h) * stride;
         const float e = exp2f(p[0] - M);
         L += e * p[1];
         A += e * p[2 + r];
@@ -119,63 +151,40 @@ __device__ __forceinline__ bf16x8 keep_first(bf16x8 v, int valid) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
+// One page's MFMA operands for this lane.
 template <int D, int PS, int R>
-__global__ __launch_bounds__(256) void attend_mfma_kernel(AttendArgs a) {
-  constexpr int KS = D / 32;   // 32-dim steps of q.k
-  constexpr int NC = PS / 32;  // 32-token chunks per page
-  constexpr int MT = R / 16;   // 16-channel tiles of the latent
-  __shared__ WaveState st;
-
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int pair = wg / a.n_wsplit, split = wg % a.n_wsplit;
-  const int H = a.s.n_kv_heads, G = a.s.group;
-  const int b = pair / H, g = pair % H;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n = lane & 15, qd = lane >> 4;
-
-  const int seq_len = a.seq_lens[b];
-  const int nsel = seq_len > 0 ? a.n_sel[pair] : 0;
-  const int first = (split * ATTEND_WAVES + wave) * a.pages_per_wave;
-  const int last = min(first + a.pages_per_wave, nsel);
-
-  const uint16_t* Kp = static_cast<const uint16_t*>(a.K);
-  const uint16_t* Zp = static_cast<const uint16_t*>(a.Z);
-
-  bf16x8 qb[KS];
-  {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                         ((size_t)b * a.s.n_q_heads + g * G + (n < G ? n : 0)) * D;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qb[s] = n < G ? load_bf16x8(qp + 8 * qd + 32 * s) : zero_bf16x8();
-  }
-
-  float m_run = NEG_INF, l_run = 0.f;
-  f32x4 acc[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int i = first; i < last; ++i) {
-    const int j = a.sel[(size_t)pair * a.s.top_k + i];
-    const int phys = a.page_table[(size_t)b * a.s.max_pages + j];
-    const int cnt = min(PS, seq_len - j * PS);
-    const uint16_t* kp = Kp + ((size_t)phys * H + g) * PS * D;
-    const uint16_t* zp = Zp + ((size_t)phys * H + g) * R * PS;
-
-    bf16x8 kf[NC][2][KS];
-    bf16x8 zf[NC][MT];
+struct PageFrags {
+  static constexpr int KS = D / 32, NC = PS / 32, MT = R / 16;
+  bf16x8 k[NC][2][KS];
+  bf16x8 z[NC][MT];
+  __device__ __forceinline__ void load(const uint16_t* kp, const uint16_t* zp, int n, int qd) {
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         const int tok = 32 * c + 8 * (n >> 2) + 4 * t2 + (n & 3);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) kf[c][t2][s] = load_bf16x8(kp + tok * D + 8 * qd + 32 * s);
+        for (int s = 0; s < KS; ++s) k[c][t2][s] = load_bf16x8(kp + tok * D + 8 * qd + 32 * s);
       }
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int t = 0; t < MT; ++t) zf[c][t] = load_bf16x8(zp + (16 * t + n) * PS + 32 * c + 8 * qd);
+      for (int t = 0; t < MT; ++t) z[c][t] = load_bf16x8(zp + (16 * t + n) * PS + 32 * c + 8 * qd);
+  }
+};
 
+template <int D, int PS, int R>
+struct OnlineSoftmax {
+  static constexpr int KS = D / 32, NC = PS / 32, MT = R / 16;
+  float m = NEG_INF, l = 0.f;
+  f32x4 acc[MT];
+  __device__ __forceinline__ OnlineSoftmax() {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // Fold one page (cnt valid tokens) into the state.
+  __device__ __forceinline__ void page(PageFrags<D, PS, R>& f, const bf16x8 (&qb)[KS], int cnt, int qd,
+                                       float scale_log2) {
     float sv[NC][8];
 #pragma unroll
     for (int c = 0; c < NC; ++c)
@@ -183,12 +192,10 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttendArgs a) {
       for (int t2 = 0; t2 < 2; ++t2) {
         f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-          s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c][t2][s], qb[s], s4, 0, 0, 0);
+        for (int s = 0; s < KS; ++s) s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k[c][t2][s], qb[s], s4, 0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sv[c][4 * t2 + e] = s4[e] * a.scale_log2;
+        for (int e = 0; e < 4; ++e) sv[c][4 * t2 + e] = s4[e] * scale_log2;
       }
-
     if (cnt < PS) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -197,10 +204,9 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttendArgs a) {
         for (int e = 0; e < 8; ++e)
           if (e >= valid) sv[c][e] = NEG_INF;
 #pragma unroll
-        for (int t = 0; t < MT; ++t) zf[c][t] = keep_first(zf[c][t], valid);
+        for (int t = 0; t < MT; ++t) f.z[c][t] = keep_first(f.z[c][t], valid);
       }
     }
-
     float mx = NEG_INF;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
@@ -208,11 +214,11 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttendArgs a) {
       for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sv[c][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    if (m_new == NEG_INF) continue;  // nothing valid yet
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
+    const float m_new = fmaxf(m, mx);
+    if (m_new == NEG_INF) return;  // wave-uniform: no valid token so far
+    const float alpha = exp2f(m - m_new);
+    m = m_new;
+    l *= alpha;
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[t] *= alpha;
 #pragma unroll
@@ -221,29 +227,97 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttendArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         p[e] = bf16_to_f32(f32_to_bf16(exp2f(sv[c][e] - m_new)));
-        l_run += p[e];
+        l += p[e];
       }
       const bf16x8 pb = pack_bf16x8(p);
 #pragma unroll
-      for (int t = 0; t < MT; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zf[c][t], pb, acc[t], 0, 0, 0);
+      for (int t = 0; t < MT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.z[c][t], pb, acc[t], 0, 0, 0);
+    }
+  }
+};
+
+template <int D, int PS, int R, bool PIPE>
+__global__ __launch_bounds__(256) void attend_mfma_kernel(AttendArgs a) {
+  constexpr int KS = D / 32, MT = R / 16;
+  __shared__ WaveState st;
+  extern __shared__ float s_part[];
+
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int pair = wg / a.n_wsplit, split = wg % a.n_wsplit;
+  const int H = a.s.n_kv_heads, G = a.s.group;
+  const int b = pair / H, g = pair % H;
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n = lane & 15, qd = lane >> 4;
+
+  const int seq_len = a.seq_lens[b];
+  const int nsel = seq_len > 0 ? a.n_sel[pair] : 0;
+  const int first = (split * ATTEND_WAVES + wave) * a.pages_per_wave;
+  const int np = max(0, min(first + a.pages_per_wave, nsel) - first);  // pages of this wave
+
+  // page ids and valid-token counts of this wave's pages, lane u holds page u
+  int my_phys = 0, my_cnt = 0;
+  if (lane < np) {
+    const size_t at = (size_t)pair * a.s.top_k + first + lane;
+    const int j = a.sel[at];
+    my_phys = a.sel_phys ? a.sel_phys[at] : a.page_table[(size_t)b * a.s.max_pages + j];
+    my_cnt = min(PS, seq_len - j * PS);
+  }
+  bf16x8 qb[KS];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                         ((size_t)b * a.s.n_q_heads + g * G + (n < G ? n : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qb[s] = n < G ? load_bf16x8(qp + 8 * qd + 32 * s) : zero_bf16x8();
+  }
+  const uint16_t* Kp = static_cast<const uint16_t*>(a.K);
+  const uint16_t* Zp = static_cast<const uint16_t*>(a.Z);
+  auto kpage = [&](int u) {
+    const int phys = __builtin_amdgcn_readlane(my_phys, u);
+    return Kp + ((size_t)phys * H + g) * PS * D;
+  };
+  auto zpage = [&](int u) {
+    const int phys = __builtin_amdgcn_readlane(my_phys, u);
+    return Zp + ((size_t)phys * H + g) * R * PS;
+  };
+
+  OnlineSoftmax<D, PS, R> os;
+  if (PIPE) {  // several pages per wave: the next page's loads overlap this page's math
+    PageFrags<D, PS, R> fa, fb;
+    if (np > 0) fa.load(kpage(0), zpage(0), n, qd);
+    for (int u = 0; u < np; u += 2) {
+      if (u + 1 < np) fb.load(kpage(u + 1), zpage(u + 1), n, qd);
+      __builtin_amdgcn_sched_barrier(0);
+      os.page(fa, qb, __builtin_amdgcn_readlane(my_cnt, u), qd, a.scale_log2);
+      if (u + 1 < np) {
+        if (u + 2 < np) fa.load(kpage(u + 2), zpage(u + 2), n, qd);
+        __builtin_amdgcn_sched_barrier(0);
+        os.page(fb, qb, __builtin_amdgcn_readlane(my_cnt, u + 1), qd, a.scale_log2);
+      }
+    }
+  } else {
+    for (int u = 0; u < np; ++u) {
+      PageFrags<D, PS, R> fa;
+      fa.load(kpage(u), zpage(u), n, qd);
+      __builtin_amdgcn_sched_barrier(0);
+      os.page(fa, qb, __builtin_amdgcn_readlane(my_cnt, u), qd, a.scale_log2);
     }
   }
 
   // this wave's state into LDS: head n lives in lanes n, n+16, n+32, n+48
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  float l = os.l;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
   if (n < G) {
     if (qd == 0) {
-      st.m[wave][n] = m_run;
-      st.l[wave][n] = l_run;
+      st.m[wave][n] = os.m;
+      st.l[wave][n] = l;
     }
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) st.acc[wave][n][16 * t + 4 * qd + e] = acc[t][e];
+      for (int e = 0; e < 4; ++e) st.acc[wave][n][16 * t + 4 * qd + e] = os.acc[t][e];
   }
-  finish_pair(a, st, pair, split);
+  finish_pair(a, st, s_part, pair, split);
 }
 
 // Plain VALU kernel: one lane per token for q.k, one lane per latent channel
@@ -253,6 +327,7 @@ __global__ __launch_bounds__(256) void attend_valu_kernel(AttendArgs a) {
   __shared__ WaveState st;
   __shared__ float s_q[MAX_GROUP][128];
   __shared__ float s_p[ATTEND_WAVES][64];
+  extern __shared__ float s_part[];
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int pair = wg / a.n_wsplit, split = wg % a.n_wsplit;
@@ -315,8 +390,10 @@ __global__ __launch_bounds__(256) void attend_valu_kernel(AttendArgs a) {
     }
     if (lane < R) st.acc[wave][h][lane] = acc[h];
   }
-  finish_pair(a, st, pair, split);
+  finish_pair(a, st, s_part, pair, split);
 }
+
+size_t part_floats(const Shape& s, int n_wsplit) { return (size_t)n_wsplit * s.group * (s.rank_v + 2); }
 
 }  // namespace
 
@@ -327,27 +404,37 @@ bool attend_mfma_supported(const Shape& s) {
 }
 
 AttendPlan plan_attend(const Shape& s) {
-  // About 16 waves per CU over 256 CUs once every page unit is counted.
+  // About 16 waves per CU over 256 CUs once every page unit is counted, and
+  // a partial-merge staging area of at most 40 KiB.
   const long units = (long)s.batch * s.n_kv_heads * s.top_k;
   int ppw = (int)((units + 4095) / 4096);
   if (ppw < 1) ppw = 1;
   if (ppw > 8) ppw = 8;
   const char* env = getenv("BASISKV_PAGES_PER_WAVE");
-  if (env && atoi(env) > 0) ppw = atoi(env);
+  if (env && atoi(env) > 0) ppw = atoi(env) < 32 ? atoi(env) : 32;
   AttendPlan p;
-  p.pages_per_wave = ppw;
-  p.n_wsplit = (s.top_k + ATTEND_WAVES * ppw - 1) / (ATTEND_WAVES * ppw);
+  for (;;) {
+    p.pages_per_wave = ppw;
+    p.n_wsplit = (s.top_k + ATTEND_WAVES * ppw - 1) / (ATTEND_WAVES * ppw);
+    if (p.n_wsplit == 1 || part_floats(s, p.n_wsplit) * sizeof(float) <= 40 * 1024) break;
+    ++ppw;
+  }
   return p;
 }
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   const int pairs = a.s.batch * a.s.n_kv_heads;
   const dim3 grid(pairs * a.n_wsplit), block(256);
+  const size_t lds = a.n_wsplit > 1 ? part_floats(a.s, a.n_wsplit) * sizeof(float) : 0;
   if (attend_mfma_supported(a.s)) {
+    const bool pipe = a.pages_per_wave > 1;
     const int key = a.s.head_dim * 10000 + a.s.page_size * 100 + a.s.rank_v;
     switch (key) {
 #define BKV_CASE(D, PS, R) \
-  case D * 10000 + PS * 100 + R: hipLaunchKernelGGL((attend_mfma_kernel<D, PS, R>), grid, block, 0, st, a); break;
+  case D * 10000 + PS * 100 + R:                                                                 \
+    if (pipe) hipLaunchKernelGGL((attend_mfma_kernel<D, PS, R, true>), grid, block, lds, st, a);   \
+    else hipLaunchKernelGGL((attend_mfma_kernel<D, PS, R, false>), grid, block, lds, st, a);       \
+    break;
       BKV_CASE(128, 64, 16) BKV_CASE(128, 64, 32) BKV_CASE(128, 64, 48) BKV_CASE(128, 64, 64)
       BKV_CASE(128, 32, 16) BKV_CASE(128, 32, 32) BKV_CASE(128, 32, 48) BKV_CASE(128, 32, 64)
       BKV_CASE(64, 64, 16) BKV_CASE(64, 64, 32) BKV_CASE(64, 64, 48) BKV_CASE(64, 64, 64)
@@ -356,9 +443,9 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
       default: return hipErrorInvalidValue;
     }
   } else if (a.s.dtype == 0) {
-    hipLaunchKernelGGL((attend_valu_kernel<float>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attend_valu_kernel<float>), grid, block, lds, st, a);
   } else {
-    hipLaunchKernelGGL((attend_valu_kernel<uint16_t>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attend_valu_kernel<uint16_t>), grid, block, lds, st, a);
   }
   return hipGetLastError();
 }

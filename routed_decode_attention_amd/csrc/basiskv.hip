@@ -80,21 +80,22 @@ int check_dims(const basiskv_dims* d, bkv::Shape* s) {
 }
 
 struct WsLayout {
-  size_t route_cnt, attend_cnt, partials, z, total;
+  size_t attend_cnt, partials, z, sel_phys, total;
 };
 
+// Workspace: attention merge counters, split-K partials, then latent rows.
 WsLayout ws_layout(const bkv::Shape& s, int max_prefill_tokens) {
   const size_t pairs = (size_t)s.batch * s.n_kv_heads;
   const bkv::AttendPlan p = bkv::plan_attend(s);
   WsLayout L;
-  L.route_cnt = 0;
-  L.attend_cnt = pairs * sizeof(unsigned);
-  L.partials = align256(2 * pairs * sizeof(unsigned));
+  L.attend_cnt = 0;
+  L.partials = align256(pairs * sizeof(unsigned));
   const size_t part_bytes = pairs * p.n_wsplit * s.group * (s.rank_v + 2) * sizeof(float);
   L.z = L.partials + align256(part_bytes);
   size_t rows = (size_t)s.batch;
   if (max_prefill_tokens > 0 && (size_t)max_prefill_tokens > rows) rows = max_prefill_tokens;
-  L.total = L.z + align256(rows * s.n_q_heads * s.rank_v * sizeof(float));
+  L.sel_phys = L.z + align256(rows * s.n_q_heads * s.rank_v * sizeof(float));
+  L.total = L.sel_phys + align256(pairs * s.top_k * sizeof(int32_t));
   return L;
 }
 
@@ -109,7 +110,7 @@ inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 int do_attend(const bkv::Shape& s, const basiskv_cache* cache, const int32_t* seq_lens, const void* q,
               const int32_t* sel, const int32_t* n_sel, void* ws, size_t ws_bytes, float* z_out,
-              void* stream) {
+              void* stream, const int32_t* sel_phys = nullptr) {
   const WsLayout L = ws_layout(s, 0);
   if (ws_bytes < L.partials + (L.z - L.partials))
     return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, attention needs %zu", ws_bytes,
@@ -123,6 +124,7 @@ int do_attend(const bkv::Shape& s, const basiskv_cache* cache, const int32_t* se
   a.q = q;
   a.sel = sel;
   a.n_sel = n_sel;
+  a.sel_phys = sel_phys;
   char* w = static_cast<char*>(ws);
   a.partials = reinterpret_cast<float*>(w + L.partials);
   a.counters = reinterpret_cast<unsigned*>(w + L.attend_cnt);
@@ -171,8 +173,36 @@ int do_write(const bkv::Shape& s, const basiskv_factors* f, const basiskv_cache*
   return e == hipSuccess ? BASISKV_OK : hip_fail(e, "writer launch");
 }
 
+int do_route(const bkv::Shape& s, const basiskv_factors* f, const basiskv_cache* cache, const int32_t* pos,
+             const void* k_new, const void* v_new, const int32_t* seq_lens, const void* q, int32_t* sel,
+             int32_t* n_sel, float* scores, void* stream, int32_t* sel_phys = nullptr) {
+  bkv::RouteArgs a;
+  a.s = s;
+  a.B = f->B;
+  a.P = f->P;
+  a.R_enc = f->R_enc;
+  a.R_dec = f->R_dec;
+  a.K = cache->K;
+  a.Z = cache->Z;
+  a.S = cache->S;
+  a.summ = cache->summ;
+  a.page_table = cache->page_table;
+  a.seq_lens = seq_lens;
+  a.q = q;
+  a.pos = pos;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.sel = sel;
+  a.n_sel = n_sel;
+  a.sel_phys = sel_phys;
+  a.scores = scores;
+  const hipError_t e = bkv::launch_route(a, as_stream(stream));
+  return e == hipSuccess ? BASISKV_OK : hip_fail(e, "route launch");
+}
+
 }  // namespace
 
+#pragma GCC visibility push(default)
 extern "C" {
 
 int basiskv_version(void) { return BASISKV_VERSION; }
@@ -231,34 +261,30 @@ int basiskv_append(const basiskv_dims* dims, const basiskv_factors* f, const bas
 }
 
 int basiskv_route(const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
-                  const int32_t* seq_lens, const void* q, void* ws, size_t ws_bytes, int32_t* sel,
-                  int32_t* n_sel, float* scores, void* stream) {
+                  const int32_t* seq_lens, const void* q, int32_t* sel, int32_t* n_sel, float* scores,
+                  void* stream) {
   bkv::Shape s;
   int rc = check_dims(dims, &s);
   if (rc) return rc;
   if (!f || !f->P || !f->R_dec) return fail(BASISKV_E_NULL, "route: factors P and R_dec required");
   if ((rc = check_cache(cache, false, false, false))) return rc;
-  if (!seq_lens || !q || !ws || !sel || !n_sel || !scores)
-    return fail(BASISKV_E_NULL, "route: seq_lens, q, ws, sel, n_sel and scores are required");
-  const WsLayout L = ws_layout(s, 0);
-  if (ws_bytes < L.partials)
-    return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, routing needs %zu", ws_bytes, L.partials);
-  bkv::RouteArgs a;
-  a.s = s;
-  a.P = f->P;
-  a.R_dec = f->R_dec;
-  a.summ = cache->summ;
-  a.page_table = cache->page_table;
-  a.seq_lens = seq_lens;
-  a.q = q;
-  a.sel = sel;
-  a.n_sel = n_sel;
-  a.scores = scores;
-  a.counters = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + L.route_cnt);
-  a.pages_per_wg = bkv::route_pages_per_wg(s);
-  a.n_chunks = (s.max_pages + a.pages_per_wg - 1) / a.pages_per_wg;
-  const hipError_t e = bkv::launch_route(a, as_stream(stream));
-  return e == hipSuccess ? BASISKV_OK : hip_fail(e, "route launch");
+  if (!seq_lens || !q || !sel || !n_sel || !scores)
+    return fail(BASISKV_E_NULL, "route: seq_lens, q, sel, n_sel and scores are required");
+  return do_route(s, f, cache, nullptr, nullptr, nullptr, seq_lens, q, sel, n_sel, scores, stream);
+}
+
+int basiskv_append_route(const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
+                         const int32_t* pos, const void* k_new, const void* v_new, const int32_t* seq_lens,
+                         const void* q, int32_t* sel, int32_t* n_sel, float* scores, void* stream) {
+  bkv::Shape s;
+  int rc = check_dims(dims, &s);
+  if (rc) return rc;
+  if (!f || !f->B || !f->P || !f->R_enc || !f->R_dec)
+    return fail(BASISKV_E_NULL, "append_route: factors B, P, R_enc and R_dec required");
+  if ((rc = check_cache(cache, true, true, true))) return rc;
+  if (!pos || !k_new || !v_new || !seq_lens || !q || !sel || !n_sel || !scores)
+    return fail(BASISKV_E_NULL, "append_route: pos, k_new, v_new, seq_lens, q, sel, n_sel, scores required");
+  return do_route(s, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, stream);
 }
 
 size_t basiskv_workspace_bytes(const basiskv_dims* dims, int32_t max_prefill_tokens) {
@@ -319,6 +345,29 @@ int basiskv_decode(const basiskv_dims* dims, const basiskv_factors* f, const bas
   return do_project(s, f, z, s.batch, out, stream);
 }
 
+int basiskv_decode_step(const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
+                        const int32_t* pos, const void* k_new, const void* v_new, const int32_t* seq_lens,
+                        const void* q, int32_t* sel, int32_t* n_sel, float* scores, void* ws, size_t ws_bytes,
+                        float* z_out, float* out, void* stream) {
+  bkv::Shape s;
+  int rc = check_dims(dims, &s);
+  if (rc) return rc;
+  if (!f || !f->B || !f->P || !f->R_enc || !f->R_dec || !f->W_ofT)
+    return fail(BASISKV_E_NULL, "decode_step: every factor is required");
+  if ((rc = check_cache(cache, true, true, true))) return rc;
+  if (!pos || !k_new || !v_new || !seq_lens || !q || !sel || !n_sel || !scores || !ws || !out)
+    return fail(BASISKV_E_NULL, "decode_step: a required pointer is NULL");
+  const WsLayout L = ws_layout(s, 0);
+  if (ws_bytes < L.total)
+    return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, decode needs %zu", ws_bytes, L.total);
+  int32_t* sel_phys = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.sel_phys);
+  if ((rc = do_route(s, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, stream, sel_phys)))
+    return rc;
+  float* z = z_out ? z_out : reinterpret_cast<float*>(static_cast<char*>(ws) + L.z);
+  if ((rc = do_attend(s, cache, seq_lens, q, sel, n_sel, ws, ws_bytes, z, stream, sel_phys))) return rc;
+  return do_project(s, f, z, s.batch, out, stream);
+}
+
 int basiskv_prefill(const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
                     int32_t seq, int32_t start_pos, int32_t n_tok, const void* q, const void* k,
                     const void* v, void* ws, size_t ws_bytes, float* z_out, float* out, void* stream) {
@@ -357,3 +406,4 @@ int basiskv_prefill(const basiskv_dims* dims, const basiskv_factors* f, const ba
 }
 
 }  // extern "C"
+#pragma GCC visibility pop

@@ -34,14 +34,16 @@ struct WriteArgs {
 
 struct RouteArgs {
   Shape s;
-  const float *P, *R_dec;
-  const float* summ;
+  const float *B, *P, *R_enc, *R_dec;
+  void *K, *Z, *S;            // written only by the fused append
+  float* summ;
   const int32_t *page_table, *seq_lens;
   const void* q;
+  const int32_t* pos;         // fused append of one token per row at pos[b]; nullptr: route only
+  const void *k_new, *v_new;
   int32_t *sel, *n_sel;
+  int32_t* sel_phys;          // optional [batch][n_kv_heads][top_k]: physical ids of sel
   float* scores;
-  unsigned* counters;       // [batch * n_kv_heads], zero on entry and exit
-  int pages_per_wg, n_chunks;
 };
 
 struct AttendArgs {
@@ -50,6 +52,7 @@ struct AttendArgs {
   const int32_t *page_table, *seq_lens;
   const void* q;
   const int32_t *sel, *n_sel;
+  const int32_t* sel_phys;  // physical ids of sel (nullptr: looked up in page_table)
   float* partials;          // [pairs][n_wsplit][group][rank_v + 2]
   unsigned* counters;       // [pairs], zero on entry and exit
   float* z_out;             // [batch][n_q_heads][rank_v]
@@ -74,12 +77,18 @@ struct PrefillArgs {
   float scale_log2;
 };
 
+// Raise a kernel's dynamic-LDS limit when a launch needs more than the
+// default allows alongside its static arrays (gfx950 has 160 KiB per CU).
+inline hipError_t allow_lds(const void* kernel, size_t dynamic_bytes) {
+  if (dynamic_bytes <= 32 * 1024) return hipSuccess;
+  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dynamic_bytes);
+}
+
 // Host-side planning shared by workspace sizing and launches.
 struct AttendPlan {
   int pages_per_wave, n_wsplit;
 };
 AttendPlan plan_attend(const Shape& s);
-int route_pages_per_wg(const Shape& s);
 
 bool attend_mfma_supported(const Shape& s);
 bool project_mfma_supported(int kdim, int n, int dtype);

@@ -16,6 +16,7 @@
 // produce identical sums, and rewriting a position is idempotent.
 #include "common.hpp"
 #include "internal.hpp"
+#include "token_math.hpp"
 
 namespace bkv {
 
@@ -24,12 +25,17 @@ namespace {
 constexpr int THREADS = 256;
 constexpr int TB = 16;  // tokens per LDS batch
 
+// LDS floats the writer needs: staged B, P (row stride D+1), R_enc, then a
+// batch of v, k (reused for the Key remainder) and stored latents.
+size_t writer_lds_floats(const Shape& s) {
+  const int D = s.head_dim, R = s.rank_v, RK = s.rank_k, ps = s.page_size;
+  return (size_t)D * R + (size_t)R * lds_row(D) + (size_t)D * RK + 2 * TB * D + TB * R +
+         (size_t)R * (ps + 1) + (size_t)ps * RK;
+}
+
 template <typename T>
 __global__ __launch_bounds__(THREADS) void write_kernel(WriteArgs a) {
-  __shared__ float s_v[TB][128];   // v, then the Key remainder e
-  __shared__ float s_k[TB][128];
-  __shared__ float s_z[TB][MAX_RANK];
-
+  extern __shared__ float lds[];
   const int H = a.s.n_kv_heads, D = a.s.head_dim, R = a.s.rank_v, RK = a.s.rank_k;
   const int ps = a.s.page_size;
   const int g = blockIdx.y;
@@ -48,6 +54,19 @@ __global__ __launch_bounds__(THREADS) void write_kernel(WriteArgs a) {
     if (t0 >= t1) return;
     row0 = t0 - a.start;
   }
+  const int LDP = lds_row(D);
+  float* sB = lds;
+  float* sP = sB + D * R;
+  float* sRe = sP + R * LDP;
+  float* s_v = sRe + D * RK;  // [TB][D]: v, then the Key remainder
+  float* s_k = s_v + TB * D;  // [TB][D]
+  float* s_z = s_k + TB * D;  // [TB][R] stored latents
+  float* sZp = s_z + TB * R;  // [R][ps+1] the page's stored latents, for its sums
+  float* sSp = sZp + R * (ps + 1);  // [ps][RK] ... and residuals
+  stage_matrix(sB, R, a.B + (size_t)g * D * R, D, R);
+  stage_matrix(sP, LDP, a.P + (size_t)g * R * D, R, D);
+  stage_matrix(sRe, RK, a.R_enc + (size_t)g * D * RK, D, RK);
+
   const int page = t0 / ps;
   const int phys = a.page_table[(size_t)b * a.s.max_pages + page];
   const T* kin = static_cast<const T*>(a.k);
@@ -55,9 +74,6 @@ __global__ __launch_bounds__(THREADS) void write_kernel(WriteArgs a) {
   T* Kp = static_cast<T*>(a.K);
   T* Zp = static_cast<T*>(a.Z);
   T* Sp = static_cast<T*>(a.S);
-  const float* Bg = a.B + (size_t)g * D * R;
-  const float* Pg = a.P + (size_t)g * R * D;
-  const float* Eg = a.R_enc + (size_t)g * D * RK;
   const size_t kbase = ((size_t)phys * H + g) * ps * D;
   const size_t zbase = ((size_t)phys * H + g) * R * ps;
   const size_t sbase = ((size_t)phys * H + g) * ps * RK;
@@ -65,33 +81,28 @@ __global__ __launch_bounds__(THREADS) void write_kernel(WriteArgs a) {
 
   for (int tb = t0; tb < t1; tb += TB) {
     const int nb = min(TB, t1 - tb);
+    const int slot0 = tb - page * ps;
     for (int o = tid; o < nb * D; o += THREADS) {
       const int t = o / D, i = o % D;
       const size_t src = ((size_t)(row0 + tb - t0 + t) * H + g) * D + i;
-      s_v[t][i] = ld_elem(vin, src);
-      s_k[t][i] = ld_elem(kin, src);
-      Kp[kbase + (size_t)(tb - page * ps + t) * D + i] = kin[src];  // the exact Key, bit for bit
+      s_v[t * D + i] = ld_elem(vin, src);
+      s_k[t * D + i] = ld_elem(kin, src);
+      Kp[kbase + (size_t)(slot0 + t) * D + i] = kin[src];  // the exact Key, bit for bit
     }
     __syncthreads();
     for (int o = tid; o < nb * R; o += THREADS) {
       const int t = o / R, r = o % R;
-      float z = 0.f;
-      for (int i = 0; i < D; ++i) z += s_v[t][i] * Bg[(size_t)i * R + r];
-      s_z[t][r] = round_store(Zp, zbase + (size_t)r * ps + (tb - page * ps + t), z);
+      s_z[t * R + r] = round_store(Zp, zbase + (size_t)r * ps + slot0 + t, latent_dot(s_v + t * D, sB, D, R, r));
     }
     __syncthreads();
     for (int o = tid; o < nb * D; o += THREADS) {
       const int t = o / D, i = o % D;
-      float kh = 0.f;
-      for (int r = 0; r < R; ++r) kh += s_z[t][r] * Pg[(size_t)r * D + i];
-      s_v[t][i] = s_k[t][i] - kh;
+      s_v[t * D + i] = key_remainder(s_k[t * D + i], s_z + t * R, sP, LDP, R, i);
     }
     __syncthreads();
     for (int o = tid; o < nb * RK; o += THREADS) {
       const int t = o / RK, j = o % RK;
-      float s = 0.f;
-      for (int i = 0; i < D; ++i) s += s_v[t][i] * Eg[(size_t)i * RK + j];
-      round_store(Sp, sbase + (size_t)(tb - page * ps + t) * RK + j, s);
+      round_store(Sp, sbase + (size_t)(slot0 + t) * RK + j, residual_dot(s_v + t * D, sRe, D, RK, j));
     }
     __syncthreads();
   }
@@ -100,15 +111,10 @@ __global__ __launch_bounds__(THREADS) void write_kernel(WriteArgs a) {
   __threadfence_block();
   __syncthreads();
   const int valid = t1 - page * ps;
-  for (int x = tid; x < R + RK; x += THREADS) {
-    float acc = 0.f;
-    if (x < R) {
-      for (int t = 0; t < valid; ++t) acc += ld_elem(Zp, zbase + (size_t)x * ps + t);
-    } else {
-      for (int t = 0; t < valid; ++t) acc += ld_elem(Sp, sbase + (size_t)t * RK + (x - R));
-    }
-    a.summ[((size_t)phys * H + g) * (R + RK) + x] = acc;
-  }
+  stage_page(sZp, sSp, Zp + zbase, Sp + sbase, R, RK, ps);
+  __syncthreads();
+  for (int x = tid; x < R + RK; x += THREADS)
+    a.summ[((size_t)phys * H + g) * (R + RK) + x] = page_channel_sum(sZp, sSp, R, RK, ps, x, valid);
 }
 
 // W_ofT[c][h*R + j] = round(sum_i B[g(h)][i][j] * W_O[h*D + i][c]); one block
@@ -142,8 +148,16 @@ hipError_t launch_write(const WriteArgs& a, hipStream_t st) {
     const int pages = (a.start + a.n_tok - 1) / ps - a.start / ps + 1;
     grid = dim3(pages, a.s.n_kv_heads);
   }
-  if (a.s.dtype == 0) hipLaunchKernelGGL((write_kernel<float>), grid, dim3(THREADS), 0, st, a);
-  else hipLaunchKernelGGL((write_kernel<uint16_t>), grid, dim3(THREADS), 0, st, a);
+  const size_t lds = writer_lds_floats(a.s) * sizeof(float);
+  if (a.s.dtype == 0) {
+    const hipError_t e = allow_lds((const void*)write_kernel<float>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((write_kernel<float>), grid, dim3(THREADS), lds, st, a);
+  } else {
+    const hipError_t e = allow_lds((const void*)write_kernel<uint16_t>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((write_kernel<uint16_t>), grid, dim3(THREADS), lds, st, a);
+  }
   return hipGetLastError();
 }
 

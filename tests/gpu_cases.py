@@ -102,7 +102,7 @@ def route(g: Dev, q: Optional[torch.Tensor] = None):
     n_sel = torch.full((g.d.batch, g.d.n_kv_heads), -7, dtype=torch.int32, device="cuda")
     scores = torch.zeros((g.d.batch, g.d.n_kv_heads, g.d.max_pages_per_seq), dtype=torch.float32,
                          device="cuda")
-    rda.basiskv_route(g.d, g.f, g.cache, g.seq_lens, g.q if q is None else q, g.ws, sel, n_sel, scores)
+    rda.basiskv_route(g.d, g.f, g.cache, g.seq_lens, g.q if q is None else q, sel, n_sel, scores)
     torch.cuda.synchronize()
     return host(sel), host(n_sel), host(scores)
 

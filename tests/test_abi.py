@@ -36,6 +36,14 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == set(lib.EXPORTS)
 
 
+def test_exports_nothing_but_the_declared_api(lib):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    syms = {x for x in syms if not x.startswith("__hip_cuid")}
+    assert syms == set(declared_functions())
+
+
 def test_version_matches_header(lib):
     m = re.search(r"#define BASISKV_VERSION (\d+)", open(HEADER).read())
     assert lib.basiskv_version() == int(m.group(1))
@@ -52,14 +60,22 @@ def _dims(lib, **kw):
 FAKE = C.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
 
 
-def _route(lib, d, ws_bytes=1 << 20, **ptrs):
+def _route(lib, d, **ptrs):
     raw = lib.basiskv._lib
     f = lib.basiskv.basiskv_factors(FAKE.value, FAKE.value, FAKE.value, FAKE.value, FAKE.value)
     c = lib.basiskv.basiskv_cache(FAKE.value, FAKE.value, FAKE.value, FAKE.value, FAKE.value)
-    args = dict(seq_lens=FAKE, q=FAKE, ws=FAKE, sel=FAKE, n_sel=FAKE, scores=FAKE)
+    args = dict(seq_lens=FAKE, q=FAKE, sel=FAKE, n_sel=FAKE, scores=FAKE)
     args.update(ptrs)
     return raw.basiskv_route(C.byref(d.c()), C.byref(f), C.byref(c), args["seq_lens"], args["q"],
-                             args["ws"], ws_bytes, args["sel"], args["n_sel"], args["scores"], None)
+                             args["sel"], args["n_sel"], args["scores"], None)
+
+
+def _decode(lib, d, ws_bytes):
+    raw = lib.basiskv._lib
+    f = lib.basiskv.basiskv_factors(FAKE.value, FAKE.value, FAKE.value, FAKE.value, FAKE.value)
+    c = lib.basiskv.basiskv_cache(FAKE.value, FAKE.value, FAKE.value, FAKE.value, FAKE.value)
+    return raw.basiskv_decode(C.byref(d.c()), C.byref(f), C.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE,
+                              ws_bytes, None, FAKE, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -83,9 +99,10 @@ def test_route_rejects_bad_dims(lib, kw, code):
 
 def test_null_pointers_and_small_workspace(lib):
     assert _route(lib, _dims(lib), sel=None) == -1
-    assert _route(lib, _dims(lib), ws_bytes=0) == -4
+    assert _decode(lib, _dims(lib), 0) == -4
+    assert _decode(lib, _dims(lib), lib.workspace_bytes(_dims(lib)) - 1) == -4
     raw = lib.basiskv._lib
-    assert raw.basiskv_route(None, None, None, None, None, None, 0, None, None, None, None) == -1
+    assert raw.basiskv_route(None, None, None, None, None, None, None, None, None) == -1
 
 
 def test_workspace_bytes(lib):

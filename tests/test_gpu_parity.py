@@ -347,3 +347,59 @@ def test_prefill_matches_oracle(name, chunks):
     np.testing.assert_allclose(np.concatenate(zs), z_ref, rtol=rtol, atol=atol)
     np.testing.assert_allclose(np.concatenate(outs), out_ref, rtol=rtol, atol=atol)
     compare_written(sc, gc.cache_host(g), ora)
+
+
+@pytest.mark.parametrize("name", ["g4_d128_p64", "g8_2kv_r48_p32", "ragged_permuted", "tiny_f32"])
+def test_fused_append_route_equals_separate_calls(name):
+    import routed_decode_attention_amd as rda
+    sc = scenario(name)
+    outs = []
+    for fused in (False, True):
+        g = gc.upload(sc)
+        gc.write_all(g, sc, upto_last=True, chunk=333)
+        B = sc.batch
+        kn = gc.dev(np.stack([sc.K[b][int(sc.lengths[b]) - 1] for b in range(B)]), sc.w.dtype)
+        vn = gc.dev(np.stack([sc.V[b][int(sc.lengths[b]) - 1] for b in range(B)]), sc.w.dtype)
+        pos = torch.from_numpy(np.asarray(sc.lengths, np.int32) - 1).cuda()
+        sel = torch.full((B, g.d.n_kv_heads, g.d.top_k), -7, dtype=torch.int32, device="cuda")
+        n_sel = torch.zeros((B, g.d.n_kv_heads), dtype=torch.int32, device="cuda")
+        scores = torch.zeros((B, g.d.n_kv_heads, g.d.max_pages_per_seq), device="cuda")
+        z = torch.zeros((B, g.d.n_q_heads, g.d.rank_v), device="cuda")
+        out = torch.zeros((B, g.d.d_model), device="cuda")
+        if fused:
+            rda.basiskv_decode_step(g.d, g.f, g.cache, pos, kn, vn, g.seq_lens, g.q, sel, n_sel, scores,
+                                    g.ws, out, z_out=z)
+        else:
+            rda.basiskv_append(g.d, g.f, g.cache, pos, kn, vn)
+            rda.basiskv_route(g.d, g.f, g.cache, g.seq_lens, g.q, sel, n_sel, scores)
+            rda.basiskv_decode(g.d, g.f, g.cache, g.seq_lens, g.q, sel, n_sel, g.ws, out, z_out=z)
+        torch.cuda.synchronize()
+        npg = [-(-int(n) // sc.w.page_size) for n in sc.lengths]
+        sc_host = gc.host(scores)
+        outs.append((gc.cache_host(g), gc.host(sel), gc.host(n_sel),
+                     [sc_host[b, :, :npg[b]] for b in range(B)], gc.host(out), gc.host(z)))
+    a, b = outs
+    for k in a[0]:
+        assert np.array_equal(a[0][k], b[0][k]), k
+    for x, y in zip(a[1:3] + a[4:], b[1:3] + b[4:]):
+        assert np.array_equal(x, y)
+    for x, y in zip(a[3], b[3]):
+        assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("ppw", [1, 2, 3, 5])
+def test_pages_per_wave_plans(ppw, monkeypatch):
+    """Every split plan (one page per wave, or several with the next page's
+    loads overlapping) matches the oracle; the ragged tail of the selection
+    lands in a partly filled wave."""
+    monkeypatch.setenv("BASISKV_PAGES_PER_WAVE", str(ppw))
+    for name in ("g4_d128_p64", "g8_2kv_r48_p32"):
+        w, lengths = CASES[name]
+        w = w.with_(top_k=11)
+        sc = cases.make_scenario(w, lengths=lengths)
+        sel, n_sel, _ = oracle.route(sc.d, sc.fac, sc.cache, sc.lengths, sc.q)
+        z_ref, out_ref = oracle.decode(sc.d, sc.W_ofT, sc.cache, sc.lengths, sc.q, sel, n_sel)
+        g = gc.upload(sc, cache=True, W_ofT=sc.W_ofT)
+        z, out = gc.decode(g, sel, n_sel)
+        np.testing.assert_allclose(z, z_ref, rtol=2e-2, atol=2e-3)
+        np.testing.assert_allclose(out, out_ref, rtol=2e-2, atol=2e-3)
