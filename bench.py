@@ -166,13 +166,16 @@ def main():
         torch.cuda.synchronize()
         return np.array([evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(n)]) * 1e3  # us
 
-    sel_fixed = sel.clone()
-    nsel_fixed = n_sel.clone()
+    sel_phys = torch.zeros_like(sel)
+    rda.basiskv_route(d, f, caches[0], seq_lens, q, sel, n_sel, scores, sel_phys=sel_phys)
+    sel_fixed, nsel_fixed, phys_fixed = sel.clone(), n_sel.clone(), sel_phys.clone()
     n_launch = args.kernel_launches
+    # the attention as the decode step runs it: physical page ids from the router
     t_attend = time_launches(lambda i: rda.basiskv_attend(d, caches[i % L], seq_lens, q, sel_fixed,
-                                                          nsel_fixed, ws, z), n_launch)
+                                                          nsel_fixed, ws, z, sel_phys=phys_fixed), n_launch)
     t_route = time_launches(lambda i: rda.basiskv_append_route(d, f, caches[i % L], pos, k_new, v_new,
-                                                               seq_lens, q, sel, n_sel, scores), n_launch)
+                                                               seq_lens, q, sel, n_sel, scores,
+                                                               sel_phys=sel_phys), n_launch)
     t_project = time_launches(lambda i: rda.basiskv_project(d, f, z, B, out), n_launch)
 
     sb = accounting.decode_step_bytes(w, lengths, selections=gc.host(sel_fixed), n_selected=gc.host(nsel_fixed))

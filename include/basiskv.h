@@ -163,11 +163,14 @@ int basiskv_append(const basiskv_dims *dims, const basiskv_factors *f,
  *   scores [batch][n_kv_heads][max_pages_per_seq] fp32 (required): score(j)
  *          for j < n_pg; entries j >= n_pg are left unspecified;
  *   sel    [batch][n_kv_heads][top_k] int32 ascending logical pages, -1 padded;
- *   n_sel  [batch][n_kv_heads] int32 = min(top_k, n_pg).
+ *   n_sel  [batch][n_kv_heads] int32 = min(top_k, n_pg);
+ *   sel_phys (nullable) [batch][n_kv_heads][top_k] int32: page_table entries of
+ *          sel (-1 padded), which basiskv_attend/decode may take to skip the
+ *          page-table lookup.
  */
 int basiskv_route(const basiskv_dims *dims, const basiskv_factors *f,
                   const basiskv_cache *cache, const int32_t *seq_lens, const void *q,
-                  int32_t *sel, int32_t *n_sel, float *scores, void *stream);
+                  int32_t *sel, int32_t *n_sel, float *scores, int32_t *sel_phys, void *stream);
 
 /*
  * basiskv_append followed by basiskv_route, in one launch (the decode step
@@ -177,7 +180,8 @@ int basiskv_route(const basiskv_dims *dims, const basiskv_factors *f,
 int basiskv_append_route(const basiskv_dims *dims, const basiskv_factors *f,
                          const basiskv_cache *cache, const int32_t *pos, const void *k_new,
                          const void *v_new, const int32_t *seq_lens, const void *q,
-                         int32_t *sel, int32_t *n_sel, float *scores, void *stream);
+                         int32_t *sel, int32_t *n_sel, float *scores, int32_t *sel_phys,
+                         void *stream);
 
 /*
  * Device workspace, in bytes, that basiskv_attend/decode/decode_step (batch
@@ -198,12 +202,13 @@ int basiskv_workspace_init(const basiskv_dims *dims, void *ws, size_t ws_bytes, 
  *   s_t = scale * q_h . k_t   for every token t < seq_lens[b] of every page
  *                             listed in sel[b][g][0 .. n_sel[b][g])
  *   z_out[b][h] = sum_t softmax(s)_t * z~_t          (fp32 [batch][n_q_heads][rank_v])
- * A sequence with no selected page gets z_out = 0.
+ * A sequence with no selected page gets z_out = 0.  sel_phys (nullable): the
+ * physical ids of sel as basiskv_route writes them; NULL looks them up.
  */
 int basiskv_attend(const basiskv_dims *dims, const basiskv_cache *cache,
                    const int32_t *seq_lens, const void *q, const int32_t *sel,
-                   const int32_t *n_sel, void *ws, size_t ws_bytes, float *z_out,
-                   void *stream);
+                   const int32_t *n_sel, const int32_t *sel_phys, void *ws, size_t ws_bytes,
+                   float *z_out, void *stream);
 
 /*
  * Output projection through the folded weights: out[m][c] = sum_x z[m][x] * W_ofT[c][x]
@@ -216,13 +221,13 @@ int basiskv_project(const basiskv_dims *dims, const basiskv_factors *f, const fl
 
 /*
  * One decode layer step after the append: basiskv_attend then basiskv_project
- * over the batch.  z_out may be NULL (the latents then live in the workspace).
- * out: fp32 [batch][d_model].
+ * over the batch.  z_out and sel_phys may be NULL (the latents then live in
+ * the workspace).  out: fp32 [batch][d_model].
  */
 int basiskv_decode(const basiskv_dims *dims, const basiskv_factors *f,
                    const basiskv_cache *cache, const int32_t *seq_lens, const void *q,
-                   const int32_t *sel, const int32_t *n_sel, void *ws, size_t ws_bytes,
-                   float *z_out, float *out, void *stream);
+                   const int32_t *sel, const int32_t *n_sel, const int32_t *sel_phys, void *ws,
+                   size_t ws_bytes, float *z_out, float *out, void *stream);
 
 /*
  * The whole decode layer step in three launches: append + route (one kernel),

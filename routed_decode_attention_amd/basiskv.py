@@ -69,14 +69,14 @@ def _load() -> C.CDLL:
         "basiskv_fold_output": ([D, p, p, p, p], C.c_int),
         "basiskv_write": ([D, Fp, Cp, i32, i32, i32, p, p, p], C.c_int),
         "basiskv_append": ([D, Fp, Cp, p, p, p, p], C.c_int),
-        "basiskv_route": ([D, Fp, Cp, p, p, p, p, p, p], C.c_int),
-        "basiskv_append_route": ([D, Fp, Cp, p, p, p, p, p, p, p, p, p], C.c_int),
+        "basiskv_route": ([D, Fp, Cp, p, p, p, p, p, p, p], C.c_int),
+        "basiskv_append_route": ([D, Fp, Cp, p, p, p, p, p, p, p, p, p, p], C.c_int),
         "basiskv_decode_step": ([D, Fp, Cp, p, p, p, p, p, p, p, p, p, sz, p, p, p], C.c_int),
         "basiskv_workspace_bytes": ([D, i32], sz),
         "basiskv_workspace_init": ([D, p, sz, p], C.c_int),
-        "basiskv_attend": ([D, Cp, p, p, p, p, p, sz, p, p], C.c_int),
+        "basiskv_attend": ([D, Cp, p, p, p, p, p, p, sz, p, p], C.c_int),
         "basiskv_project": ([D, Fp, p, i32, p, p], C.c_int),
-        "basiskv_decode": ([D, Fp, Cp, p, p, p, p, p, sz, p, p, p], C.c_int),
+        "basiskv_decode": ([D, Fp, Cp, p, p, p, p, p, p, sz, p, p, p], C.c_int),
         "basiskv_prefill": ([D, Fp, Cp, i32, i32, i32, p, p, p, p, sz, p, p, p], C.c_int),
     }
     for name, (args, res) in sig.items():
@@ -245,7 +245,8 @@ def basiskv_workspace_init(d: Dims, ws: torch.Tensor, stream=None) -> None:
 
 
 def basiskv_route(d: Dims, f: Factors, cache: Cache, seq_lens: torch.Tensor, q: torch.Tensor,
-                  sel: torch.Tensor, n_sel: torch.Tensor, scores: torch.Tensor, stream=None) -> None:
+                  sel: torch.Tensor, n_sel: torch.Tensor, scores: torch.Tensor, sel_phys=None,
+                  stream=None) -> None:
     pairs = d.batch * d.n_kv_heads
     fc, cc = f.c(d), cache.c(d)
     _check(_lib.basiskv_route(
@@ -253,13 +254,14 @@ def basiskv_route(d: Dims, f: Factors, cache: Cache, seq_lens: torch.Tensor, q: 
         _ptr(seq_lens, "seq_lens", torch.int32, d.batch),
         _ptr(q, "q", d.torch_dtype, d.batch * d.n_q_heads * d.head_dim),
         _ptr(sel, "sel", torch.int32, pairs * d.top_k), _ptr(n_sel, "n_sel", torch.int32, pairs),
-        _ptr(scores, "scores", torch.float32, pairs * d.max_pages_per_seq), _stream(stream)))
+        _ptr(scores, "scores", torch.float32, pairs * d.max_pages_per_seq),
+        _ptr(sel_phys, "sel_phys", torch.int32, pairs * d.top_k), _stream(stream)))
 
 
 def basiskv_append_route(d: Dims, f: Factors, cache: Cache, pos: torch.Tensor, k_new: torch.Tensor,
                          v_new: torch.Tensor, seq_lens: torch.Tensor, q: torch.Tensor,
                          sel: torch.Tensor, n_sel: torch.Tensor, scores: torch.Tensor,
-                         stream=None) -> None:
+                         sel_phys=None, stream=None) -> None:
     pairs = d.batch * d.n_kv_heads
     need = d.batch * d.n_kv_heads * d.head_dim
     fc, cc = f.c(d), cache.c(d)
@@ -269,7 +271,8 @@ def basiskv_append_route(d: Dims, f: Factors, cache: Cache, pos: torch.Tensor, k
         _ptr(seq_lens, "seq_lens", torch.int32, d.batch),
         _ptr(q, "q", d.torch_dtype, d.batch * d.n_q_heads * d.head_dim),
         _ptr(sel, "sel", torch.int32, pairs * d.top_k), _ptr(n_sel, "n_sel", torch.int32, pairs),
-        _ptr(scores, "scores", torch.float32, pairs * d.max_pages_per_seq), _stream(stream)))
+        _ptr(scores, "scores", torch.float32, pairs * d.max_pages_per_seq),
+        _ptr(sel_phys, "sel_phys", torch.int32, pairs * d.top_k), _stream(stream)))
 
 
 def basiskv_decode_step(d: Dims, f: Factors, cache: Cache, pos, k_new, v_new, seq_lens, q, sel, n_sel,
@@ -289,13 +292,15 @@ def basiskv_decode_step(d: Dims, f: Factors, cache: Cache, pos, k_new, v_new, se
         _ptr(out, "out", torch.float32, d.batch * d.d_model), _stream(stream)))
 
 
-def basiskv_attend(d: Dims, cache: Cache, seq_lens, q, sel, n_sel, ws, z_out, stream=None) -> None:
+def basiskv_attend(d: Dims, cache: Cache, seq_lens, q, sel, n_sel, ws, z_out, sel_phys=None,
+                   stream=None) -> None:
     pairs = d.batch * d.n_kv_heads
     cc = cache.c(d)
     _check(_lib.basiskv_attend(
         C.byref(d.c()), C.byref(cc), _ptr(seq_lens, "seq_lens", torch.int32, d.batch),
         _ptr(q, "q", d.torch_dtype, d.batch * d.n_q_heads * d.head_dim),
         _ptr(sel, "sel", torch.int32, pairs * d.top_k), _ptr(n_sel, "n_sel", torch.int32, pairs),
+        _ptr(sel_phys, "sel_phys", torch.int32, pairs * d.top_k),
         _ptr(ws, "ws", torch.uint8), ws.numel(),
         _ptr(z_out, "z_out", torch.float32, d.batch * d.n_q_heads * d.rank_v), _stream(stream)))
 
@@ -310,13 +315,14 @@ def basiskv_project(d: Dims, f: Factors, z: torch.Tensor, rows: int, out: torch.
 
 
 def basiskv_decode(d: Dims, f: Factors, cache: Cache, seq_lens, q, sel, n_sel, ws, out,
-                   z_out=None, stream=None) -> None:
+                   z_out=None, sel_phys=None, stream=None) -> None:
     pairs = d.batch * d.n_kv_heads
     fc, cc = f.c(d), cache.c(d)
     _check(_lib.basiskv_decode(
         C.byref(d.c()), C.byref(fc), C.byref(cc), _ptr(seq_lens, "seq_lens", torch.int32, d.batch),
         _ptr(q, "q", d.torch_dtype, d.batch * d.n_q_heads * d.head_dim),
         _ptr(sel, "sel", torch.int32, pairs * d.top_k), _ptr(n_sel, "n_sel", torch.int32, pairs),
+        _ptr(sel_phys, "sel_phys", torch.int32, pairs * d.top_k),
         _ptr(ws, "ws", torch.uint8), ws.numel(),
         _ptr(z_out, "z_out", torch.float32, d.batch * d.n_q_heads * d.rank_v),
         _ptr(out, "out", torch.float32, d.batch * d.d_model), _stream(stream)))

@@ -262,7 +262,7 @@ int basiskv_append(const basiskv_dims* dims, const basiskv_factors* f, const bas
 
 int basiskv_route(const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
                   const int32_t* seq_lens, const void* q, int32_t* sel, int32_t* n_sel, float* scores,
-                  void* stream) {
+                  int32_t* sel_phys, void* stream) {
   bkv::Shape s;
   int rc = check_dims(dims, &s);
   if (rc) return rc;
@@ -270,12 +270,13 @@ int basiskv_route(const basiskv_dims* dims, const basiskv_factors* f, const basi
   if ((rc = check_cache(cache, false, false, false))) return rc;
   if (!seq_lens || !q || !sel || !n_sel || !scores)
     return fail(BASISKV_E_NULL, "route: seq_lens, q, sel, n_sel and scores are required");
-  return do_route(s, f, cache, nullptr, nullptr, nullptr, seq_lens, q, sel, n_sel, scores, stream);
+  return do_route(s, f, cache, nullptr, nullptr, nullptr, seq_lens, q, sel, n_sel, scores, stream, sel_phys);
 }
 
 int basiskv_append_route(const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
                          const int32_t* pos, const void* k_new, const void* v_new, const int32_t* seq_lens,
-                         const void* q, int32_t* sel, int32_t* n_sel, float* scores, void* stream) {
+                         const void* q, int32_t* sel, int32_t* n_sel, float* scores, int32_t* sel_phys,
+                         void* stream) {
   bkv::Shape s;
   int rc = check_dims(dims, &s);
   if (rc) return rc;
@@ -284,7 +285,7 @@ int basiskv_append_route(const basiskv_dims* dims, const basiskv_factors* f, con
   if ((rc = check_cache(cache, true, true, true))) return rc;
   if (!pos || !k_new || !v_new || !seq_lens || !q || !sel || !n_sel || !scores)
     return fail(BASISKV_E_NULL, "append_route: pos, k_new, v_new, seq_lens, q, sel, n_sel, scores required");
-  return do_route(s, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, stream);
+  return do_route(s, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, stream, sel_phys);
 }
 
 size_t basiskv_workspace_bytes(const basiskv_dims* dims, int32_t max_prefill_tokens) {
@@ -306,15 +307,15 @@ int basiskv_workspace_init(const basiskv_dims* dims, void* ws, size_t ws_bytes, 
 }
 
 int basiskv_attend(const basiskv_dims* dims, const basiskv_cache* cache, const int32_t* seq_lens,
-                   const void* q, const int32_t* sel, const int32_t* n_sel, void* ws, size_t ws_bytes,
-                   float* z_out, void* stream) {
+                   const void* q, const int32_t* sel, const int32_t* n_sel, const int32_t* sel_phys, void* ws,
+                   size_t ws_bytes, float* z_out, void* stream) {
   bkv::Shape s;
   int rc = check_dims(dims, &s);
   if (rc) return rc;
   if ((rc = check_cache(cache, true, true, false))) return rc;
   if (!seq_lens || !q || !sel || !n_sel || !ws || !z_out)
     return fail(BASISKV_E_NULL, "attend: seq_lens, q, sel, n_sel, ws and z_out are required");
-  return do_attend(s, cache, seq_lens, q, sel, n_sel, ws, ws_bytes, z_out, stream);
+  return do_attend(s, cache, seq_lens, q, sel, n_sel, ws, ws_bytes, z_out, stream, sel_phys);
 }
 
 int basiskv_project(const basiskv_dims* dims, const basiskv_factors* f, const float* z, int32_t rows,
@@ -329,7 +330,7 @@ int basiskv_project(const basiskv_dims* dims, const basiskv_factors* f, const fl
 
 int basiskv_decode(const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
                    const int32_t* seq_lens, const void* q, const int32_t* sel, const int32_t* n_sel,
-                   void* ws, size_t ws_bytes, float* z_out, float* out, void* stream) {
+                   const int32_t* sel_phys, void* ws, size_t ws_bytes, float* z_out, float* out, void* stream) {
   bkv::Shape s;
   int rc = check_dims(dims, &s);
   if (rc) return rc;
@@ -341,7 +342,7 @@ int basiskv_decode(const basiskv_dims* dims, const basiskv_factors* f, const bas
   if (ws_bytes < L.total)
     return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, decode needs %zu", ws_bytes, L.total);
   float* z = z_out ? z_out : reinterpret_cast<float*>(static_cast<char*>(ws) + L.z);
-  if ((rc = do_attend(s, cache, seq_lens, q, sel, n_sel, ws, ws_bytes, z, stream))) return rc;
+  if ((rc = do_attend(s, cache, seq_lens, q, sel, n_sel, ws, ws_bytes, z, stream, sel_phys))) return rc;
   return do_project(s, f, z, s.batch, out, stream);
 }
 

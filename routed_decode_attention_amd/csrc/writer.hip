@@ -63,9 +63,15 @@ __global__ __launch_bounds__(THREADS) void write_kernel(WriteArgs a) {
   float* s_z = s_k + TB * D;  // [TB][R] stored latents
   float* sZp = s_z + TB * R;  // [R][ps+1] the page's stored latents, for its sums
   float* sSp = sZp + R * (ps + 1);  // [ps][RK] ... and residuals
-  stage_matrix(sB, R, a.B + (size_t)g * D * R, D, R);
-  stage_matrix(sP, LDP, a.P + (size_t)g * R * D, R, D);
-  stage_matrix(sRe, RK, a.R_enc + (size_t)g * D * RK, D, RK);
+  {
+    StageList L;
+    L.it[0] = StageItem{sB, a.B + (size_t)g * D * R, R, D, R};
+    L.it[1] = StageItem{sP, a.P + (size_t)g * R * D, LDP, R, D};
+    L.it[2] = StageItem{sRe, a.R_enc + (size_t)g * D * RK, RK, D, RK};
+    L.it[3] = L.it[2];
+    L.n = 3;
+    stage_matrices(L);
+  }
 
   const int page = t0 / ps;
   const int phys = a.page_table[(size_t)b * a.s.max_pages + page];

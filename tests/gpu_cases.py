@@ -107,11 +107,12 @@ def route(g: Dev, q: Optional[torch.Tensor] = None):
     return host(sel), host(n_sel), host(scores)
 
 
-def decode(g: Dev, sel: np.ndarray, n_sel: np.ndarray):
+def decode(g: Dev, sel: np.ndarray, n_sel: np.ndarray, sel_phys: Optional[np.ndarray] = None):
     z = torch.full((g.d.batch, g.d.n_q_heads, g.d.rank_v), float("nan"), device="cuda")
     out = torch.full((g.d.batch, g.d.d_model), float("nan"), device="cuda")
+    phys = None if sel_phys is None else torch.from_numpy(sel_phys).cuda()
     rda.basiskv_decode(g.d, g.f, g.cache, g.seq_lens, g.q, torch.from_numpy(sel).cuda(),
-                       torch.from_numpy(n_sel).cuda(), g.ws, out, z_out=z)
+                       torch.from_numpy(n_sel).cuda(), g.ws, out, z_out=z, sel_phys=phys)
     torch.cuda.synchronize()
     return host(z).astype(np.float64), host(out).astype(np.float64)
 

@@ -206,6 +206,27 @@ def test_decode_matches_oracle(name):
     rtol, atol = gc.tol(sc.w)
     np.testing.assert_allclose(z, z_ref, rtol=rtol, atol=atol)
     np.testing.assert_allclose(out, out_ref, rtol=rtol, atol=atol)
+    # the same with physical page ids handed in: bit-identical
+    phys = np.where(sel >= 0, np.take_along_axis(sc.page_table[:, None, :], np.maximum(sel, 0), axis=2), -1)
+    z2, out2 = gc.decode(g, sel, n_sel, sel_phys=np.ascontiguousarray(phys, np.int32))
+    assert np.array_equal(z, z2) and np.array_equal(out, out2)
+
+
+@pytest.mark.parametrize("name", ["g4_d128_p64", "ragged_permuted", "g8_2kv_r48_p32"])
+def test_route_physical_ids(name):
+    import routed_decode_attention_amd as rda
+    sc = scenario(name)
+    g = gc.upload(sc, cache=True)
+    B, H, K = sc.batch, sc.w.n_kv_heads, sc.w.top_k
+    sel = torch.full((B, H, K), -7, dtype=torch.int32, device="cuda")
+    n_sel = torch.zeros((B, H), dtype=torch.int32, device="cuda")
+    phys = torch.full((B, H, K), -7, dtype=torch.int32, device="cuda")
+    scores = torch.zeros((B, H, g.d.max_pages_per_seq), device="cuda")
+    rda.basiskv_route(g.d, g.f, g.cache, g.seq_lens, g.q, sel, n_sel, scores, sel_phys=phys)
+    torch.cuda.synchronize()
+    s_, p_ = gc.host(sel), gc.host(phys)
+    want = np.where(s_ >= 0, np.take_along_axis(sc.page_table[:, None, :], np.maximum(s_, 0), axis=2), -1)
+    assert np.array_equal(p_, want)
 
 
 @pytest.mark.parametrize("name", ["g4_d128_p64", "g8_2kv_r48_p32", "ragged_permuted"])
