@@ -116,3 +116,88 @@ def check_selection_valid(ref_scores: np.ndarray, chosen: Sequence[int], k: int,
     lo = min(float(ref_scores[j]) for j in chosen)
     hi = max(float(ref_scores[j]) for j in rest)
     assert lo >= hi - rtol * max(abs(lo), abs(hi), 1e-30), (lo, hi)
+
+
+U32 = 2.0 ** -24  # fp32 unit roundoff
+
+
+def ulp(x: np.ndarray, dtype: int) -> np.ndarray:
+    """Spacing of the storage dtype at |x| (bf16: 8 significant bits, fp32: 24)."""
+    bits = 8 if dtype == BF16 else 24
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return 2.0 ** (e - bits + 1)
+
+
+def check_rounded_dot(got, ref, n_terms, mag, dtype, extra=0.0, exact_frac=None):
+    """A stored result of an n-term fp32 dot product against the oracle's
+    correctly rounded one: |got - ref| <= n*u*sum|terms| + extra + one
+    storage ulp (both sides round once; fp32 accumulation error bound)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    bound = n_terms * U32 * mag + extra + ulp(np.maximum(np.abs(got), np.abs(ref)), dtype)
+    bad = np.abs(got - ref) > bound
+    assert not bad.any(), (np.argwhere(bad)[:5], got[bad][:5], ref[bad][:5], bound[bad][:5])
+    if exact_frac is not None:
+        assert (got == ref).mean() >= exact_frac
+
+
+def _valid_slots(sc, page_table):
+    """(page, slot) of every written token, and the tokens' Keys/Values in that order."""
+    P, T, K, V = [], [], [], []
+    ps = sc.w.page_size
+    for b, n in enumerate(sc.lengths):
+        for t in range(int(n)):
+            P.append(page_table[b, t // ps])
+            T.append(t % ps)
+        K.append(sc.K[b][:int(n)])
+        V.append(sc.V[b][:int(n)])
+    return np.array(P), np.array(T), np.concatenate(K), np.concatenate(V)
+
+
+def compare_written(sc, got, ora, got_page_table=None):
+    """A GPU-written cache (host arrays K, Z, S, summ) against the oracle-written
+    one: Keys bit for bit; latents and residuals within the fp32 accumulation
+    bound plus one storage ulp of the oracle's correctly rounded values (at
+    least 99% / 98% identical in bf16); page sums equal to the fp32 slot-order
+    sum of the GPU's own stored values.  got_page_table: the GPU's placement
+    of the scenario's rows (default: the scenario's own)."""
+    w = sc.w
+    dt = w.dtype
+    D, R, RK = w.head_dim, w.rank_v, w.rank_k
+    gpt = sc.page_table if got_page_table is None else got_page_table
+    P, T, Kt, Vt = _valid_slots(sc, sc.page_table)
+    Pg, _, _, _ = _valid_slots(sc, gpt)
+    # exact Keys, bit for bit
+    assert np.array_equal(got["K"][Pg, :, T], ora.K[P, :, T])
+    zg = synth.storage_to_f64(got["Z"][Pg, :, :, T], dt)   # [tokens][H][R]
+    zo = synth.storage_to_f64(ora.Z[P, :, :, T], dt)
+    sg = synth.storage_to_f64(got["S"][Pg, :, T], dt)      # [tokens][H][RK]
+    so = synth.storage_to_f64(ora.S[P, :, T], dt)
+    K = synth.storage_to_f64(Kt, dt)
+    V = synth.storage_to_f64(Vt, dt)
+    frac = 0.99 if dt == BF16 else None
+    for g in range(w.n_kv_heads):
+        B = np.abs(sc.fac.B[g].astype(np.float64))
+        Pm = np.abs(sc.fac.P[g].astype(np.float64))
+        Re = np.abs(sc.fac.R_enc[g].astype(np.float64))
+        # latent z = v.B: D terms
+        check_rounded_dot(zg[:, g], zo[:, g], D, np.abs(V[:, g]) @ B, dt, exact_frac=frac)
+        # residual s = (k - z~.P).R_enc: the latent's own difference propagates,
+        # then R + D accumulated terms
+        prop = (np.abs(zg[:, g] - zo[:, g]) @ Pm) @ Re
+        mag = (np.abs(K[:, g]) + np.abs(zo[:, g]) @ Pm) @ Re
+        check_rounded_dot(sg[:, g], so[:, g], D + R, mag, dt, extra=prop,
+                          exact_frac=0.98 if dt == BF16 else None)
+    # page sums: the fp32 sum of the GPU's own stored values, in slot order
+    ps = w.page_size
+    vz = synth.storage_to_f64(got["Z"], dt)
+    vs = synth.storage_to_f64(got["S"], dt)
+    for b, n in enumerate(sc.lengths):
+        for j in range(-(-int(n) // ps)):
+            p = gpt[b, j]
+            cnt = min(ps, int(n) - j * ps)
+            for g in range(w.n_kv_heads):
+                x = np.concatenate([vz[p, g, :, :cnt].T, vs[p, g, :cnt, :]], axis=1)  # [cnt][R+RK]
+                ref = x.sum(axis=0)
+                bound = cnt * U32 * np.abs(x).sum(axis=0) + 1e-30
+                assert np.all(np.abs(got["summ"][p, g] - ref) <= bound), (b, j, g)
