@@ -35,6 +35,24 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def measured_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE x its measured copy scale + WRITE_SIZE), or None when
+    the attention kernel's source has changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "attend_llama8b_32k_counters.md")
+    src = os.path.join(ROOT, "routed_decode_attention_amd", "csrc", "attend.hip")
+    try:
+        text = open(path).read()
+        want = re.search(r"attend\.hip sha256: ([0-9a-f]{64})", text).group(1)
+        traffic = int(re.search(r"traffic bytes per launch: (\d+)", text).group(1))
+    except (OSError, AttributeError):
+        return None
+    have = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    return traffic if have == want else None
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
@@ -58,7 +76,6 @@ def main():
 
     import torch
     import routed_decode_attention_amd as rda
-    from tests import cases
     from tests import gpu_cases as gc
     from workloads import accounting, configs, synth
 
@@ -154,17 +171,19 @@ def main():
     log(f"{steps} steps in {ms:.2f} ms (wall {t_wall * 1e3:.1f} ms): {ms_per_step * 1e3:.2f} us/step, "
         f"{tokens_per_s / 1e6:.3f} M tokens/s per layer step")
 
-    # ---- per-kernel launch durations, live, GPU kept busy so launches run back to back
+    # ---- per-kernel launch durations, live: n back-to-back launches between two
+    # events on the stream they run on, queued while the GPU spins so that no
+    # host gap enters (the mean agrees with rocprofv3's kernel durations) ----
     def time_launches(fn, n):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         torch.cuda._sleep(int(2.0e8))  # ~0.1 s of GPU spin while the launches are queued
+        e0.record()
         for i in range(n):
-            evs[2 * i].record()
             fn(i)
-            evs[2 * i + 1].record()
+        e1.record()
         torch.cuda.synchronize()
-        return np.array([evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(n)]) * 1e3  # us
+        return e0.elapsed_time(e1) * 1e3 / n  # us per launch
 
     sel_phys = torch.zeros_like(sel)
     rda.basiskv_route(d, f, caches[0], seq_lens, q, sel, n_sel, scores, sel_phys=sel_phys)
@@ -180,21 +199,22 @@ def main():
 
     sb = accounting.decode_step_bytes(w, lengths, selections=gc.host(sel_fixed), n_selected=gc.host(nsel_fixed))
     attend_bytes = sb.attend_kernel
-    att_us = float(np.mean(t_attend))
+    att_us = float(t_attend)
     achieved = attend_bytes / (att_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "kernel": "attend_mfma_kernel<128,64,32>", "bytes_per_launch": attend_bytes,
                 "avg_launch_us": round(att_us, 3), "launches": n_launch}
     step_tbs = sb.total / (ms_per_step * 1e-3) / 1e12
     log(f"attend {att_us:.2f} us ({achieved:.0f} GB/s, {100 * achieved / HBM_PEAK_GBS:.1f}% of 8 TB/s); "
-        f"append+route {np.mean(t_route):.2f} us, project {np.mean(t_project):.2f} us")
+        f"append+route {t_route:.2f} us, project {t_project:.2f} us")
 
     # ---- CPU baseline: the oracle timed on the same workload; its outputs are
     # also the parity reference of the GPU step ----------------------------------
     cpu, parity = None, None
     if not args.no_cpu:
         import oracle
+        from tests import cases
         cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
         full = cases.make_scenario(w, seed=args.seed, upto_last=True)
         kn = np.stack([full.K[b][int(lengths[b]) - 1:int(lengths[b])] for b in range(B)])
@@ -250,8 +270,8 @@ def main():
                    "layers_rotated": L, "graph_captured": True},
         "hbm_step": {"algorithmic_bytes": sb.total, "TB_per_s": round(step_tbs, 3),
                      "frac_of_8TBs": round(step_tbs / 8.0, 4)},
-        "kernels_us": {"append_route": round(float(np.mean(t_route)), 3),
-                       "attend": round(att_us, 3), "project": round(float(np.mean(t_project)), 3)},
+        "kernels_us": {"append_route": round(float(t_route), 3),
+                       "attend": round(att_us, 3), "project": round(float(t_project), 3)},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": parity,
