@@ -249,18 +249,27 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttendArgs a) {
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, qd = lane >> 4;
 
+  const int first = (split * ATTEND_WAVES + wave) * a.pages_per_wave;
+  // this wave's slice of the selection is read in the same round trip as the
+  // sequence length and the selection count (every slot < top_k is in bounds;
+  // slots past the count are masked below)
+  int my_j = 0, my_phys = 0;
+  const bool in_list = lane < a.pages_per_wave && first + lane < a.s.top_k;
+  if (in_list) {
+    const size_t at = (size_t)pair * a.s.top_k + first + lane;
+    my_j = a.sel[at];
+    if (a.sel_phys) my_phys = a.sel_phys[at];
+  }
   const int seq_len = a.seq_lens[b];
   const int nsel = seq_len > 0 ? a.n_sel[pair] : 0;
-  const int first = (split * ATTEND_WAVES + wave) * a.pages_per_wave;
   const int np = max(0, min(first + a.pages_per_wave, nsel) - first);  // pages of this wave
-
   // page ids and valid-token counts of this wave's pages, lane u holds page u
-  int my_phys = 0, my_cnt = 0;
+  int my_cnt = 0;
   if (lane < np) {
-    const size_t at = (size_t)pair * a.s.top_k + first + lane;
-    const int j = a.sel[at];
-    my_phys = a.sel_phys ? a.sel_phys[at] : a.page_table[(size_t)b * a.s.max_pages + j];
-    my_cnt = min(PS, seq_len - j * PS);
+    if (!a.sel_phys) my_phys = a.page_table[(size_t)b * a.s.max_pages + my_j];
+    my_cnt = min(PS, seq_len - my_j * PS);
+  } else {
+    my_phys = 0;
   }
   bf16x8 qb[KS];
   {

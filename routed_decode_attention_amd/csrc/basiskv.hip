@@ -176,6 +176,9 @@ int do_write(const bkv::Shape& s, const basiskv_factors* f, const basiskv_cache*
 int do_route(const bkv::Shape& s, const basiskv_factors* f, const basiskv_cache* cache, const int32_t* pos,
              const void* k_new, const void* v_new, const int32_t* seq_lens, const void* q, int32_t* sel,
              int32_t* n_sel, float* scores, void* stream, int32_t* sel_phys = nullptr) {
+  if (!bkv::route_fits(s, pos != nullptr))
+    return fail(BASISKV_E_UNSUPPORTED, "route: page table of %d pages with these factor sizes exceeds the LDS",
+                s.max_pages);
   bkv::RouteArgs a;
   a.s = s;
   a.B = f->B;

@@ -46,6 +46,23 @@ __device__ __forceinline__ float round_only(float x, const uint16_t*) {
   return bf16_to_f32(f32_to_bf16(x));
 }
 
+// Element k of a 16-byte chunk of storage-dtype values, as fp32.
+template <typename T>
+__device__ __forceinline__ float unpack_elem(const u32x4& w, int k) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t x = w[k >> 1];
+    return __uint_as_float(((k & 1) ? (x >> 16) : (x & 0xffffu)) << 16);
+  } else {
+    return __uint_as_float(w[k]);
+  }
+}
+
+// Store a value that is exactly representable in the storage dtype.
+__device__ __forceinline__ void store_elem(float* p, size_t i, float x) { p[i] = x; }
+__device__ __forceinline__ void store_elem(uint16_t* p, size_t i, float x) {
+  p[i] = static_cast<uint16_t>(__float_as_uint(x) >> 16);
+}
+
 // 16-byte global load as an MFMA bf16x8 operand.
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
   u32x4 v = *reinterpret_cast<const u32x4*>(p);

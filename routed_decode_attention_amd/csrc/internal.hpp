@@ -91,6 +91,7 @@ struct AttendPlan {
 AttendPlan plan_attend(const Shape& s);
 
 bool attend_mfma_supported(const Shape& s);
+bool route_fits(const Shape& s, bool append);  // the router's LDS fits one CU
 bool project_mfma_supported(int kdim, int n, int dtype);
 bool prefill_mfma_supported(const Shape& s);
 

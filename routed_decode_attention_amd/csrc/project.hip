@@ -37,35 +37,46 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void project_mfma_kernel(Pr
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = 0; k0 < a.kdim; k0 += 32) {
-    bf16x8 af[WM], al[WM], bfr[WN];
+  // KB slices of 32 along the contraction per batch: every fragment of a
+  // batch is loaded before its first MFMA (one memory round trip per batch).
+  constexpr int KB = (WM + WN) <= 2 ? 8 : 2;
+  for (int k0 = 0; k0 < a.kdim; k0 += 32 * KB) {
+    float4 zr[KB][WM][2];
+    bf16x8 bfr[KB][WN];
 #pragma unroll
-    for (int i = 0; i < WM; ++i) {
-      const int row = row0 + 16 * i + n;
-      if (row < a.rows) {
-        const float4* zp = reinterpret_cast<const float4*>(a.z + (size_t)row * a.kdim + k0 + 8 * qd);
-        const float4 x0 = zp[0], x1 = zp[1];
-        const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    for (int kb = 0; kb < KB; ++kb) {
+      const int k = k0 + 32 * kb;
+      if (k < a.kdim) {
+#pragma unroll
+        for (int i = 0; i < WM; ++i) {
+          const int row = row0 + 16 * i + n;
+          const float4* zp = reinterpret_cast<const float4*>(a.z + (size_t)row * a.kdim + k + 8 * qd);
+          zr[kb][i][0] = row < a.rows ? zp[0] : float4{0.f, 0.f, 0.f, 0.f};
+          zr[kb][i][1] = row < a.rows ? zp[1] : float4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int j = 0; j < WN; ++j) bfr[kb][j] = load_bf16x8(W + (size_t)(col0 + 16 * j + n) * a.kdim + k + 8 * qd);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      if (k0 + 32 * kb >= a.kdim) break;
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        const float x[8] = {zr[kb][i][0].x, zr[kb][i][0].y, zr[kb][i][0].z, zr[kb][i][0].w,
+                            zr[kb][i][1].x, zr[kb][i][1].y, zr[kb][i][1].z, zr[kb][i][1].w};
         float lo[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) lo[e] = x[e] - bf16_to_f32(f32_to_bf16(x[e]));
-        af[i] = pack_bf16x8(x);
-        al[i] = pack_bf16x8(lo);
-      } else {
-        af[i] = zero_bf16x8();
-        al[i] = zero_bf16x8();
+        const bf16x8 af = pack_bf16x8(x), al = pack_bf16x8(lo);
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[kb][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bfr[kb][j], acc[i][j], 0, 0, 0);
+        }
       }
     }
-#pragma unroll
-    for (int j = 0; j < WN; ++j)
-      bfr[j] = load_bf16x8(W + (size_t)(col0 + 16 * j + n) * a.kdim + k0 + 8 * qd);
-#pragma unroll
-    for (int i = 0; i < WM; ++i)
-#pragma unroll
-      for (int j = 0; j < WN; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
   }
 #pragma unroll
   for (int i = 0; i < WM; ++i)

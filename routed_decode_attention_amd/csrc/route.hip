@@ -15,12 +15,18 @@
 // "KV-кэширование", "Фаза Decode"), so the fused variant writes it first.
 //
 // One 512-thread workgroup per (sequence, KV head), no cross-workgroup
-// traffic: the factors are staged in LDS (P and R_dec rows padded to 16-byte
-// aligned strides for float4 dot products), one lane scores one page from its
-// fp32 sums with every load of the kernel's front in flight at once; an
-// MSB-first 8-bit radix select over order-preserving keys in LDS (per-wave
-// histograms merged once per pass) finds the k-th score, and ballots plus
-// per-wave counts compact the selection in page order.
+// traffic.  The kernel is a short chain of memory round trips, and its
+// serial parts are kept to few instructions:
+//   1. the page-table row, the factors, the query and the new token are
+//      copied straight into LDS together (16-byte direct loads);
+//   2. every lane requests the sums of its first page; meanwhile wave 0
+//      appends the new token (the writer's wave functions, then the page's
+//      sums from scratch over its LDS image) and the other waves project
+//      the query through P and R_dec, four lanes per output;
+//   3. one lane scores one page from its fp32 sums held in registers;
+//   4. an MSB-first 8-bit radix select over order-preserving keys in LDS
+//      (per-wave histograms merged once per pass) finds the k-th score, and
+//      ballots plus per-wave counts compact the selection in page order.
 #include "common.hpp"
 #include "internal.hpp"
 #include "token_math.hpp"
@@ -30,242 +36,229 @@ namespace bkv {
 namespace {
 
 constexpr int RT = 512;
-constexpr int VMAX = 64;  // page-sum channels held in registers per pass
+constexpr int NW = RT / 64;
+constexpr int VMAX = 64;                      // page-sum channels held in registers per pass
+constexpr int XMAX = MAX_RANK + MAX_RESID;    // projected-query width bound
 
-// One staging round: every 16-byte chunk of every item is loaded before the
-// first LDS store, so the whole front of the kernel costs one memory round
-// trip.  Items: fp32 matrices (rows padded to ld floats), storage-dtype
-// vectors (converted to fp32), and a latent page (channel rows padded to
-// ps+1 floats).
-enum ChunkKind { CK_F32_MATRIX = 0, CK_VECTOR = 1, CK_ZPAGE = 2 };
-struct ChunkItem {
-  const void* src;
-  float* dst;
-  int n16;    // 16-byte chunks
-  int kind;
-  int cols;   // CK_F32_MATRIX: row length; CK_ZPAGE: page size
-  int ld;     // CK_F32_MATRIX: LDS row stride
-};
-constexpr int MAX_ITEMS = 9;
-constexpr int CHUNKS_PER_THREAD = 8;
-
-template <typename T>
-__device__ __forceinline__ void stage_chunks(const ChunkItem (&it)[MAX_ITEMS], int n_items) {
-  constexpr int PER = 16 / sizeof(T);
-  int start[MAX_ITEMS + 1];
-  start[0] = 0;
-#pragma unroll
-  for (int m = 0; m < MAX_ITEMS; ++m) start[m + 1] = start[m] + (m < n_items ? it[m].n16 : 0);
-  const int total = start[MAX_ITEMS];
-  for (int base = threadIdx.x; base < total; base += RT * CHUNKS_PER_THREAD) {
-    u32x4 v[CHUNKS_PER_THREAD];
-#pragma unroll
-    for (int u = 0; u < CHUNKS_PER_THREAD; ++u) {
-      const int c = base + u * RT;
-      if (c < total) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(it[0].src) + c;
-#pragma unroll
-        for (int m = 1; m < MAX_ITEMS; ++m)
-          if (c >= start[m]) src = reinterpret_cast<const u32x4*>(it[m].src) + (c - start[m]);
-        v[u] = *src;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < CHUNKS_PER_THREAD; ++u) {
-      const int c = base + u * RT;
-      if (c >= total) continue;
-      int m = 0;
-#pragma unroll
-      for (int mm = 1; mm < MAX_ITEMS; ++mm)
-        if (c >= start[mm]) m = mm;
-      int cc = c, kind = it[0].kind, cols = it[0].cols, ld = it[0].ld;
-      float* dst = it[0].dst;
-#pragma unroll
-      for (int mm = 1; mm < MAX_ITEMS; ++mm)
-        if (mm == m) {
-          cc = c - start[mm];
-          kind = it[mm].kind;
-          cols = it[mm].cols;
-          ld = it[mm].ld;
-          dst = it[mm].dst;
-        }
-      if (kind == CK_F32_MATRIX) {
-        const int e = cc * 4;
-        float* d = dst + (e / cols) * ld + e % cols;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) d[k] = __uint_as_float(v[u][k]);
-      } else {
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-          const uint32_t w = v[u][k * sizeof(T) / 4];
-          const float f = sizeof(T) == 2 ? __uint_as_float(((k & 1) ? (w >> 16) : (w & 0xffffu)) << 16)
-                                         : __uint_as_float(w);
-          const int e = cc * PER + k;
-          if (kind == CK_VECTOR) dst[e] = f;
-          else dst[(e / cols) * (cols + 1) + e % cols] = f;
-        }
-      }
-    }
-  }
+// Sum over the four lanes of a quad (every lane gets the total).
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // lanes ^1
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // lanes ^2
+  return x;
 }
 
-template <typename T, bool APPEND>
+// Four consecutive storage-dtype elements from LDS as fp32.
+__device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 lds4(const uint16_t* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+               __uint_as_float(w.y & 0xffff0000u)};
+}
+
+// Dynamic LDS layout (bytes, every part 16-byte aligned).
+struct RouteLds {
+  size_t pid, P, Rd, q, B, Re, vk, img, total;
+};
+__host__ __device__ inline size_t a16(size_t x) { return (x + 15) & ~(size_t)15; }
+__host__ __device__ inline RouteLds route_lds(int maxp, int D, int R, int RK, int G, int ps, int es, bool append) {
+  RouteLds L;
+  L.pid = 0;
+  L.P = a16((size_t)maxp * 4);
+  L.Rd = L.P + (size_t)R * D * 4;
+  L.q = L.Rd + (size_t)RK * D * 4;
+  L.B = L.q + a16((size_t)G * D * es);
+  L.Re = L.B + (append ? (size_t)D * R * 4 : 0);
+  L.vk = L.Re + (append ? (size_t)D * RK * 4 : 0);
+  L.img = L.vk + (append ? (size_t)2 * D * es : 0);
+  L.total = L.img + (append ? (size_t)(R * ps + ps * RK) * es : 0);
+  // the score keys reuse the space from P on
+  if (L.total < L.P + (size_t)maxp * 4) L.total = L.P + (size_t)maxp * 4;
+  return L;
+}
+
+template <typename T, bool APPEND, int D>
 __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
   extern __shared__ float lds[];
-  __shared__ float s_q[MAX_GROUP * 128];  // [G][D]
-  __shared__ float s_qc[MAX_GROUP][MAX_RANK + MAX_RESID];
-  __shared__ float s_tok[3][128];  // appended token: v, k, Key remainder
-  __shared__ float s_zt[MAX_RANK];
-  __shared__ float s_newsum[MAX_RANK + MAX_RESID];  // the appended page's sums
+  __shared__ float s_qc[MAX_GROUP][XMAX];   // scale * (P.q_h | R_dec.q_h), zero past r + r_k
+  __shared__ float s_tok[4][128];           // appended token: v, k, Key remainder; stored values
+  __shared__ float s_newsum[XMAX];          // the appended page's sums
 
   const int pair = blockIdx.x;
-  const int H = a.s.n_kv_heads, G = a.s.group, D = a.s.head_dim;
+  const int H = a.s.n_kv_heads, G = a.s.group;
   const int R = a.s.rank_v, RK = a.s.rank_k, RR = R + RK, ps = a.s.page_size;
+  const int maxp = a.s.max_pages;
   const int b = pair / H, g = pair % H;
-  const int tid = threadIdx.x;
-  const int32_t* pt = a.page_table + (size_t)b * a.s.max_pages;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int32_t* pt = a.page_table + (size_t)b * maxp;
+  char* base = reinterpret_cast<char*>(lds);
+  const RouteLds lay = route_lds(maxp, D, R, RK, G, ps, (int)sizeof(T), APPEND);
+  int32_t* s_pid = reinterpret_cast<int32_t*>(base + lay.pid);  // [maxp] the page-table row
+  float* sP = reinterpret_cast<float*>(base + lay.P);            // [R][D] rotated
+  float* sRd = reinterpret_cast<float*>(base + lay.Rd);          // [RK][D] rotated
+  T* sq = reinterpret_cast<T*>(base + lay.q);                    // [G][D] the group's query heads
+  uint32_t* s_keys = reinterpret_cast<uint32_t*>(sP);            // [maxp], once the projections are done
 
-  const int LDP = lds_row(D);
-  float* sP = lds;                 // [R][LDP]
-  float* sRd = sP + R * LDP;       // [RK][LDP]
-  float* sB = sRd + RK * LDP;      // [D][R]   (append)
-  float* sRe = sB + D * R;         // [D][RK]  (append)
-  float* sZp = sRe + D * RK;       // [R][ps+1] the appended page's stored latents
-  float* sSp = sZp + R * (ps + 1); // [ps][RK] ... and residuals
-  uint32_t* s_keys = reinterpret_cast<uint32_t*>(lds);  // [max_pages], after the projections
-
+  // ---- round trip 1: page-table row, sequence length, append position,
+  // factors, query and new token, all requested together ----
+  const int pid0 = tid < maxp ? pt[tid] : 0;  // this lane's first page, for its sums below
+  const int n = a.seq_lens[b];
   int pos = -1;
   if (APPEND) {
     pos = a.pos[b];
-    if (pos >= a.s.max_pages * ps) pos = -1;
+    if (pos < 0 || pos >= maxp * ps) pos = -1;
   }
-  const int apage = pos >= 0 ? pos / ps : -1, slot = pos >= 0 ? pos % ps : 0;
-  const int aphys = pos >= 0 ? pt[apage] : 0;
-  T* Kp = static_cast<T*>(a.K);
-  T* Zp = static_cast<T*>(a.Z);
-  T* Sp = static_cast<T*>(a.S);
-  const size_t zbase = ((size_t)aphys * H + g) * R * ps;
-  const size_t sbase = ((size_t)aphys * H + g) * ps * RK;
-
-  // ---- one round of loads: factors, query, the new token and the appended
-  // page into LDS; each scoring lane's page sums into registers ----
+  const bool app = APPEND && pos >= 0;
+  const int apage = app ? pos / ps : 0, slot = app ? pos % ps : 0;
+  const int npg = n > 0 ? min((n + ps - 1) / ps, maxp) : 0;
+  const bool in_regs = RR <= VMAX;  // a page's sums fit one lane's registers
+  const bool pt16 = (maxp & 3) == 0 && (reinterpret_cast<uintptr_t>(pt) & 15) == 0;
   {
-    const T* q = static_cast<const T*>(a.q) + ((size_t)b * a.s.n_q_heads + g * G) * D;
-    const bool app = APPEND && pos >= 0;
-    const size_t tok = ((size_t)b * H + g) * D;
-    const int tchunks = (int)(D * sizeof(T) / 16);
-    // fixed slots (the append's items carry no chunks when there is no append)
-    ChunkItem it[MAX_ITEMS] = {
-        {a.P + (size_t)g * R * D, sP, R * D / 4, CK_F32_MATRIX, D, LDP},
-        {a.R_dec + (size_t)g * RK * D, sRd, RK * D / 4, CK_F32_MATRIX, D, LDP},
-        {q, s_q, (int)(G * D * sizeof(T) / 16), CK_VECTOR, 0, 0},
-        {a.B + (size_t)g * D * R, sB, app ? D * R / 4 : 0, CK_F32_MATRIX, R, R},
-        {a.R_enc + (size_t)g * D * RK, sRe, app ? D * RK / 4 : 0, CK_F32_MATRIX, RK, RK},
-        {static_cast<const T*>(a.v_new) + tok, s_tok[0], app ? tchunks : 0, CK_VECTOR, 0, 0},
-        {static_cast<const T*>(a.k_new) + tok, s_tok[1], app ? tchunks : 0, CK_VECTOR, 0, 0},
-        {Zp + zbase, sZp, app ? (int)(R * ps * sizeof(T) / 16) : 0, CK_ZPAGE, ps, 0},
-        {Sp + sbase, sSp, app ? (int)(ps * RK * sizeof(T) / 16) : 0, CK_VECTOR, 0, 0}};
-    stage_chunks<T>(it, MAX_ITEMS);
+    const char* P = reinterpret_cast<const char*>(a.P + (size_t)g * R * D);
+    const char* Rd = reinterpret_cast<const char*>(a.R_dec + (size_t)g * RK * D);
+    const char* q = reinterpret_cast<const char*>(static_cast<const T*>(a.q) + ((size_t)b * a.s.n_q_heads + g * G) * D);
+    const char* ptc = reinterpret_cast<const char*>(pt);
+    int first = dma_stage(sP, R * D / 4, [&](int G_) { return P + 16 * rot_source(G_, D); }, 0, NW, wave, lane);
+    first = dma_stage(sRd, RK * D / 4, [&](int G_) { return Rd + 16 * rot_source(G_, D); }, first, NW, wave, lane);
+    first = dma_stage(sq, (int)(G * D * sizeof(T) / 16), [&](int G_) { return q + 16 * G_; }, first, NW, wave, lane);
+    if (pt16) first = dma_stage(s_pid, maxp / 4, [&](int G_) { return ptc + 16 * G_; }, first, NW, wave, lane);
+    if (app) {
+      const char* B = reinterpret_cast<const char*>(a.B + (size_t)g * D * R);
+      const char* Re = reinterpret_cast<const char*>(a.R_enc + (size_t)g * D * RK);
+      const size_t tok = ((size_t)b * H + g) * D;
+      const char* vn = reinterpret_cast<const char*>(static_cast<const T*>(a.v_new) + tok);
+      const char* kn = reinterpret_cast<const char*>(static_cast<const T*>(a.k_new) + tok);
+      const int tc = (int)(D * sizeof(T) / 16);
+      first = dma_stage(base + lay.B, D * R / 4, [&](int G_) { return B + 16 * G_; }, first, NW, wave, lane);
+      first = dma_stage(base + lay.Re, D * RK / 4, [&](int G_) { return Re + 16 * G_; }, first, NW, wave, lane);
+      dma_stage(base + lay.vk, 2 * tc, [&](int G_) { return G_ < tc ? vn + 16 * G_ : kn + 16 * (G_ - tc); }, first,
+                NW, wave, lane);
+    }
   }
-  const int n = a.seq_lens[b];
-  const int npg = n > 0 ? min((n + ps - 1) / ps, a.s.max_pages) : 0;
-  // this lane's page sums (lane j scores page j; npg <= 512 and r + r_k <= 64
-  // take the prefetched one-pass path)
+  if (!pt16)
+    for (int j = tid; j < maxp; j += RT) s_pid[j] = pt[j];
+  __syncthreads();
+
+  // ---- round trip 2: this lane's first page sums (lane j scores page j)
   float v[VMAX];
-  const bool one_pass = npg <= RT && RR <= VMAX;
-  if (one_pass && tid < npg) {
-    const float* sm = a.summ + ((size_t)pt[tid] * H + g) * RR;
+  auto load_row = [&](float (&dst)[VMAX], int phys) {
+    const float* sm = a.summ + ((size_t)phys * H + g) * RR;
 #pragma unroll
     for (int u = 0; u < VMAX / 4; ++u) {
       float4 t4 = {0.f, 0.f, 0.f, 0.f};
       if (4 * u < RR) t4 = *reinterpret_cast<const float4*>(sm + 4 * u);
-      v[4 * u] = t4.x;
-      v[4 * u + 1] = t4.y;
-      v[4 * u + 2] = t4.z;
-      v[4 * u + 3] = t4.w;
+      dst[4 * u] = t4.x;
+      dst[4 * u + 1] = t4.y;
+      dst[4 * u + 2] = t4.z;
+      dst[4 * u + 3] = t4.w;
     }
-  }
-  __syncthreads();
-
-  if (APPEND && pos >= 0) {
-    // the new token: exact Key, rounded latent and residual, then its page's sums
-    const size_t kbase = ((size_t)aphys * H + g) * ps * D;
-    if (tid < R) {
-      const float zt = round_store(Zp, zbase + (size_t)tid * ps + slot, latent_dot(s_tok[0], sB, D, R, tid));
-      s_zt[tid] = zt;
-      sZp[tid * (ps + 1) + slot] = zt;
-    }
-    if (tid >= RT - D)
-      Kp[kbase + (size_t)slot * D + (tid - (RT - D))] =
-          static_cast<const T*>(a.k_new)[((size_t)b * H + g) * D + (tid - (RT - D))];
-    __syncthreads();
-    if (tid < D) s_tok[2][tid] = key_remainder(s_tok[1][tid], s_zt, sP, LDP, R, tid);
-    __syncthreads();
-    if (tid < RK) sSp[slot * RK + tid] = round_store(Sp, sbase + (size_t)slot * RK + tid, residual_dot(s_tok[2], sRe, D, RK, tid));
-    __syncthreads();
-    if (tid < RR) {
-      const float sum = page_channel_sum(sZp, sSp, R, RK, ps, tid, slot + 1);
-      a.summ[((size_t)aphys * H + g) * RR + tid] = sum;
-      s_newsum[tid] = sum;
-    }
-    __syncthreads();
-  }
-
-  // the query seen through the latent predictor P and the residual decoder R_dec
-  for (int o = tid; o < G * 128; o += RT) {
-    const int h = o / 128, x = o % 128;
-    float acc = 0.f;
-    if (x < RR) {
-      const float4* row = reinterpret_cast<const float4*>(x < R ? sP + x * LDP : sRd + (x - R) * LDP);
-      const float4* qv = reinterpret_cast<const float4*>(s_q + h * D);
-      for (int i = 0; i < D / 4; ++i) {
-        const float4 p4 = row[i], q4 = qv[i];
-        acc = fmaf(p4.x, q4.x, acc);
-        acc = fmaf(p4.y, q4.y, acc);
-        acc = fmaf(p4.z, q4.z, acc);
-        acc = fmaf(p4.w, q4.w, acc);
-      }
-    }
-    s_qc[h][x] = acc * a.s.scale;
-  }
-  __syncthreads();
-
-  // one lane per page: score from the page's fp32 sums
-  // one lane per page; the page sums in registers, 64 channels at a time
-  float d[MAX_GROUP];
-  auto accumulate = [&](const float (&vv)[VMAX], int x0) {
-#pragma unroll
-    for (int h = 0; h < MAX_GROUP; ++h)
-      if (h < G) {
-#pragma unroll
-        for (int x = 0; x < VMAX; ++x)
-          if (x0 + x < RR) d[h] = fmaf(s_qc[h][x0 + x], vv[x], d[h]);
-      }
   };
-  auto finish = [&](int j) {
-    const int cnt = min(ps, n - j * ps);
-    float best = -__builtin_huge_valf();
+  if (in_regs && tid < npg) load_row(v, pid0);
+
+  if (app && wave == 0) {
+    // ---- the new token (wave 0): exact Key, rounded latent and residual,
+    // then its page's sums from scratch over slots [0, slot] ----
+    const int aphys = s_pid[apage];
+    T* Kp = static_cast<T*>(a.K) + ((size_t)aphys * H + g) * ps * D;
+    T* Zp = static_cast<T*>(a.Z) + ((size_t)aphys * H + g) * R * ps;
+    T* Sp = static_cast<T*>(a.S) + ((size_t)aphys * H + g) * ps * RK;
+    T* img = reinterpret_cast<T*>(base + lay.img);
+    PageImage pg;
+    pg.load(Zp, Sp, (int)(R * ps * sizeof(T) / 16), (int)(ps * RK * sizeof(T) / 16), lane);
+    const T* vk = reinterpret_cast<const T*>(base + lay.vk);
 #pragma unroll
-    for (int h = 0; h < MAX_GROUP; ++h)
-      if (h < G) best = fmaxf(best, d[h]);
-    const float sc = best / (float)cnt;
-    a.scores[(size_t)pair * a.s.max_pages + j] = sc;
+    for (int i = lane; i < D; i += 64) {
+      s_tok[0][i] = ld_elem(vk, i);
+      s_tok[1][i] = ld_elem(vk, D + i);
+    }
+    wave_sync();
+    const TokenLds L{s_tok[0], s_tok[1], reinterpret_cast<const float*>(base + lay.B), sP,
+                     reinterpret_cast<const float*>(base + lay.Re), s_tok[2], s_tok[3]};
+    wave_write_token<T, D>(L, R, RK, ps, slot, Kp + (size_t)slot * D, Zp, Sp, lane);
+    pg.store(img, lane);
+    wave_sync();
+    // the new token's values replace what the page held in its slot
+    for (int x = lane; x < RR; x += 64) {
+      if (x < R) store_elem(img, (size_t)x * ps + slot, L.st[x]);
+      else store_elem(img, (size_t)R * ps + (size_t)slot * RK + (x - R), L.st[x]);
+    }
+    wave_sync();
+    wave_page_sums(img, img + (size_t)R * ps, R, RK, ps, slot + 1, s_newsum, lane);
+    wave_sync();
+    for (int x = lane; x < RR; x += 64) a.summ[((size_t)aphys * H + g) * RR + x] = s_newsum[x];
+  } else {
+    // ---- the query seen through the latent predictor P and the residual
+    // decoder R_dec: four lanes per output, lane c taking 16-byte pieces
+    // 4u + c of the rows; outputs past r + r_k (up to VMAX) are zero ----
+    const int q0 = app ? 64 : 0;
+    const int XP = RR > VMAX ? RR : VMAX;
+    for (int t = tid - q0; t < G * XP * 4; t += RT - q0) {
+      const int o = t >> 2, c = t & 3;
+      const int h = o / XP, x = o % XP;
+      float acc = 0.f;
+      if (x < RR) {
+        const int xr = x < R ? x : x - R;
+        const float* row = (x < R ? sP : sRd) + xr * D;
+        const T* qh = sq + h * D;
+#pragma unroll
+        for (int u = 0; u < D / 16; ++u) {
+          const f32x4 p4 = lds4(row + rot_granule(xr, 4 * u + c, D) * 4);
+          const f32x4 q4 = lds4(qh + 16 * u + 4 * c);
+          acc = fmaf(p4[0], q4[0], acc);
+          acc = fmaf(p4[1], q4[1], acc);
+          acc = fmaf(p4[2], q4[2], acc);
+          acc = fmaf(p4[3], q4[3], acc);
+        }
+      }
+      acc = quad_sum(acc);
+      if (c == 0) s_qc[h][x] = acc * a.s.scale;
+    }
+  }
+  __syncthreads();
+
+  // ---- one lane per page: score from the page's fp32 sums ----
+  auto finish = [&](int j, float best) {
+    const float sc = best / (float)min(ps, n - j * ps);
+    a.scores[(size_t)pair * maxp + j] = sc;
     s_keys[j] = float_key(sc);
   };
-  if (one_pass) {
-    if (tid < npg) {
-      if (APPEND && tid == apage) {
+  if (in_regs) {
+    // max over the group's heads of (q_h seen through P | R_dec) . sums, over
+    // VMAX channels (both zero past r + r_k)
+    auto score_row = [&](const float (&vv)[VMAX]) {
+      float best = -__builtin_huge_valf();
+      for (int h = 0; h < G; ++h) {
+        const f32x4* qc = reinterpret_cast<const f32x4*>(s_qc[h]);
+        float acc = 0.f;
+#pragma unroll
+        for (int u = 0; u < VMAX / 4; ++u) {
+          const f32x4 c4 = qc[u];
+          acc = fmaf(c4[0], vv[4 * u], acc);
+          acc = fmaf(c4[1], vv[4 * u + 1], acc);
+          acc = fmaf(c4[2], vv[4 * u + 2], acc);
+          acc = fmaf(c4[3], vv[4 * u + 3], acc);
+        }
+        best = fmaxf(best, acc);
+      }
+      return best;
+    };
+    // lanes with several pages request the next page's sums before scoring
+    // the current one
+    float w[VMAX];
+    for (int j = tid; j < npg; j += RT) {
+      if (j + RT < npg) load_row(w, s_pid[j + RT]);
+      if (app && j == apage) {
 #pragma unroll
         for (int x = 0; x < VMAX; ++x) v[x] = x < RR ? s_newsum[x] : 0.f;
       }
+      finish(j, score_row(v));
 #pragma unroll
-      for (int h = 0; h < MAX_GROUP; ++h) d[h] = 0.f;
-      accumulate(v, 0);
-      finish(tid);
+      for (int x = 0; x < VMAX; ++x) v[x] = w[x];
     }
   } else {
+    // wide sums (r + r_k > 64): 64 channels at a time, every head's dot kept
+    float d[MAX_GROUP];
     for (int j = tid; j < npg; j += RT) {
-      const float* sm = a.summ + ((size_t)pt[j] * H + g) * RR;
+      const float* sm = a.summ + ((size_t)s_pid[j] * H + g) * RR;
 #pragma unroll
       for (int h = 0; h < MAX_GROUP; ++h) d[h] = 0.f;
       for (int x0 = 0; x0 < RR; x0 += VMAX) {
@@ -278,20 +271,33 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
           v[4 * u + 2] = t4.z;
           v[4 * u + 3] = t4.w;
         }
-        accumulate(v, x0);
+        if (app && j == apage) {
+#pragma unroll
+          for (int x = 0; x < VMAX; ++x)
+            if (x0 + x < RR) v[x] = s_newsum[x0 + x];
+        }
+#pragma unroll
+        for (int h = 0; h < MAX_GROUP; ++h)
+          if (h < G) {
+#pragma unroll
+            for (int x = 0; x < VMAX; ++x)
+              if (x0 + x < RR) d[h] = fmaf(s_qc[h][x0 + x], v[x], d[h]);
+          }
       }
-      finish(j);
+      float best = -__builtin_huge_valf();
+#pragma unroll
+      for (int h = 0; h < MAX_GROUP; ++h)
+        if (h < G) best = fmaxf(best, d[h]);
+      finish(j, best);
     }
   }
   __syncthreads();
 
   // ---- top-k selection: per-wave histograms, one merge per radix pass ----
-  constexpr int NW = RT / 64;
   __shared__ int s_whist[NW][256];
   __shared__ int s_tot[256];
   __shared__ int s_wcnt[NW][2];
   __shared__ int s_digit, s_krem;
-  const int wave = tid >> 6, lane = tid & 63;
   const int k = min(a.s.top_k, npg);
   int32_t* sel = a.sel + (size_t)pair * a.s.top_k;
   int32_t* selp = a.sel_phys ? a.sel_phys + (size_t)pair * a.s.top_k : nullptr;
@@ -382,7 +388,7 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
       const int p = taken + take_before + __popcll(tm & below);
       if (p < k) {
         sel[p] = j;
-        if (selp) selp[p] = pt[j];
+        if (selp) selp[p] = s_pid[j];
       }
     }
     eq_seen += eq_total;
@@ -392,28 +398,35 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
 }
 
 size_t route_lds_bytes(const Shape& s, bool append) {
-  const size_t D = s.head_dim, R = s.rank_v, RK = s.rank_k, ps = s.page_size;
-  size_t f = (R + RK) * lds_row(s.head_dim);
-  if (append) f += D * R + D * RK + R * (ps + 1) + ps * RK;
-  if (f < (size_t)s.max_pages) f = s.max_pages;
-  return f * sizeof(float);
+  return route_lds(s.max_pages, s.head_dim, s.rank_v, s.rank_k, s.group, s.page_size, s.dtype == 0 ? 4 : 2, append)
+      .total;
+}
+
+template <typename T, bool APPEND, int D>
+hipError_t launch_t(const RouteArgs& a, hipStream_t st) {
+  const size_t lds = route_lds_bytes(a.s, APPEND);
+  const hipError_t e = allow_lds((const void*)route_kernel<T, APPEND, D>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((route_kernel<T, APPEND, D>), dim3(a.s.batch * a.s.n_kv_heads), dim3(RT), lds, st, a);
+  return hipGetLastError();
 }
 
 template <typename T, bool APPEND>
-hipError_t launch_t(const RouteArgs& a, hipStream_t st) {
-  const size_t lds = route_lds_bytes(a.s, APPEND);
-  const hipError_t e = allow_lds((const void*)route_kernel<T, APPEND>, lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((route_kernel<T, APPEND>), dim3(a.s.batch * a.s.n_kv_heads), dim3(RT), lds, st, a);
-  return hipGetLastError();
+hipError_t launch_d(const RouteArgs& a, hipStream_t st) {
+  return a.s.head_dim == 64 ? launch_t<T, APPEND, 64>(a, st) : launch_t<T, APPEND, 128>(a, st);
 }
 
 }  // namespace
 
+bool route_fits(const Shape& s, bool append) {
+  // the kernel's static arrays take under 24 KiB; gfx950 has 160 KiB per CU
+  return route_lds_bytes(s, append) + 24 * 1024 <= 160 * 1024;
+}
+
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
   const bool append = a.pos != nullptr;
-  if (a.s.dtype == 0) return append ? launch_t<float, true>(a, st) : launch_t<float, false>(a, st);
-  return append ? launch_t<uint16_t, true>(a, st) : launch_t<uint16_t, false>(a, st);
+  if (a.s.dtype == 0) return append ? launch_d<float, true>(a, st) : launch_d<float, false>(a, st);
+  return append ? launch_d<uint16_t, true>(a, st) : launch_d<uint16_t, false>(a, st);
 }
 
 }  // namespace bkv

@@ -9,11 +9,13 @@
 //
 // One workgroup writes the tokens that fall in one page for one KV head
 // (decode append: a single token; prefill chunk: up to a page of tokens),
-// 16 tokens at a time through LDS:
+// one wave per token:
 //   z~ = round(v.B);  e = k - z~.P;  s~ = round(e.R_enc);  store k, z~, s~.
-// Then it sets the page's sums to the fp32 sum, in slot order, of the stored
-// z~ and s~ over slots [0, last written].  Append and chunk writes therefore
-// produce identical sums, and rewriting a position is idempotent.
+// The page's earlier slots are copied into an LDS image that receives the
+// new values; then its sums over slots [0, last written] are set from
+// scratch.  The fused decode-step append runs the same wave functions, so
+// append and chunk writes are bit-identical, and rewriting a position is
+// idempotent.
 #include "common.hpp"
 #include "internal.hpp"
 #include "token_math.hpp"
@@ -23,20 +25,21 @@ namespace bkv {
 namespace {
 
 constexpr int THREADS = 256;
-constexpr int TB = 16;  // tokens per LDS batch
+constexpr int NWAVES = THREADS / 64;
+constexpr int TOKEN_SCRATCH = 3 * 128 + 128;  // per wave: v, k, Key remainder [D], stored values [R + RK]
 
-// LDS floats the writer needs: staged B, P (row stride D+1), R_enc, then a
-// batch of v, k (reused for the Key remainder) and stored latents.
-size_t writer_lds_floats(const Shape& s) {
-  const int D = s.head_dim, R = s.rank_v, RK = s.rank_k, ps = s.page_size;
-  return (size_t)D * R + (size_t)R * lds_row(D) + (size_t)D * RK + 2 * TB * D + TB * R +
-         (size_t)R * (ps + 1) + (size_t)ps * RK;
+// LDS bytes: B, rotated P, R_enc (fp32), the page image (storage dtype), and
+// each wave's token scratch.
+size_t writer_lds_bytes(const Shape& s) {
+  const size_t D = s.head_dim, R = s.rank_v, RK = s.rank_k, ps = s.page_size;
+  const size_t es = s.dtype == 0 ? 4 : 2;
+  return (D * R + R * D + D * RK) * 4 + (R * ps + ps * RK) * es + NWAVES * TOKEN_SCRATCH * 4;
 }
 
-template <typename T>
+template <typename T, int D>
 __global__ __launch_bounds__(THREADS) void write_kernel(WriteArgs a) {
   extern __shared__ float lds[];
-  const int H = a.s.n_kv_heads, D = a.s.head_dim, R = a.s.rank_v, RK = a.s.rank_k;
+  const int H = a.s.n_kv_heads, R = a.s.rank_v, RK = a.s.rank_k, RR = R + RK;
   const int ps = a.s.page_size;
   const int g = blockIdx.y;
   int b, t0, t1, row0;
@@ -54,73 +57,57 @@ __global__ __launch_bounds__(THREADS) void write_kernel(WriteArgs a) {
     if (t0 >= t1) return;
     row0 = t0 - a.start;
   }
-  const int LDP = lds_row(D);
-  float* sB = lds;
-  float* sP = sB + D * R;
-  float* sRe = sP + R * LDP;
-  float* s_v = sRe + D * RK;  // [TB][D]: v, then the Key remainder
-  float* s_k = s_v + TB * D;  // [TB][D]
-  float* s_z = s_k + TB * D;  // [TB][R] stored latents
-  float* sZp = s_z + TB * R;  // [R][ps+1] the page's stored latents, for its sums
-  float* sSp = sZp + R * (ps + 1);  // [ps][RK] ... and residuals
-  {
-    StageList L;
-    L.it[0] = StageItem{sB, a.B + (size_t)g * D * R, R, D, R};
-    L.it[1] = StageItem{sP, a.P + (size_t)g * R * D, LDP, R, D};
-    L.it[2] = StageItem{sRe, a.R_enc + (size_t)g * D * RK, RK, D, RK};
-    L.it[3] = L.it[2];
-    L.n = 3;
-    stage_matrices(L);
-  }
-
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int page = t0 / ps;
   const int phys = a.page_table[(size_t)b * a.s.max_pages + page];
   const T* kin = static_cast<const T*>(a.k);
   const T* vin = static_cast<const T*>(a.v);
-  T* Kp = static_cast<T*>(a.K);
-  T* Zp = static_cast<T*>(a.Z);
-  T* Sp = static_cast<T*>(a.S);
-  const size_t kbase = ((size_t)phys * H + g) * ps * D;
-  const size_t zbase = ((size_t)phys * H + g) * R * ps;
-  const size_t sbase = ((size_t)phys * H + g) * ps * RK;
-  const int tid = threadIdx.x;
+  T* Kp = static_cast<T*>(a.K) + ((size_t)phys * H + g) * ps * D;
+  T* Zp = static_cast<T*>(a.Z) + ((size_t)phys * H + g) * R * ps;
+  T* Sp = static_cast<T*>(a.S) + ((size_t)phys * H + g) * ps * RK;
 
-  for (int tb = t0; tb < t1; tb += TB) {
-    const int nb = min(TB, t1 - tb);
-    const int slot0 = tb - page * ps;
-    for (int o = tid; o < nb * D; o += THREADS) {
-      const int t = o / D, i = o % D;
-      const size_t src = ((size_t)(row0 + tb - t0 + t) * H + g) * D + i;
-      s_v[t * D + i] = ld_elem(vin, src);
-      s_k[t * D + i] = ld_elem(kin, src);
-      Kp[kbase + (size_t)(slot0 + t) * D + i] = kin[src];  // the exact Key, bit for bit
-    }
-    __syncthreads();
-    for (int o = tid; o < nb * R; o += THREADS) {
-      const int t = o / R, r = o % R;
-      s_z[t * R + r] = round_store(Zp, zbase + (size_t)r * ps + slot0 + t, latent_dot(s_v + t * D, sB, D, R, r));
-    }
-    __syncthreads();
-    for (int o = tid; o < nb * D; o += THREADS) {
-      const int t = o / D, i = o % D;
-      s_v[t * D + i] = key_remainder(s_k[t * D + i], s_z + t * R, sP, LDP, R, i);
-    }
-    __syncthreads();
-    for (int o = tid; o < nb * RK; o += THREADS) {
-      const int t = o / RK, j = o % RK;
-      round_store(Sp, sbase + (size_t)(slot0 + t) * RK + j, residual_dot(s_v + t * D, sRe, D, RK, j));
-    }
-    __syncthreads();
+  float* sB = lds;            // [D][R]
+  float* sP = sB + D * R;     // [R][D] rotated
+  float* sRe = sP + R * D;    // [D][RK]
+  T* img = reinterpret_cast<T*>(sRe + D * RK);  // the page: Z [R][ps], then S [ps][RK]
+  const int nz16 = (int)(R * ps * sizeof(T) / 16), ns16 = (int)(ps * RK * sizeof(T) / 16);
+  float* my = reinterpret_cast<float*>(img + (size_t)R * ps + (size_t)ps * RK) + wave * TOKEN_SCRATCH;
+
+  {
+    const char* B = reinterpret_cast<const char*>(a.B + (size_t)g * D * R);
+    const char* P = reinterpret_cast<const char*>(a.P + (size_t)g * R * D);
+    const char* Re = reinterpret_cast<const char*>(a.R_enc + (size_t)g * D * RK);
+    const char* Zs = reinterpret_cast<const char*>(Zp);
+    const char* Ss = reinterpret_cast<const char*>(Sp);
+    int first = dma_stage(sB, D * R / 4, [&](int G) { return B + 16 * G; }, 0, NWAVES, wave, lane);
+    first = dma_stage(sP, R * D / 4, [&](int G) { return P + 16 * rot_source(G, D); }, first, NWAVES, wave, lane);
+    first = dma_stage(sRe, D * RK / 4, [&](int G) { return Re + 16 * G; }, first, NWAVES, wave, lane);
+    dma_stage(img, nz16 + ns16, [&](int G) { return G < nz16 ? Zs + 16 * G : Ss + 16 * (G - nz16); }, first,
+              NWAVES, wave, lane);
   }
+  __syncthreads();
 
-  // page sums over slots [0, last written], in slot order
-  __threadfence_block();
+  const TokenLds L{my, my + D, sB, sP, sRe, my + 2 * D, my + 3 * D};
+  for (int t = t0 + wave; t < t1; t += NWAVES) {
+    const int slot = t - page * ps;
+    const size_t src = ((size_t)(row0 + t - t0) * H + g) * D;
+#pragma unroll
+    for (int i = lane; i < D; i += 64) {
+      my[i] = ld_elem(vin, src + i);
+      my[D + i] = ld_elem(kin, src + i);
+    }
+    wave_sync();
+    wave_write_token<T, D>(L, R, RK, ps, slot, Kp + (size_t)slot * D, Zp, Sp, lane);
+    for (int x = lane; x < RR; x += 64) {
+      if (x < R) store_elem(img, (size_t)x * ps + slot, L.st[x]);
+      else store_elem(img, (size_t)R * ps + (size_t)slot * RK + (x - R), L.st[x]);
+    }
+    wave_sync();
+  }
   __syncthreads();
-  const int valid = t1 - page * ps;
-  stage_page(sZp, sSp, Zp + zbase, Sp + sbase, R, RK, ps);
-  __syncthreads();
-  for (int x = tid; x < R + RK; x += THREADS)
-    a.summ[((size_t)phys * H + g) * (R + RK) + x] = page_channel_sum(sZp, sSp, R, RK, ps, x, valid);
+  if (wave == 0)
+    wave_page_sums(img, img + (size_t)R * ps, R, RK, ps, t1 - page * ps,
+                   a.summ + ((size_t)phys * H + g) * RR, lane);
 }
 
 // W_ofT[c][h*R + j] = round(sum_i B[g(h)][i][j] * W_O[h*D + i][c]); one block
@@ -154,16 +141,21 @@ hipError_t launch_write(const WriteArgs& a, hipStream_t st) {
     const int pages = (a.start + a.n_tok - 1) / ps - a.start / ps + 1;
     grid = dim3(pages, a.s.n_kv_heads);
   }
-  const size_t lds = writer_lds_floats(a.s) * sizeof(float);
+  const size_t lds = writer_lds_bytes(a.s);
+  const void* k = nullptr;
+  if (a.s.dtype == 0) k = a.s.head_dim == 64 ? (const void*)write_kernel<float, 64> : (const void*)write_kernel<float, 128>;
+  else k = a.s.head_dim == 64 ? (const void*)write_kernel<uint16_t, 64> : (const void*)write_kernel<uint16_t, 128>;
+  const hipError_t e = allow_lds(k, lds);
+  if (e != hipSuccess) return e;
+#define BKV_W(T, D) hipLaunchKernelGGL((write_kernel<T, D>), grid, dim3(THREADS), lds, st, a)
   if (a.s.dtype == 0) {
-    const hipError_t e = allow_lds((const void*)write_kernel<float>, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((write_kernel<float>), grid, dim3(THREADS), lds, st, a);
+    if (a.s.head_dim == 64) BKV_W(float, 64);
+    else BKV_W(float, 128);
   } else {
-    const hipError_t e = allow_lds((const void*)write_kernel<uint16_t>, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((write_kernel<uint16_t>), grid, dim3(THREADS), lds, st, a);
+    if (a.s.head_dim == 64) BKV_W(uint16_t, 64);
+    else BKV_W(uint16_t, 128);
   }
+#undef BKV_W
   return hipGetLastError();
 }
 
