@@ -186,13 +186,13 @@ int basiskv_append_route(const basiskv_dims *dims, const basiskv_factors *f,
 /*
  * Device workspace, in bytes, that basiskv_attend/decode/decode_step (batch
  * rows) and basiskv_prefill (up to max_prefill_tokens queries) need.  Host function.
- * Its first bytes hold counters that must be zero before first use: allocate
- * it zero-filled or call basiskv_workspace_init once.  Every call leaves them
- * zero again.  Calls that share a workspace must not overlap in time.
+ * It carries the attention splits' partial results and intermediate latents
+ * between the launches of one call; it needs no initialisation and keeps no
+ * state between calls.  Calls that share a workspace must not overlap in time.
  */
 size_t basiskv_workspace_bytes(const basiskv_dims *dims, int32_t max_prefill_tokens);
 
-/* Zero the workspace counters with a fill kernel (safe under graph capture). */
+/* Zero-fill a workspace with a fill kernel (optional; safe under graph capture). */
 int basiskv_workspace_init(const basiskv_dims *dims, void *ws, size_t ws_bytes, void *stream);
 
 /*
@@ -204,11 +204,23 @@ int basiskv_workspace_init(const basiskv_dims *dims, void *ws, size_t ws_bytes, 
  *   z_out[b][h] = sum_t softmax(s)_t * z~_t          (fp32 [batch][n_q_heads][rank_v])
  * A sequence with no selected page gets z_out = 0.  sel_phys (nullable): the
  * physical ids of sel as basiskv_route writes them; NULL looks them up.
+ * The selection of each (sequence, KV head) is processed in splits whose
+ * partial results are combined afterwards (flash-decoding style).  z_out may
+ * be NULL: the combination is then left to the caller and the partials stay
+ * at the start of ws, fp32 [batch*n_kv_heads][n_split][group][rank_v] partial
+ * sums sum_t 2^(s_t*log2(e) - m) z~_t, followed (at the next 256-byte
+ * boundary) by [batch*n_kv_heads][n_split][group][2] pairs (m, sum_t
+ * 2^(s_t*log2(e) - m)) with m the split's max of s_t*log2(e) (-inf for an
+ * empty split); n_split = basiskv_attend_splits(dims).
  */
 int basiskv_attend(const basiskv_dims *dims, const basiskv_cache *cache,
                    const int32_t *seq_lens, const void *q, const int32_t *sel,
                    const int32_t *n_sel, const int32_t *sel_phys, void *ws, size_t ws_bytes,
                    float *z_out, void *stream);
+
+/* Number of splits per (sequence, KV head) that basiskv_attend plans for
+ * these dims (>= 1), or a negative error code.  Host function. */
+int basiskv_attend_splits(const basiskv_dims *dims);
 
 /*
  * Output projection through the folded weights: out[m][c] = sum_x z[m][x] * W_ofT[c][x]

@@ -27,7 +27,8 @@ OK, E_NULL, E_DIMS, E_UNSUPPORTED, E_WORKSPACE, E_HIP, E_DATA = 0, -1, -2, -3, -
 EXPORTS = (
     "basiskv_version", "basiskv_strerror", "basiskv_last_error", "basiskv_fold_output",
     "basiskv_write", "basiskv_append", "basiskv_route", "basiskv_append_route",
-    "basiskv_workspace_bytes", "basiskv_workspace_init", "basiskv_attend", "basiskv_project",
+    "basiskv_workspace_bytes", "basiskv_workspace_init", "basiskv_attend", "basiskv_attend_splits",
+    "basiskv_project",
     "basiskv_decode", "basiskv_decode_step", "basiskv_prefill",
 )
 
@@ -74,6 +75,7 @@ def _load() -> C.CDLL:
         "basiskv_decode_step": ([D, Fp, Cp, p, p, p, p, p, p, p, p, p, sz, p, p, p], C.c_int),
         "basiskv_workspace_bytes": ([D, i32], sz),
         "basiskv_workspace_init": ([D, p, sz, p], C.c_int),
+        "basiskv_attend_splits": ([D], C.c_int),
         "basiskv_attend": ([D, Cp, p, p, p, p, p, p, sz, p, p], C.c_int),
         "basiskv_project": ([D, Fp, p, i32, p, p], C.c_int),
         "basiskv_decode": ([D, Fp, Cp, p, p, p, p, p, p, sz, p, p, p], C.c_int),
@@ -235,8 +237,8 @@ basiskv_workspace_bytes = workspace_bytes
 
 
 def new_workspace(d: Dims, max_prefill_tokens: int = 0, device="cuda") -> torch.Tensor:
-    """A zero-filled workspace (its counters start at zero)."""
-    return torch.zeros(workspace_bytes(d, max_prefill_tokens), dtype=torch.uint8, device=device)
+    """A workspace of basiskv_workspace_bytes bytes (needs no initialisation)."""
+    return torch.empty(workspace_bytes(d, max_prefill_tokens), dtype=torch.uint8, device=device)
 
 
 def basiskv_workspace_init(d: Dims, ws: torch.Tensor, stream=None) -> None:
@@ -292,8 +294,15 @@ def basiskv_decode_step(d: Dims, f: Factors, cache: Cache, pos, k_new, v_new, se
         _ptr(out, "out", torch.float32, d.batch * d.d_model), _stream(stream)))
 
 
+def attend_splits(d: Dims) -> int:
+    n = _lib.basiskv_attend_splits(C.byref(d.c()))
+    _check(min(n, 0))
+    return n
+
+
 def basiskv_attend(d: Dims, cache: Cache, seq_lens, q, sel, n_sel, ws, z_out, sel_phys=None,
                    stream=None) -> None:
+    """z_out None: the split partials stay in ws (see the header)."""
     pairs = d.batch * d.n_kv_heads
     cc = cache.c(d)
     _check(_lib.basiskv_attend(

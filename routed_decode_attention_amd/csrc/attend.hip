@@ -11,17 +11,11 @@
 // n_wsplit workgroup splits of ATTEND_WAVES waves; each wave owns
 // pages_per_wave consecutive selected pages and keeps an online softmax
 // (running max m, denominator l, latent accumulator) for every query head of
-// the group.  The waves of a workgroup merge through LDS; the workgroup that
-// finishes last for its pair loads every split's partial into LDS in one
-// round trip, merges them and writes the normalised latent (counter in the
-// workspace, reset by that workgroup).  The partials cross workgroups (and
-// XCDs, whose L2s are not coherent with each other) through device-scope
-// accesses only: they are written with relaxed agent-scope atomic stores
-// (write-through to the device coherence point), each thread waits for its
-// stores to complete before the workgroup barrier, one thread then bumps the
-// counter, and the last workgroup reads them with agent-scope atomic loads.
-// This avoids agent-scope fences, which write back and invalidate a whole
-// L2 and cost far more than the merge itself.
+// the group.  The waves of a workgroup merge through LDS and the workgroup
+// writes one partial (acc, m, l) per query head; the splits are combined by
+// the kernel that consumes them (the merge, or the merge fused with the
+// output projection), so no workgroup waits for another.  With a single
+// split the workgroup writes the normalised latent itself.
 //
 // bf16 storage, d_h in {64,128}, page 32/64, r in {16,32,48,64}: matrix-core
 // kernel.  Per 32-token chunk of a page, S = K.q^T runs as two 16x16x32 bf16
@@ -41,6 +35,7 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "split_merge.hpp"
 
 namespace bkv {
 
@@ -56,17 +51,15 @@ struct WaveState {  // LDS image of one wave's online-softmax state
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Merge the workgroup's waves into one partial; then, if this workgroup is the
-// last of its pair to finish, merge all partials into z_out.  s_part: dynamic
-// LDS of n_wsplit * group * (rank_v + 2) floats.
-__device__ void finish_pair(const AttendArgs& a, WaveState& ws, float* s_part, int pair, int split) {
+// Merge the workgroup's waves into one partial per query head: plain stores
+// of (acc, m, l), or the normalised latent when the pair has one split.
+__device__ void finish_split(const AttendArgs& a, WaveState& ws, int pair, int split) {
   const int G = a.s.group, R = a.s.rank_v;
-  const int stride = R + 2;
   const int tid = threadIdx.x;
   __syncthreads();
-  float* part = a.partials + ((size_t)pair * a.n_wsplit + split) * G * stride;
-  const bool single = a.n_wsplit == 1;
+  const bool single = a.n_wsplit == 1 && a.z_out != nullptr;
   const int b = pair / a.s.n_kv_heads, g = pair % a.s.n_kv_heads;
+  const size_t ps = (size_t)pair * a.n_wsplit + split;
   for (int o = tid; o < G * R; o += blockDim.x) {
     const int h = o / R, r = o % R;
     float M = NEG_INF;
@@ -84,59 +77,10 @@ __device__ void finish_pair(const AttendArgs& a, WaveState& ws, float* s_part, i
     if (single) {
       a.z_out[((size_t)b * a.s.n_q_heads + g * G + h) * R + r] = L > 0.f ? A / L : 0.f;
     } else {
-      __hip_atomic_store(&part[h * stride + 2 + r], A, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (r == 0) {
-        __hip_atomic_store(&part[h * stride], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&part[h * stride + 1], L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      a.part_acc[(ps * G + h) * R + r] = A;
+      if (r == 0) *reinterpret_cast<float2*>(a.part_ml + (ps * G + h) * 2) = make_float2(M, L);
     }
   }
-  if (single) return;
-
-  __shared__ int s_last;
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
-  __syncthreads();                // ... and every other thread's of the workgroup
-  if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(&a.counters[pair], 1u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == (unsigned)(a.n_wsplit - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  // every partial of the pair into LDS, up to 8 device-scope loads in flight per thread
-  const float* base = a.partials + (size_t)pair * a.n_wsplit * G * stride;
-  const int total = a.n_wsplit * G * stride;
-  for (int i0 = tid; i0 < total; i0 += blockDim.x * 8) {
-    float v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = i0 + u * blockDim.x;
-      v[u] = i < total ? __hip_atomic_load(base + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = i0 + u * blockDim.x;
-      if (i < total) s_part[i] = v[u];
-    }
-  }
-  __syncthreads();
-  for (int o = tid; o < G * R; o += blockDim.x) {
-    const int h = o / R, r = o % R;
-    float M = NEG_INF;
-    for (int sp = 0; sp < a.n_wsplit; ++sp) M = fmaxf(M, s_part[(sp * G + h) * stride]);
-    float L = 0.f, A = 0.f;
-    if (M != NEG_INF) {
-      for (int sp = 0; sp < a.n_wsplit; ++sp) {
-        const float* p = s_part + (sp * G + h) * stride;
-        const float e = exp2f(p[0] - M);
-        L += e * p[1];
-        A += e * p[2 + r];
-      }
-    }
-    a.z_out[((size_t)b * a.s.n_q_heads + g * G + h) * R + r] = L > 0.f ? A / L : 0.f;
-  }
-  if (tid == 0)
-    __hip_atomic_store(&a.counters[pair], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Zero the bf16 elements j of v whose index is >= valid (0 <= valid <= 8).
@@ -225,11 +169,12 @@ struct OnlineSoftmax {
     for (int c = 0; c < NC; ++c) {
       float p[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = bf16_to_f32(f32_to_bf16(exp2f(sv[c][e] - m_new)));
-        l += p[e];
-      }
+      for (int e = 0; e < 8; ++e) p[e] = exp2f(sv[c][e] - m_new);
+      // the weights enter the product rounded to bf16; the denominator sums
+      // the same rounded values
       const bf16x8 pb = pack_bf16x8(p);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) l += bf16x8_elem(pb, e);
 #pragma unroll
       for (int t = 0; t < MT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.z[c][t], pb, acc[t], 0, 0, 0);
     }
@@ -240,7 +185,6 @@ template <int D, int PS, int R, bool PIPE>
 __global__ __launch_bounds__(256) void attend_mfma_kernel(AttendArgs a) {
   constexpr int KS = D / 32, MT = R / 16;
   __shared__ WaveState st;
-  extern __shared__ float s_part[];
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int pair = wg / a.n_wsplit, split = wg % a.n_wsplit;
@@ -326,7 +270,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttendArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) st.acc[wave][n][16 * t + 4 * qd + e] = os.acc[t][e];
   }
-  finish_pair(a, st, s_part, pair, split);
+  finish_split(a, st, pair, split);
 }
 
 // Plain VALU kernel: one lane per token for q.k, one lane per latent channel
@@ -336,7 +280,6 @@ __global__ __launch_bounds__(256) void attend_valu_kernel(AttendArgs a) {
   __shared__ WaveState st;
   __shared__ float s_q[MAX_GROUP][128];
   __shared__ float s_p[ATTEND_WAVES][64];
-  extern __shared__ float s_part[];
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int pair = wg / a.n_wsplit, split = wg % a.n_wsplit;
@@ -399,10 +342,23 @@ __global__ __launch_bounds__(256) void attend_valu_kernel(AttendArgs a) {
     }
     if (lane < R) st.acc[wave][h][lane] = acc[h];
   }
-  finish_pair(a, st, s_part, pair, split);
+  finish_split(a, st, pair, split);
 }
 
-size_t part_floats(const Shape& s, int n_wsplit) { return (size_t)n_wsplit * s.group * (s.rank_v + 2); }
+// One workgroup per pair: every split of the pair combined, four latent
+// channels per thread.
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  const int pair = blockIdx.x;
+  const int G = a.s.group, R = a.s.rank_v;
+  const int b = pair / a.s.n_kv_heads, g = pair % a.s.n_kv_heads;
+  const float* acc = a.part_acc + (size_t)pair * a.n_wsplit * G * R;
+  const float* ml = a.part_ml + (size_t)pair * a.n_wsplit * G * 2;
+  for (int t = threadIdx.x; t < G * R / 4; t += blockDim.x) {
+    const int h = t / (R / 4), r0 = 4 * (t % (R / 4));
+    const f32x4 z = merge_splits4(acc, ml, a.n_wsplit, G, R, h, r0);
+    *reinterpret_cast<f32x4*>(a.z_out + ((size_t)b * a.s.n_q_heads + g * G + h) * R + r0) = z;
+  }
+}
 
 }  // namespace
 
@@ -413,8 +369,7 @@ bool attend_mfma_supported(const Shape& s) {
 }
 
 AttendPlan plan_attend(const Shape& s) {
-  // About 16 waves per CU over 256 CUs once every page unit is counted, and
-  // a partial-merge staging area of at most 40 KiB.
+  // About 16 waves per CU over 256 CUs once every page unit is counted.
   const long units = (long)s.batch * s.n_kv_heads * s.top_k;
   int ppw = (int)((units + 4095) / 4096);
   if (ppw < 1) ppw = 1;
@@ -422,19 +377,15 @@ AttendPlan plan_attend(const Shape& s) {
   const char* env = getenv("BASISKV_PAGES_PER_WAVE");
   if (env && atoi(env) > 0) ppw = atoi(env) < 32 ? atoi(env) : 32;
   AttendPlan p;
-  for (;;) {
-    p.pages_per_wave = ppw;
-    p.n_wsplit = (s.top_k + ATTEND_WAVES * ppw - 1) / (ATTEND_WAVES * ppw);
-    if (p.n_wsplit == 1 || part_floats(s, p.n_wsplit) * sizeof(float) <= 40 * 1024) break;
-    ++ppw;
-  }
+  p.pages_per_wave = ppw;
+  p.n_wsplit = (s.top_k + ATTEND_WAVES * ppw - 1) / (ATTEND_WAVES * ppw);
   return p;
 }
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   const int pairs = a.s.batch * a.s.n_kv_heads;
   const dim3 grid(pairs * a.n_wsplit), block(256);
-  const size_t lds = a.n_wsplit > 1 ? part_floats(a.s, a.n_wsplit) * sizeof(float) : 0;
+  const size_t lds = 0;
   if (attend_mfma_supported(a.s)) {
     const bool pipe = a.pages_per_wave > 1;
     const int key = a.s.head_dim * 10000 + a.s.page_size * 100 + a.s.rank_v;
@@ -456,6 +407,11 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   } else {
     hipLaunchKernelGGL((attend_valu_kernel<uint16_t>), grid, block, lds, st, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(merge_kernel, dim3(a.s.batch * a.s.n_kv_heads), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -80,18 +80,19 @@ int check_dims(const basiskv_dims* d, bkv::Shape* s) {
 }
 
 struct WsLayout {
-  size_t attend_cnt, partials, z, sel_phys, total;
+  size_t part_acc, part_ml, z, sel_phys, total;
 };
 
-// Workspace: attention merge counters, split-K partials, then latent rows.
+// Workspace: split-K partials (latent sums, then max/denominator pairs),
+// latent rows, then the router's physical page ids.
 WsLayout ws_layout(const bkv::Shape& s, int max_prefill_tokens) {
   const size_t pairs = (size_t)s.batch * s.n_kv_heads;
   const bkv::AttendPlan p = bkv::plan_attend(s);
+  const size_t splits = pairs * p.n_wsplit * s.group;
   WsLayout L;
-  L.attend_cnt = 0;
-  L.partials = align256(pairs * sizeof(unsigned));
-  const size_t part_bytes = pairs * p.n_wsplit * s.group * (s.rank_v + 2) * sizeof(float);
-  L.z = L.partials + align256(part_bytes);
+  L.part_acc = 0;
+  L.part_ml = align256(splits * s.rank_v * sizeof(float));
+  L.z = L.part_ml + align256(splits * 2 * sizeof(float));
   size_t rows = (size_t)s.batch;
   if (max_prefill_tokens > 0 && (size_t)max_prefill_tokens > rows) rows = max_prefill_tokens;
   L.sel_phys = L.z + align256(rows * s.n_q_heads * s.rank_v * sizeof(float));
@@ -108,13 +109,15 @@ int check_cache(const basiskv_cache* c, bool needs_k, bool needs_z, bool needs_s
 
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// Attention over the selection.  Several splits leave their partials in the
+// workspace; with `merge` they are combined into z_out right away, otherwise
+// the caller consumes them (the fused merge + projection).
 int do_attend(const bkv::Shape& s, const basiskv_cache* cache, const int32_t* seq_lens, const void* q,
               const int32_t* sel, const int32_t* n_sel, void* ws, size_t ws_bytes, float* z_out,
-              void* stream, const int32_t* sel_phys = nullptr) {
+              void* stream, const int32_t* sel_phys, bool merge) {
   const WsLayout L = ws_layout(s, 0);
-  if (ws_bytes < L.partials + (L.z - L.partials))
-    return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, attention needs %zu", ws_bytes,
-                L.z);
+  if (ws_bytes < L.z)
+    return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, attention needs %zu", ws_bytes, L.z);
   bkv::AttendArgs a;
   a.s = s;
   a.K = cache->K;
@@ -126,15 +129,26 @@ int do_attend(const bkv::Shape& s, const basiskv_cache* cache, const int32_t* se
   a.n_sel = n_sel;
   a.sel_phys = sel_phys;
   char* w = static_cast<char*>(ws);
-  a.partials = reinterpret_cast<float*>(w + L.partials);
-  a.counters = reinterpret_cast<unsigned*>(w + L.attend_cnt);
+  a.part_acc = reinterpret_cast<float*>(w + L.part_acc);
+  a.part_ml = reinterpret_cast<float*>(w + L.part_ml);
   a.z_out = z_out;
   const bkv::AttendPlan p = bkv::plan_attend(s);
   a.n_wsplit = p.n_wsplit;
   a.pages_per_wave = p.pages_per_wave;
   a.scale_log2 = s.scale * 1.4426950408889634f;
-  const hipError_t e = bkv::launch_attend(a, as_stream(stream));
-  return e == hipSuccess ? BASISKV_OK : hip_fail(e, "attention launch");
+  hipError_t e = bkv::launch_attend(a, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  if (merge && p.n_wsplit > 1) {
+    bkv::MergeArgs m;
+    m.s = s;
+    m.part_acc = a.part_acc;
+    m.part_ml = a.part_ml;
+    m.n_wsplit = p.n_wsplit;
+    m.z_out = z_out;
+    e = bkv::launch_merge(m, as_stream(stream));
+    if (e != hipSuccess) return hip_fail(e, "split merge launch");
+  }
+  return BASISKV_OK;
 }
 
 int do_project(const bkv::Shape& s, const basiskv_factors* f, const float* z, int rows, float* out,
@@ -149,6 +163,31 @@ int do_project(const bkv::Shape& s, const basiskv_factors* f, const float* z, in
   a.dtype = s.dtype;
   const hipError_t e = bkv::launch_project(a, as_stream(stream));
   return e == hipSuccess ? BASISKV_OK : hip_fail(e, "projection launch");
+}
+
+// Decode attention then output projection: the split merge is fused into
+// the projection when the matrix-core path applies, else merged first.
+int attend_project(const bkv::Shape& s, const basiskv_factors* f, const basiskv_cache* cache,
+                   const int32_t* seq_lens, const void* q, const int32_t* sel, const int32_t* n_sel,
+                   const int32_t* sel_phys, void* ws, size_t ws_bytes, float* z_out, float* out, void* stream) {
+  const WsLayout L = ws_layout(s, 0);
+  const bkv::AttendPlan p = bkv::plan_attend(s);
+  char* w = static_cast<char*>(ws);
+  float* z = z_out ? z_out : reinterpret_cast<float*>(w + L.z);
+  const bool fused = bkv::merge_project_supported(s, p.n_wsplit);
+  int rc = do_attend(s, cache, seq_lens, q, sel, n_sel, ws, ws_bytes, z, stream, sel_phys, !fused);
+  if (rc) return rc;
+  if (!fused) return do_project(s, f, z, s.batch, out, stream);
+  bkv::MergeProjectArgs m;
+  m.s = s;
+  m.part_acc = reinterpret_cast<const float*>(w + L.part_acc);
+  m.part_ml = reinterpret_cast<const float*>(w + L.part_ml);
+  m.n_wsplit = p.n_wsplit;
+  m.W = f->W_ofT;
+  m.out = out;
+  m.z_out = z_out;
+  const hipError_t e = bkv::launch_merge_project(m, as_stream(stream));
+  return e == hipSuccess ? BASISKV_OK : hip_fail(e, "merge + projection launch");
 }
 
 int do_write(const bkv::Shape& s, const basiskv_factors* f, const basiskv_cache* c, const int32_t* pos,
@@ -303,8 +342,8 @@ int basiskv_workspace_init(const basiskv_dims* dims, void* ws, size_t ws_bytes, 
   if (rc) return rc;
   if (!ws) return fail(BASISKV_E_NULL, "workspace is NULL");
   const WsLayout L = ws_layout(s, 0);
-  if (ws_bytes < L.partials) return fail(BASISKV_E_WORKSPACE, "workspace too small for its counters");
-  const hipError_t e = bkv::launch_zero_u32(static_cast<unsigned*>(ws), L.partials / sizeof(unsigned),
+  if (ws_bytes < L.total) return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, needs %zu", ws_bytes, L.total);
+  const hipError_t e = bkv::launch_zero_u32(static_cast<unsigned*>(ws), ws_bytes / sizeof(unsigned),
                                             as_stream(stream));
   return e == hipSuccess ? BASISKV_OK : hip_fail(e, "workspace init");
 }
@@ -316,9 +355,16 @@ int basiskv_attend(const basiskv_dims* dims, const basiskv_cache* cache, const i
   int rc = check_dims(dims, &s);
   if (rc) return rc;
   if ((rc = check_cache(cache, true, true, false))) return rc;
-  if (!seq_lens || !q || !sel || !n_sel || !ws || !z_out)
-    return fail(BASISKV_E_NULL, "attend: seq_lens, q, sel, n_sel, ws and z_out are required");
-  return do_attend(s, cache, seq_lens, q, sel, n_sel, ws, ws_bytes, z_out, stream, sel_phys);
+  if (!seq_lens || !q || !sel || !n_sel || !ws)
+    return fail(BASISKV_E_NULL, "attend: seq_lens, q, sel, n_sel and ws are required");
+  return do_attend(s, cache, seq_lens, q, sel, n_sel, ws, ws_bytes, z_out, stream, sel_phys, z_out != nullptr);
+}
+
+int basiskv_attend_splits(const basiskv_dims* dims) {
+  bkv::Shape s;
+  const int rc = check_dims(dims, &s);
+  if (rc) return rc;
+  return bkv::plan_attend(s).n_wsplit;
 }
 
 int basiskv_project(const basiskv_dims* dims, const basiskv_factors* f, const float* z, int32_t rows,
@@ -344,9 +390,7 @@ int basiskv_decode(const basiskv_dims* dims, const basiskv_factors* f, const bas
   const WsLayout L = ws_layout(s, 0);
   if (ws_bytes < L.total)
     return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, decode needs %zu", ws_bytes, L.total);
-  float* z = z_out ? z_out : reinterpret_cast<float*>(static_cast<char*>(ws) + L.z);
-  if ((rc = do_attend(s, cache, seq_lens, q, sel, n_sel, ws, ws_bytes, z, stream, sel_phys))) return rc;
-  return do_project(s, f, z, s.batch, out, stream);
+  return attend_project(s, f, cache, seq_lens, q, sel, n_sel, sel_phys, ws, ws_bytes, z_out, out, stream);
 }
 
 int basiskv_decode_step(const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
@@ -367,9 +411,7 @@ int basiskv_decode_step(const basiskv_dims* dims, const basiskv_factors* f, cons
   int32_t* sel_phys = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.sel_phys);
   if ((rc = do_route(s, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, stream, sel_phys)))
     return rc;
-  float* z = z_out ? z_out : reinterpret_cast<float*>(static_cast<char*>(ws) + L.z);
-  if ((rc = do_attend(s, cache, seq_lens, q, sel, n_sel, ws, ws_bytes, z, stream, sel_phys))) return rc;
-  return do_project(s, f, z, s.batch, out, stream);
+  return attend_project(s, f, cache, seq_lens, q, sel, n_sel, sel_phys, ws, ws_bytes, z_out, out, stream);
 }
 
 int basiskv_prefill(const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,

@@ -24,10 +24,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-// Two fp32 -> packed bf16 pair (low half = a).
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
-}
 
 // Storage element access: T is float (fp32 storage) or uint16_t (bf16 storage).
 __device__ __forceinline__ float ld_elem(const float* p, size_t i) { return p[i]; }
@@ -69,13 +65,35 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Eight fp32 -> an MFMA bf16x8 operand with the hardware's packed
+// round-to-nearest-even conversion (one instruction per pair).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 __device__ __forceinline__ bf16x8 pack_bf16x8(const float (&x)[8]) {
   u32x4 v;
-  v[0] = pack_bf16x2(x[0], x[1]);
-  v[1] = pack_bf16x2(x[2], x[3]);
-  v[2] = pack_bf16x2(x[4], x[5]);
-  v[3] = pack_bf16x2(x[6], x[7]);
+  v[0] = cvt_pk_bf16(x[0], x[1]);
+  v[1] = cvt_pk_bf16(x[2], x[3]);
+  v[2] = cvt_pk_bf16(x[4], x[5]);
+  v[3] = cvt_pk_bf16(x[6], x[7]);
   return __builtin_bit_cast(bf16x8, v);
+}
+// Element e of a packed bf16x8 as fp32.
+__device__ __forceinline__ float bf16x8_elem(const bf16x8& v, int e) {
+  const u32x4 u = __builtin_bit_cast(u32x4, v);
+  const uint32_t w = u[e >> 1];
+  return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+// x split into a bf16 high part and the bf16 rounding of the remainder.
+__device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+  hi = pack_bf16x8(x);
+  float r[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = x[e] - bf16x8_elem(hi, e);
+  lo = pack_bf16x8(r);
 }
 
 __device__ __forceinline__ bf16x8 zero_bf16x8() {

@@ -53,11 +53,29 @@ struct AttendArgs {
   const void* q;
   const int32_t *sel, *n_sel;
   const int32_t* sel_phys;  // physical ids of sel (nullptr: looked up in page_table)
-  float* partials;          // [pairs][n_wsplit][group][rank_v + 2]
-  unsigned* counters;       // [pairs], zero on entry and exit
-  float* z_out;             // [batch][n_q_heads][rank_v]
+  float* part_acc;          // [pairs][n_wsplit][group][rank_v]  split partial sums
+  float* part_ml;           // [pairs][n_wsplit][group][2]       split (max, denominator)
+  float* z_out;             // [batch][n_q_heads][rank_v], written directly when n_wsplit == 1
   int n_wsplit, pages_per_wave;
   float scale_log2;         // softmax scale * log2(e)
+};
+
+// Combining the split partials of AttendArgs into the normalised latent.
+struct MergeArgs {
+  Shape s;
+  const float *part_acc, *part_ml;
+  int n_wsplit;
+  float* z_out;             // [batch][n_q_heads][rank_v]
+};
+
+// Merge fused with the output projection (decode rows = batch).
+struct MergeProjectArgs {
+  Shape s;
+  const float *part_acc, *part_ml;
+  int n_wsplit;
+  const void* W;            // [d_model][n_q_heads * rank_v] bf16
+  float* out;               // [batch][d_model]
+  float* z_out;             // nullable [batch][n_q_heads][rank_v]
 };
 
 struct ProjectArgs {
@@ -92,6 +110,7 @@ AttendPlan plan_attend(const Shape& s);
 
 bool attend_mfma_supported(const Shape& s);
 bool route_fits(const Shape& s, bool append);  // the router's LDS fits one CU
+bool merge_project_supported(const Shape& s, int n_wsplit);
 bool project_mfma_supported(int kdim, int n, int dtype);
 bool prefill_mfma_supported(const Shape& s);
 
@@ -99,6 +118,8 @@ hipError_t launch_fold(const Shape& s, const float* B, const void* W_O, void* W_
 hipError_t launch_write(const WriteArgs& a, hipStream_t st);
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
+hipError_t launch_merge_project(const MergeProjectArgs& a, hipStream_t st);
 hipError_t launch_project(const ProjectArgs& a, hipStream_t st);
 hipError_t launch_prefill_attend(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_zero_u32(unsigned* p, size_t n, hipStream_t st);

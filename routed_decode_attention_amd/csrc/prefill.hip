@@ -151,11 +151,12 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
     for (int c = 0; c < NC; ++c) {
       float p[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = m_new == NEG_INF ? 0.f : bf16_to_f32(f32_to_bf16(exp2f(sv[c][e] - m_new)));
-        l_run += p[e];
-      }
+      for (int e = 0; e < 8; ++e) p[e] = m_new == NEG_INF ? 0.f : exp2f(sv[c][e] - m_new);
+      // the weights enter the product rounded to bf16; the denominator sums
+      // the same rounded values
       const bf16x8 pb = pack_bf16x8(p);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) l_run += bf16x8_elem(pb, e);
 #pragma unroll
       for (int t = 0; t < MT; ++t)
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.z[c][t], pb, acc[t], 0, 0, 0);

@@ -47,6 +47,56 @@ __device__ __forceinline__ float quad_sum(float x) {
   return x;
 }
 
+// Wave-wide max / min of a 32-bit key (every lane gets the result).
+#define BKV_DPPU(x, ctrl) (uint32_t) __builtin_amdgcn_update_dpp(0, (int)(x), ctrl, 0xF, 0xF, false)
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
+  x = max(x, BKV_DPPU(x, 0xB1));
+  x = max(x, BKV_DPPU(x, 0x4E));
+  x = max(x, BKV_DPPU(x, 0x124));  // row_ror:4
+  x = max(x, BKV_DPPU(x, 0x128));  // row_ror:8
+  auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = max(r[0], r[1]);
+  r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max(r[0], r[1]);
+}
+__device__ __forceinline__ uint32_t wave_umin(uint32_t x) {
+  x = min(x, BKV_DPPU(x, 0xB1));
+  x = min(x, BKV_DPPU(x, 0x4E));
+  x = min(x, BKV_DPPU(x, 0x124));
+  x = min(x, BKV_DPPU(x, 0x128));
+  auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = min(r[0], r[1]);
+  r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return min(r[0], r[1]);
+}
+#undef BKV_DPPU
+
+constexpr int PPL = 4;  // pages per scoring lane and group
+
+// best[i] = max over the group's heads h of qc[h] . sums(page i), each dot
+// split over the four lanes of a quad (NG 16-byte channel granules per lane,
+// granule part + 4u) and summed by the quad.
+template <int NG>
+__device__ __forceinline__ void score_group(const f32x4 (&sv)[PPL][4], const float (*qc)[XMAX], int G, int part,
+                                            float (&best)[PPL]) {
+#pragma unroll
+  for (int i = 0; i < PPL; ++i) best[i] = -__builtin_huge_valf();
+  for (int h = 0; h < G; ++h) {
+    f32x4 qg[NG];
+#pragma unroll
+    for (int u = 0; u < NG; ++u) qg[u] = *reinterpret_cast<const f32x4*>(&qc[h][4 * (part + 4 * u)]);
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) {
+      float acc = 0.f;
+#pragma unroll
+      for (int u = 0; u < NG; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = fmaf(qg[u][e], sv[i][u][e], acc);
+      best[i] = fmaxf(best[i], quad_sum(acc));
+    }
+  }
+}
+
 // Four consecutive storage-dtype elements from LDS as fp32.
 __device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ f32x4 lds4(const uint16_t* p) {
@@ -100,7 +150,6 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
 
   // ---- round trip 1: page-table row, sequence length, append position,
   // factors, query and new token, all requested together ----
-  const int pid0 = tid < maxp ? pt[tid] : 0;  // this lane's first page, for its sums below
   const int n = a.seq_lens[b];
   int pos = -1;
   if (APPEND) {
@@ -138,21 +187,24 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
     for (int j = tid; j < maxp; j += RT) s_pid[j] = pt[j];
   __syncthreads();
 
-  // ---- round trip 2: this lane's first page sums (lane j scores page j)
-  float v[VMAX];
-  auto load_row = [&](float (&dst)[VMAX], int phys) {
-    const float* sm = a.summ + ((size_t)phys * H + g) * RR;
+  // ---- round trip 2: page sums for scoring, requested now.  Four lanes
+  // per page: lane `part` of a quad holds channel granules part + 4u of its
+  // page's row (contiguous 64 bytes per quad and load); quad q takes pages
+  // q + 128 m, PPL of them per group ----
+  const int quad = wave * 16 + (lane >> 2), part = lane & 3;
+  f32x4 sv[PPL][4];
+  auto load_group = [&](int m0) {
 #pragma unroll
-    for (int u = 0; u < VMAX / 4; ++u) {
-      float4 t4 = {0.f, 0.f, 0.f, 0.f};
-      if (4 * u < RR) t4 = *reinterpret_cast<const float4*>(sm + 4 * u);
-      dst[4 * u] = t4.x;
-      dst[4 * u + 1] = t4.y;
-      dst[4 * u + 2] = t4.z;
-      dst[4 * u + 3] = t4.w;
+    for (int i = 0; i < PPL; ++i) {
+      const int j = quad + 128 * (m0 + i);
+      const f32x4* row = j < npg ? reinterpret_cast<const f32x4*>(a.summ + ((size_t)s_pid[j] * H + g) * RR) : nullptr;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int gr = part + 4 * u;
+        sv[i][u] = (row && 4 * gr < RR) ? row[gr] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
   };
-  if (in_regs && tid < npg) load_row(v, pid0);
 
   if (app && wave == 0) {
     // ---- the new token (wave 0): exact Key, rounded latent and residual,
@@ -170,10 +222,11 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
       s_tok[0][i] = ld_elem(vk, i);
       s_tok[1][i] = ld_elem(vk, D + i);
     }
+    if (in_regs) load_group(0);  // after the page, ahead of the arithmetic
     wave_sync();
     const TokenLds L{s_tok[0], s_tok[1], reinterpret_cast<const float*>(base + lay.B), sP,
                      reinterpret_cast<const float*>(base + lay.Re), s_tok[2], s_tok[3]};
-    wave_write_token<T, D>(L, R, RK, ps, slot, Kp + (size_t)slot * D, Zp, Sp, lane);
+    wave_token_values<T, D>(L, R, RK, lane);
     pg.store(img, lane);
     wave_sync();
     // the new token's values replace what the page held in its slot
@@ -184,34 +237,40 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
     wave_sync();
     wave_page_sums(img, img + (size_t)R * ps, R, RK, ps, slot + 1, s_newsum, lane);
     wave_sync();
+    // memory writes last: the token, then the page's sums
+    wave_token_store<T, D>(L, R, RK, ps, slot, Kp + (size_t)slot * D, Zp, Sp, lane);
     for (int x = lane; x < RR; x += 64) a.summ[((size_t)aphys * H + g) * RR + x] = s_newsum[x];
   } else {
     // ---- the query seen through the latent predictor P and the residual
-    // decoder R_dec: four lanes per output, lane c taking 16-byte pieces
-    // 4u + c of the rows; outputs past r + r_k (up to VMAX) are zero ----
+    // decoder R_dec: one task per (output row x, quarter c) for every head,
+    // lane c taking 16-byte pieces 4u + c of the row; a quad sums the
+    // quarters.  Outputs past r + r_k (up to VMAX) are zero ----
     const int q0 = app ? 64 : 0;
-    const int XP = RR > VMAX ? RR : VMAX;
-    for (int t = tid - q0; t < G * XP * 4; t += RT - q0) {
-      const int o = t >> 2, c = t & 3;
-      const int h = o / XP, x = o % XP;
-      float acc = 0.f;
-      if (x < RR) {
-        const int xr = x < R ? x : x - R;
-        const float* row = (x < R ? sP : sRd) + xr * D;
+    for (int t = tid - q0; t < RR * 4; t += RT - q0) {
+      const int x = t >> 2, c = t & 3;
+      const int xr = x < R ? x : x - R;
+      const float* row = (x < R ? sP : sRd) + xr * D;
+      f32x4 pr[D / 16];
+#pragma unroll
+      for (int u = 0; u < D / 16; ++u) pr[u] = lds4(row + rot_granule(xr, 4 * u + c, D) * 4);
+      for (int h = 0; h < G; ++h) {
         const T* qh = sq + h * D;
+        float acc = 0.f;
 #pragma unroll
         for (int u = 0; u < D / 16; ++u) {
-          const f32x4 p4 = lds4(row + rot_granule(xr, 4 * u + c, D) * 4);
           const f32x4 q4 = lds4(qh + 16 * u + 4 * c);
-          acc = fmaf(p4[0], q4[0], acc);
-          acc = fmaf(p4[1], q4[1], acc);
-          acc = fmaf(p4[2], q4[2], acc);
-          acc = fmaf(p4[3], q4[3], acc);
+          acc = fmaf(pr[u][0], q4[0], acc);
+          acc = fmaf(pr[u][1], q4[1], acc);
+          acc = fmaf(pr[u][2], q4[2], acc);
+          acc = fmaf(pr[u][3], q4[3], acc);
         }
+        acc = quad_sum(acc);
+        if (c == 0) s_qc[h][x] = acc * a.s.scale;
       }
-      acc = quad_sum(acc);
-      if (c == 0) s_qc[h][x] = acc * a.s.scale;
     }
+    if (RR < VMAX)
+      for (int t = tid - q0; t < G * (VMAX - RR); t += RT - q0) s_qc[t / (VMAX - RR)][RR + t % (VMAX - RR)] = 0.f;
+    if (in_regs) load_group(0);  // after the LDS work, so wave 0's page goes first
   }
   __syncthreads();
 
@@ -222,40 +281,36 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
     s_keys[j] = float_key(sc);
   };
   if (in_regs) {
-    // max over the group's heads of (q_h seen through P | R_dec) . sums, over
-    // VMAX channels (both zero past r + r_k)
-    auto score_row = [&](const float (&vv)[VMAX]) {
-      float best = -__builtin_huge_valf();
-      for (int h = 0; h < G; ++h) {
-        const f32x4* qc = reinterpret_cast<const f32x4*>(s_qc[h]);
-        float acc = 0.f;
+    const int ng = (RR + 15) / 16;  // channel granules per lane
+    for (int m0 = 0; 128 * m0 < npg; m0 += PPL) {
+      if (m0 > 0) load_group(m0);
+      if (app) {  // the appended page's new sums replace its loaded row
 #pragma unroll
-        for (int u = 0; u < VMAX / 4; ++u) {
-          const f32x4 c4 = qc[u];
-          acc = fmaf(c4[0], vv[4 * u], acc);
-          acc = fmaf(c4[1], vv[4 * u + 1], acc);
-          acc = fmaf(c4[2], vv[4 * u + 2], acc);
-          acc = fmaf(c4[3], vv[4 * u + 3], acc);
-        }
-        best = fmaxf(best, acc);
+        for (int i = 0; i < PPL; ++i)
+          if (quad + 128 * (m0 + i) == apage) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int gr = part + 4 * u;
+              sv[i][u] = 4 * gr < RR ? *reinterpret_cast<const f32x4*>(s_newsum + 4 * gr) : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+          }
       }
-      return best;
-    };
-    // lanes with several pages request the next page's sums before scoring
-    // the current one
-    float w[VMAX];
-    for (int j = tid; j < npg; j += RT) {
-      if (j + RT < npg) load_row(w, s_pid[j + RT]);
-      if (app && j == apage) {
-#pragma unroll
-        for (int x = 0; x < VMAX; ++x) v[x] = x < RR ? s_newsum[x] : 0.f;
+      float best[PPL];
+      switch (ng) {
+        case 1: score_group<1>(sv, s_qc, G, part, best); break;
+        case 2: score_group<2>(sv, s_qc, G, part, best); break;
+        case 3: score_group<3>(sv, s_qc, G, part, best); break;
+        default: score_group<4>(sv, s_qc, G, part, best); break;
       }
-      finish(j, score_row(v));
 #pragma unroll
-      for (int x = 0; x < VMAX; ++x) v[x] = w[x];
+      for (int i = 0; i < PPL; ++i) {
+        const int j = quad + 128 * (m0 + i);
+        if (part == 0 && j < npg) finish(j, best[i]);
+      }
     }
   } else {
     // wide sums (r + r_k > 64): 64 channels at a time, every head's dot kept
+    float v[VMAX];
     float d[MAX_GROUP];
     for (int j = tid; j < npg; j += RT) {
       const float* sm = a.summ + ((size_t)s_pid[j] * H + g) * RR;
@@ -293,11 +348,16 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
   }
   __syncthreads();
 
-  // ---- top-k selection: per-wave histograms, one merge per radix pass ----
+  // ---- top-k selection ----
+  // MSB-first radix select over the page keys, starting at the highest bit
+  // where they differ; a pass stops the search when the bucket holding the
+  // k-th key is exactly what remains to be taken.  The selected pages are
+  // then those whose masked key exceeds the found prefix, plus the first
+  // `take_eq` (in page order) of those equal to it.
   __shared__ int s_whist[NW][256];
-  __shared__ int s_tot[256];
   __shared__ int s_wcnt[NW][2];
-  __shared__ int s_digit, s_krem;
+  __shared__ uint32_t s_red[NW][2];
+  __shared__ int s_digit, s_krem, s_done;
   const int k = min(a.s.top_k, npg);
   int32_t* sel = a.sel + (size_t)pair * a.s.top_k;
   int32_t* selp = a.sel_phys ? a.sel_phys + (size_t)pair * a.s.top_k : nullptr;
@@ -308,92 +368,112 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
   if (tid == 0) a.n_sel[pair] = k;
   if (k == 0) return;
 
-  uint32_t thr = 0;
-  int take_eq = 0;
   const bool all = k == npg;
+  uint32_t prefix = 0, mask = 0;
+  int take_eq = 0;
   if (!all) {
-    uint32_t prefix = 0, mask = 0;
+    uint32_t kmax = 0u, kmin = 0xffffffffu;
+    for (int j = tid; j < npg; j += RT) {
+      const uint32_t key = s_keys[j];
+      kmax = max(kmax, key);
+      kmin = min(kmin, key);
+    }
+    kmax = wave_umax(kmax);
+    kmin = wave_umin(kmin);
+    if (lane == 0) {
+      s_red[wave][0] = kmax;
+      s_red[wave][1] = kmin;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      kmax = max(kmax, s_red[w][0]);
+      kmin = min(kmin, s_red[w][1]);
+    }
+    // the valid keys share every bit above the highest one where the
+    // largest and smallest differ (all of them when they are all equal)
+    const uint32_t diff = kmax ^ kmin;
+    int hi = diff ? 31 - __builtin_clz(diff) : -1;
+    mask = hi >= 0 ? ~((2u << hi) - 1u) : ~0u;
+    prefix = kmax & mask;
     int krem = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    while (hi >= 0) {
+      const int shift = hi >= 7 ? hi - 7 : 0;
+      const uint32_t dmask = (2u << (hi - shift)) - 1u;  // digit bits [shift, hi]
 #pragma unroll
       for (int u = 0; u < 4; ++u) s_whist[wave][lane + 64 * u] = 0;
       __builtin_amdgcn_wave_barrier();
       for (int j = tid; j < npg; j += RT) {
         const uint32_t key = s_keys[j];
-        if ((key & mask) == prefix) atomicAdd(&s_whist[wave][(key >> shift) & 255u], 1);
-      }
-      __syncthreads();
-      if (tid < 256) {
-        int t = 0;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) t += s_whist[w][tid];
-        s_tot[tid] = t;
+        if ((key & mask) == prefix) atomicAdd(&s_whist[wave][(key >> shift) & dmask], 1);
       }
       __syncthreads();
       if (wave == 0) {
         // lane owns digits 255-4*lane .. 252-4*lane (descending)
-        int c[4], own = 0;
+        int c[4] = {0, 0, 0, 0};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          c[u] = s_tot[255 - 4 * lane - u];
-          own += c[u];
+        for (int w = 0; w < NW; ++w) {
+          const int4 h4 = *reinterpret_cast<const int4*>(&s_whist[w][252 - 4 * lane]);
+          c[0] += h4.w;
+          c[1] += h4.z;
+          c[2] += h4.y;
+          c[3] += h4.x;
         }
+        const int own = c[0] + c[1] + c[2] + c[3];
         int run = wave_incl_scan(own) - own;  // keys with a larger digit than this lane's
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           if (run < krem && run + c[u] >= krem) {
             s_digit = 255 - 4 * lane - u;
             s_krem = krem - run;
+            s_done = c[u] == krem - run;
           }
           run += c[u];
         }
       }
       __syncthreads();
       prefix |= (uint32_t)s_digit << shift;
-      mask |= 0xffu << shift;
+      mask |= dmask << shift;
       krem = s_krem;
+      if (s_done || shift == 0) break;
+      hi = shift - 1;
     }
-    thr = prefix;
     take_eq = krem;
   }
 
-  // compaction in page order: ballots within a wave, counts across waves
+  // compaction in page order: a taken page's slot is the count of taken
+  // pages before it, i.e. greater keys before it plus min(equal keys before
+  // it, take_eq)
   const unsigned long long below = (1ull << lane) - 1ull;
-  int eq_seen = 0, taken = 0;
-  for (int base = 0; base < npg; base += RT) {
-    const int j = base + tid;
-    const uint32_t key = j < npg ? s_keys[j] : 0u;
-    const bool eq = !all && j < npg && key == thr;
-    const unsigned long long eqm = __ballot(eq);
-    if (lane == 0) s_wcnt[wave][0] = __popcll(eqm);
+  int gt_seen = 0, eq_seen = 0;
+  for (int base0 = 0; base0 < npg; base0 += RT) {
+    if (base0 > 0) __syncthreads();  // the previous round's counts are read
+    const int j = base0 + tid;
+    const uint32_t mk = j < npg ? (s_keys[j] & mask) : 0u;
+    const bool gt = j < npg && (all || mk > prefix);
+    const bool eq = j < npg && !all && mk == prefix;
+    const unsigned long long gtm = __ballot(gt), eqm = __ballot(eq);
+    if (lane == 0) {
+      s_wcnt[wave][0] = __popcll(gtm);
+      s_wcnt[wave][1] = __popcll(eqm);
+    }
     __syncthreads();
-    int eq_before = 0, eq_total = 0;
+    int gt_before = gt_seen + __popcll(gtm & below), eq_before = eq_seen + __popcll(eqm & below);
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      eq_before += w < wave ? s_wcnt[w][0] : 0;
-      eq_total += s_wcnt[w][0];
-    }
-    const bool take =
-        j < npg && (all || key > thr || (eq && eq_seen + eq_before + __popcll(eqm & below) < take_eq));
-    const unsigned long long tm = __ballot(take);
-    if (lane == 0) s_wcnt[wave][1] = __popcll(tm);
-    __syncthreads();
-    int take_before = 0, take_total = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      take_before += w < wave ? s_wcnt[w][1] : 0;
-      take_total += s_wcnt[w][1];
-    }
-    if (take) {
-      const int p = taken + take_before + __popcll(tm & below);
-      if (p < k) {
-        sel[p] = j;
-        if (selp) selp[p] = s_pid[j];
+      const int cg = s_wcnt[w][0], ce = s_wcnt[w][1];
+      if (w < wave) {
+        gt_before += cg;
+        eq_before += ce;
       }
+      gt_seen += cg;
+      eq_seen += ce;
     }
-    eq_seen += eq_total;
-    taken += take_total;
-    __syncthreads();
+    if (gt || (eq && eq_before < take_eq)) {
+      const int p = gt_before + min(eq_before, take_eq);
+      sel[p] = j;
+      if (selp) selp[p] = s_pid[j];
+    }
   }
 }
 

@@ -88,13 +88,60 @@ struct PageImage {
   }
 };
 
-// Add the values of lanes l ^ m for m = from, 2 from, ..., 32 (every lane of
-// a group ends with the same bits).
-__device__ __forceinline__ void xor_tree(f32x4& a, int from) {
-  for (int m = from; m < 64; m <<= 1) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) a[k] += __shfl_xor(a[k], m);
+// x[l] + x[l ^ M] for M in {1, 2, 4, 8, 16, 32}, on the vector ALU only (DPP
+// and the gfx950 lane-half swaps).  Both lanes of a pair get the same bits.
+#define BKV_DPP(x, ctrl) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xF, 0xF, false))
+template <int M>
+__device__ __forceinline__ float xor_add(float x, int lane) {
+  if constexpr (M == 1) {
+    return x + BKV_DPP(x, 0xB1);  // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    return x + BKV_DPP(x, 0x4E);  // quad_perm [2,3,0,1]
+  } else if constexpr (M == 4) {
+    const float up = BKV_DPP(x, 0x104), down = BKV_DPP(x, 0x114);  // row_shl:4, row_shr:4
+    return x + ((lane & 4) ? down : up);
+  } else if constexpr (M == 8) {
+    return x + BKV_DPP(x, 0x128);  // row_ror:8
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
+}
+#undef BKV_DPP
+
+// Add the values of lanes l ^ m for m = FROM, 2 FROM, ..., 32 (every lane of
+// a group ends with the same bits).
+template <int FROM>
+__device__ __forceinline__ void xor_tree(f32x4& a, int lane) {
+  if constexpr (FROM < 64) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = xor_add<FROM>(a[k], lane);
+    xor_tree<FROM * 2>(a, lane);
+  }
+}
+
+// acc[k] += x[i] * M[i][k] for i < ROWS in order (M rows nc floats apart).
+template <int ROWS>
+__device__ __forceinline__ void rows_fma(const float* x, const float* M, int nc, f32x4& acc) {
+  if constexpr (ROWS > 16) {  // at most 16 rows of operands in flight
+    rows_fma<16>(x, M, nc, acc);
+    rows_fma<ROWS - 16>(x + 16, M + (size_t)16 * nc, nc, acc);
+    return;
+  }
+  float xv[ROWS];
+  f32x4 mv[ROWS];
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) {
+    xv[i] = x[i];
+    mv[i] = *reinterpret_cast<const f32x4*>(M + (size_t)i * nc);
+  }
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[k] = fmaf(xv[i], mv[i][k], acc[k]);
 }
 
 // out[c] = sum_i x[i] * M[i][c] for c < nc (nc % 4 == 0, nc <= 64); x [D]
@@ -102,28 +149,52 @@ __device__ __forceinline__ void xor_tree(f32x4& a, int from) {
 // g = lane % GP (GP = nc/4 rounded up to a power of two), row slice
 // s = lane / GP of D / (64 / GP) consecutive rows.  Returns whether this lane
 // holds outputs 4g..4g+3 (slice 0, g < nc/4) in acc.
+template <int D, int GP>
+__device__ __forceinline__ bool wave_matvec_gp(const float* x, const float* M, int nc, int lane, f32x4& acc,
+                                               int& g) {
+  constexpr int ROWS = D * GP / 64;
+  const int G4 = nc >> 2;
+  g = lane & (GP - 1);
+  const int s = lane / GP;
+  acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  // lanes past the last output group read group 0 and are discarded
+  rows_fma<ROWS>(x + s * ROWS, M + (size_t)s * ROWS * nc + 4 * (g < G4 ? g : 0), nc, acc);
+  xor_tree<GP>(acc, lane);
+  return s == 0 && g < G4;
+}
+
 template <int D>
 __device__ __forceinline__ bool wave_matvec(const float* x, const float* M, int nc, int lane, f32x4& acc,
                                             int& g) {
   const int G4 = nc >> 2;
-  const int GP = G4 <= 1 ? 1 : 1 << (32 - __builtin_clz(G4 - 1));
-  const int S = 64 / GP, rows = D / S;
-  g = lane & (GP - 1);
-  const int s = lane / GP;
-  acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (g < G4) {
-    const float* xr = x + s * rows;
-    const float* mr = M + (size_t)s * rows * nc + 4 * g;
-#pragma unroll 4
-    for (int i = 0; i < rows; ++i) {
-      const float xi = xr[i];
-      const f32x4 m4 = *reinterpret_cast<const f32x4*>(mr + (size_t)i * nc);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) acc[k] = fmaf(xi, m4[k], acc[k]);
-    }
+  switch (G4 <= 1 ? 1 : 1 << (32 - __builtin_clz(G4 - 1))) {
+    case 1: return wave_matvec_gp<D, 1>(x, M, nc, lane, acc, g);
+    case 2: return wave_matvec_gp<D, 2>(x, M, nc, lane, acc, g);
+    case 4: return wave_matvec_gp<D, 4>(x, M, nc, lane, acc, g);
+    case 8: return wave_matvec_gp<D, 8>(x, M, nc, lane, acc, g);
+    default: return wave_matvec_gp<D, 16>(x, M, nc, lane, acc, g);
   }
-  xor_tree(acc, GP);
-  return s == 0 && g < G4;
+}
+
+// acc[q] += zt[r] * P[r][4 gi + q] over ROWS rows from r0, P rotated.
+template <int D, int ROWS>
+__device__ __forceinline__ void remainder_rows(const float* zt, const float* P, int r0, int gi, f32x4& acc) {
+  if constexpr (ROWS > 16) {  // at most 16 rows of operands in flight
+    remainder_rows<D, 16>(zt, P, r0, gi, acc);
+    remainder_rows<D, ROWS - 16>(zt, P, r0 + 16, gi, acc);
+    return;
+  }
+  float zv[ROWS];
+  f32x4 pv[ROWS];
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) {
+    zv[i] = zt[r0 + i];
+    pv[i] = *reinterpret_cast<const f32x4*>(P + (r0 + i) * D + rot_granule(r0 + i, gi, D) * 4);
+  }
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = fmaf(zv[i], pv[i][q], acc[q]);
 }
 
 // e[i] = k[i] - sum_r zt[r] * P[r][i] for i < D, P in the rotated layout.
@@ -135,14 +206,16 @@ __device__ __forceinline__ void wave_key_remainder(const float* k, const float* 
   constexpr int GD = D / 4, SR = 64 / GD;
   const int gi = lane % GD, sr = lane / GD, rows = R / SR;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int r = sr * rows; r < (sr + 1) * rows; ++r) {
-    const float z = zt[r];
-    const f32x4 p = *reinterpret_cast<const f32x4*>(P + r * D + rot_granule(r, gi, D) * 4);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc[q] = fmaf(z, p[q], acc[q]);
+  const int r0 = sr * rows;
+  switch (rows) {
+    case 4: remainder_rows<D, 4>(zt, P, r0, gi, acc); break;
+    case 8: remainder_rows<D, 8>(zt, P, r0, gi, acc); break;
+    case 12: remainder_rows<D, 12>(zt, P, r0, gi, acc); break;
+    case 16: remainder_rows<D, 16>(zt, P, r0, gi, acc); break;
+    case 24: remainder_rows<D, 24>(zt, P, r0, gi, acc); break;
+    default: remainder_rows<D, 32>(zt, P, r0, gi, acc); break;
   }
-  xor_tree(acc, GD);
+  xor_tree<GD>(acc, lane);
   if (sr == 0) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) e[4 * gi + q] = k[4 * gi + q] - acc[q];
@@ -157,30 +230,40 @@ struct TokenLds {
   float* st;                 // [R + RK] out: stored latent, then residual (fp32 values)
 };
 
-// Write one token (whole wave): the exact Key into Krow[0..D), the rounded
-// latent z~ = round(v.B) into Zpage[r * ps + slot] and the rounded residual
-// s~ = round((k - z~.P).R_enc) into Spage[slot * RK + j]; their fp32 values
-// go to L.st.
+// One token's stored values (whole wave, LDS only): the rounded latent
+// z~ = round(v.B) and the rounded residual s~ = round((k - z~.P).R_enc) as
+// fp32 into L.st.  The caller stores them with wave_token_store, after any
+// other memory work it wants issued first.
 template <typename T, int D>
-__device__ __forceinline__ void wave_write_token(const TokenLds& L, int R, int RK, int ps, int slot, T* Krow,
-                                                 T* Zpage, T* Spage, int lane) {
-#pragma unroll
-  for (int i = lane; i < D; i += 64) store_elem(Krow, i, L.k[i]);  // exact: k came from T
+__device__ __forceinline__ void wave_token_values(const TokenLds& L, int R, int RK, int lane) {
   f32x4 acc;
   int g;
   if (wave_matvec<D>(L.v, L.B, R, lane, acc, g)) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) L.st[4 * g + q] = round_store(Zpage, (size_t)(4 * g + q) * ps + slot, acc[q]);
+    for (int q = 0; q < 4; ++q) L.st[4 * g + q] = round_only(acc[q], static_cast<const T*>(nullptr));
   }
   wave_sync();
   wave_key_remainder<D>(L.k, L.st, L.P, R, lane, L.e);
   wave_sync();
   if (wave_matvec<D>(L.e, L.Re, RK, lane, acc, g)) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      L.st[R + 4 * g + q] = round_store(Spage, (size_t)slot * RK + 4 * g + q, acc[q]);
+    for (int q = 0; q < 4; ++q) L.st[R + 4 * g + q] = round_only(acc[q], static_cast<const T*>(nullptr));
   }
   wave_sync();
+}
+
+// Store one token (whole wave): the exact Key into Krow[0..D), z~ into
+// Zpage[r * ps + slot] and s~ into Spage[slot * RK + j] (values exactly
+// representable in T).
+template <typename T, int D>
+__device__ __forceinline__ void wave_token_store(const TokenLds& L, int R, int RK, int ps, int slot, T* Krow,
+                                                 T* Zpage, T* Spage, int lane) {
+#pragma unroll
+  for (int i = lane; i < D; i += 64) store_elem(Krow, i, L.k[i]);
+  for (int x = lane; x < R + RK; x += 64) {
+    if (x < R) store_elem(Zpage, (size_t)x * ps + slot, L.st[x]);
+    else store_elem(Spage, (size_t)slot * RK + (x - R), L.st[x]);
+  }
 }
 
 // Page sums over slots [0, valid) of a page image in LDS (storage dtype,
@@ -205,35 +288,47 @@ __device__ __forceinline__ void wave_page_sums(const uint16_t* Zimg, const uint1
   const int n = lane & 15, qd = lane >> 4;
   const u32x4 ones_u = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
   const bf16x8 ones = __builtin_bit_cast(bf16x8, ones_u);
-  const int kcs = (ps + 31) / 32;
-  for (int mt = 0; mt < R / 16; ++mt) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int kc = 0; kc < kcs; ++kc) {
-      const int t0 = 32 * kc + 8 * qd;
-      bf16x8 a = zero_bf16x8();
-      if (t0 < ps) a = keep_first_n(*reinterpret_cast<const bf16x8*>(Zimg + (16 * mt + n) * ps + t0), valid - t0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ones, acc, 0, 0, 0);
-    }
-    // lane (n, qd) holds rows 4 qd + i of column n; column 0 is taken
-    if (n == 0) {
+  // latents: every fragment of up to 4 channel tiles x 2 slot halves is read
+  // first (addresses clamped into the page, out-of-range parts zeroed)
+  bf16x8 a[4][2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) out[16 * mt + 4 * qd + i] = acc[i];
-    }
-  }
-  for (int nt = 0; nt < (RK + 15) / 16; ++nt) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const int ch = 16 * nt + n;
-    for (int kc = 0; kc < kcs; ++kc) {
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
       const int t0 = 32 * kc + 8 * qd;
-      u32x4 u = {0u, 0u, 0u, 0u};
+      const int row = min(16 * mt + n, R - 1), tt = min(t0, ps - 8);
+      const int keep = (16 * mt < R && t0 < ps) ? valid - t0 : 0;
+      a[mt][kc] = keep_first_n(*reinterpret_cast<const bf16x8*>(Zimg + row * ps + tt), keep);
+    }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+    if (16 * mt < R) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][0], ones, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][1], ones, acc, 0, 0, 0);
+      // lane (n, qd) holds rows 4 qd + i of column n; column 0 is taken
+      if (n == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[16 * mt + 4 * qd + i] = acc[i];
+      }
+    }
+  // residuals: 16-channel tiles as the B operand (32 slots x 16 channels)
+  for (int nt = 0; 16 * nt < RK; ++nt) {
+    const int ch = 16 * nt + n, cc = min(ch, RK - 1);
+    u32x4 u[2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int t = t0 + e;
-        const uint32_t h = (ch < RK && t < valid) ? Simg[t * RK + ch] : 0u;
-        u[e >> 1] |= (e & 1) ? (h << 16) : h;
+        const int t = 32 * kc + 8 * qd + e;
+        const uint32_t h = Simg[min(t, ps - 1) * RK + cc];
+        const uint32_t kept = (ch < RK && t < valid) ? h : 0u;
+        if (e & 1) u[kc][e >> 1] |= kept << 16;
+        else u[kc][e >> 1] = kept;
       }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, __builtin_bit_cast(bf16x8, u), acc, 0, 0, 0);
-    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, __builtin_bit_cast(bf16x8, u[0]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, __builtin_bit_cast(bf16x8, u[1]), acc, 0, 0, 0);
     // every row of the product is the column sum; row 4 qd of column n
     if (qd == 0 && ch < RK) out[R + ch] = acc[0];
   }

@@ -97,7 +97,8 @@ __global__ __launch_bounds__(THREADS) void write_kernel(WriteArgs a) {
       my[D + i] = ld_elem(kin, src + i);
     }
     wave_sync();
-    wave_write_token<T, D>(L, R, RK, ps, slot, Kp + (size_t)slot * D, Zp, Sp, lane);
+    wave_token_values<T, D>(L, R, RK, lane);
+    wave_token_store<T, D>(L, R, RK, ps, slot, Kp + (size_t)slot * D, Zp, Sp, lane);
     for (int x = lane; x < RR; x += 64) {
       if (x < R) store_elem(img, (size_t)x * ps + slot, L.st[x]);
       else store_elem(img, (size_t)R * ps + (size_t)slot * RK + (x - R), L.st[x]);

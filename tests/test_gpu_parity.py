@@ -137,6 +137,42 @@ def test_decode_matches_oracle(name):
     assert np.array_equal(z, z2) and np.array_equal(out, out2)
 
 
+@pytest.mark.parametrize("name", ["g4_d128_p64", "g8_2kv_r48_p32", "tiny_f32", "ragged_permuted"])
+def test_attend_standalone_and_split_partials(name):
+    """basiskv_attend alone: the merged latents, and (z_out NULL) the split
+    partials left in the workspace, combined here in fp64 by the layout and
+    formula the header documents; both against the oracle's latents."""
+    import routed_decode_attention_amd as rda
+    sc = scenario(name)
+    sel, n_sel, _ = oracle.route(sc.d, sc.fac, sc.cache, sc.lengths, sc.q)
+    z_ref, _ = oracle.decode(sc.d, sc.W_ofT, sc.cache, sc.lengths, sc.q, sel, n_sel)
+    g = gc.upload(sc, cache=True, W_ofT=sc.W_ofT)
+    d, w = g.d, sc.w
+    sel_t, nsel_t = torch.from_numpy(sel).cuda(), torch.from_numpy(n_sel).cuda()
+    z = torch.full((d.batch, d.n_q_heads, d.rank_v), float("nan"), device="cuda")
+    rda.basiskv_attend(d, g.cache, g.seq_lens, g.q, sel_t, nsel_t, g.ws, z)
+    torch.cuda.synchronize()
+    rtol, atol = gc.tol(w)
+    np.testing.assert_allclose(gc.host(z).astype(np.float64), z_ref, rtol=rtol, atol=atol)
+
+    g.ws.fill_(0xFF)  # NaN everywhere the kernel does not write
+    rda.basiskv_attend(d, g.cache, g.seq_lens, g.q, sel_t, nsel_t, g.ws, None)
+    torch.cuda.synchronize()
+    ns, pairs, G, R = rda.attend_splits(d), d.batch * d.n_kv_heads, w.group, w.rank_v
+    raw = gc.host(g.ws).view(np.float32)
+    acc = raw[:pairs * ns * G * R].reshape(pairs, ns, G, R).astype(np.float64)
+    ml_at = (pairs * ns * G * R * 4 + 255) // 256 * 256 // 4
+    ml = raw[ml_at:ml_at + pairs * ns * G * 2].reshape(pairs, ns, G, 2).astype(np.float64)
+    m, l = ml[..., 0], ml[..., 1]
+    M = m.max(axis=1, keepdims=True)
+    wgt = np.where(np.isfinite(M), np.exp2(m - np.where(np.isfinite(M), M, 0.0)), 0.0)  # [pairs][ns][G]
+    L = (wgt * l).sum(axis=1)
+    A = (wgt[..., None] * acc).sum(axis=1)
+    zp = np.where(L[..., None] > 0, A / np.where(L > 0, L, 1.0)[..., None], 0.0)
+    zp = zp.reshape(d.batch, d.n_kv_heads * G, R)
+    np.testing.assert_allclose(zp, z_ref, rtol=rtol, atol=atol)
+
+
 @pytest.mark.parametrize("name", ["g4_d128_p64", "ragged_permuted", "g8_2kv_r48_p32"])
 def test_route_physical_ids(name):
     import routed_decode_attention_amd as rda
