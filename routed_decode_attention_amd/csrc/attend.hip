@@ -8,7 +8,7 @@
 // "KV-кэширование", "Математическая формализация").
 //
 // Work split: a (sequence, KV head) pair's selected pages are cut into
-// n_wsplit workgroup splits of ATTEND_WAVES waves; each wave owns
+// n_wsplit workgroup splits of `waves` waves (4 or 8); each wave owns
 // pages_per_wave consecutive selected pages and keeps an online softmax
 // (running max m, denominator l, latent accumulator) for every query head of
 // the group.  The waves of a workgroup merge through LDS and the workgroup
@@ -43,17 +43,20 @@ namespace {
 
 constexpr float NEG_INF = -__builtin_huge_valf();
 
-struct WaveState {  // LDS image of one wave's online-softmax state
-  float m[ATTEND_WAVES][MAX_GROUP];
-  float l[ATTEND_WAVES][MAX_GROUP];
-  float acc[ATTEND_WAVES][MAX_GROUP][MAX_RANK];
+struct WaveState {  // LDS image of every wave's online-softmax state
+  float m[ATTEND_WAVES_MAX][MAX_GROUP];
+  float l[ATTEND_WAVES_MAX][MAX_GROUP];
 };
+// ... and of their latent accumulators: dynamic LDS [waves][group][rank_v]
+__device__ __forceinline__ float& acc_at(float* acc, int w, int h, int r, int G, int R) {
+  return acc[(w * G + h) * R + r];
+}
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Merge the workgroup's waves into one partial per query head: plain stores
 // of (acc, m, l), or the normalised latent when the pair has one split.
-__device__ void finish_split(const AttendArgs& a, WaveState& ws, int pair, int split) {
+__device__ void finish_split(const AttendArgs& a, WaveState& ws, float* wacc, int pair, int split) {
   const int G = a.s.group, R = a.s.rank_v;
   const int tid = threadIdx.x;
   __syncthreads();
@@ -64,15 +67,17 @@ __device__ void finish_split(const AttendArgs& a, WaveState& ws, int pair, int s
     const int h = o / R, r = o % R;
     float M = NEG_INF;
 #pragma unroll
-    for (int w = 0; w < ATTEND_WAVES; ++w) M = fmaxf(M, ws.m[w][h]);
+    for (int w = 0; w < ATTEND_WAVES_MAX; ++w)
+      if (w < a.waves) M = fmaxf(M, ws.m[w][h]);
     float L = 0.f, A = 0.f;
     if (M != NEG_INF) {
 #pragma unroll
-      for (int w = 0; w < ATTEND_WAVES; ++w) {
-        const float e = exp2f(ws.m[w][h] - M);
-        L += e * ws.l[w][h];
-        A += e * ws.acc[w][h][r];
-      }
+      for (int w = 0; w < ATTEND_WAVES_MAX; ++w)
+        if (w < a.waves) {
+          const float e = exp2f(ws.m[w][h] - M);
+          L += e * ws.l[w][h];
+          A += e * acc_at(wacc, w, h, r, G, R);
+        }
     }
     if (single) {
       a.z_out[((size_t)b * a.s.n_q_heads + g * G + h) * R + r] = L > 0.f ? A / L : 0.f;
@@ -182,9 +187,10 @@ struct OnlineSoftmax {
 };
 
 template <int D, int PS, int R, bool PIPE>
-__global__ __launch_bounds__(256) void attend_mfma_kernel(AttendArgs a) {
+__global__ __launch_bounds__(64 * ATTEND_WAVES_MAX) void attend_mfma_kernel(AttendArgs a) {
   constexpr int KS = D / 32, MT = R / 16;
   __shared__ WaveState st;
+  extern __shared__ float s_acc[];
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int pair = wg / a.n_wsplit, split = wg % a.n_wsplit;
@@ -193,7 +199,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttendArgs a) {
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, qd = lane >> 4;
 
-  const int first = (split * ATTEND_WAVES + wave) * a.pages_per_wave;
+  const int first = (split * a.waves + wave) * a.pages_per_wave;
   // this wave's slice of the selection is read in the same round trip as the
   // sequence length and the selection count (every slot < top_k is in bounds;
   // slots past the count are masked below)
@@ -268,18 +274,19 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttendArgs a) {
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) st.acc[wave][n][16 * t + 4 * qd + e] = os.acc[t][e];
+      for (int e = 0; e < 4; ++e) acc_at(s_acc, wave, n, 16 * t + 4 * qd + e, G, R) = os.acc[t][e];
   }
-  finish_split(a, st, pair, split);
+  finish_split(a, st, s_acc, pair, split);
 }
 
 // Plain VALU kernel: one lane per token for q.k, one lane per latent channel
 // for the weighted sum.  Any storage dtype and any supported shape.
 template <typename T>
-__global__ __launch_bounds__(256) void attend_valu_kernel(AttendArgs a) {
+__global__ __launch_bounds__(64 * ATTEND_WAVES_MAX) void attend_valu_kernel(AttendArgs a) {
   __shared__ WaveState st;
+  extern __shared__ float s_acc[];
   __shared__ float s_q[MAX_GROUP][128];
-  __shared__ float s_p[ATTEND_WAVES][64];
+  __shared__ float s_p[ATTEND_WAVES_MAX][64];
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int pair = wg / a.n_wsplit, split = wg % a.n_wsplit;
@@ -297,7 +304,7 @@ __global__ __launch_bounds__(256) void attend_valu_kernel(AttendArgs a) {
 
   const int seq_len = a.seq_lens[b];
   const int nsel = seq_len > 0 ? a.n_sel[pair] : 0;
-  const int first = (split * ATTEND_WAVES + wave) * a.pages_per_wave;
+  const int first = (split * a.waves + wave) * a.pages_per_wave;
   const int last = min(first + a.pages_per_wave, nsel);
 
   float m_run[MAX_GROUP], l_run[MAX_GROUP], acc[MAX_GROUP];
@@ -340,9 +347,9 @@ __global__ __launch_bounds__(256) void attend_valu_kernel(AttendArgs a) {
       st.m[wave][h] = m_run[h];
       st.l[wave][h] = l_run[h];
     }
-    if (lane < R) st.acc[wave][h][lane] = acc[h];
+    if (lane < R) acc_at(s_acc, wave, h, lane, G, R) = acc[h];
   }
-  finish_split(a, st, pair, split);
+  finish_split(a, st, s_acc, pair, split);
 }
 
 // One workgroup per pair: every split of the pair combined, four latent
@@ -376,16 +383,22 @@ AttendPlan plan_attend(const Shape& s) {
   if (ppw > 8) ppw = 8;
   const char* env = getenv("BASISKV_PAGES_PER_WAVE");
   if (env && atoi(env) > 0) ppw = atoi(env) < 32 ? atoi(env) : 32;
+  // Four waves per workgroup (eight halve the split partials but measured
+  // slower on the headline shape).
+  int waves = 4;
+  const char* wenv = getenv("BASISKV_ATTEND_WAVES");
+  if (wenv && (atoi(wenv) == 4 || atoi(wenv) == 8)) waves = atoi(wenv);
   AttendPlan p;
   p.pages_per_wave = ppw;
-  p.n_wsplit = (s.top_k + ATTEND_WAVES * ppw - 1) / (ATTEND_WAVES * ppw);
+  p.waves = waves;
+  p.n_wsplit = (s.top_k + waves * ppw - 1) / (waves * ppw);
   return p;
 }
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   const int pairs = a.s.batch * a.s.n_kv_heads;
-  const dim3 grid(pairs * a.n_wsplit), block(256);
-  const size_t lds = 0;
+  const dim3 grid(pairs * a.n_wsplit), block(64 * a.waves);
+  const size_t lds = (size_t)a.waves * a.s.group * a.s.rank_v * sizeof(float);
   if (attend_mfma_supported(a.s)) {
     const bool pipe = a.pages_per_wave > 1;
     const int key = a.s.head_dim * 10000 + a.s.page_size * 100 + a.s.rank_v;

@@ -6,7 +6,6 @@
 #include <stdio.h>
 #include <string.h>
 
-#include <cstdlib>
 
 #include "../../include/basiskv.h"
 #include "internal.hpp"
@@ -135,6 +134,7 @@ int do_attend(const bkv::Shape& s, const basiskv_cache* cache, const int32_t* se
   const bkv::AttendPlan p = bkv::plan_attend(s);
   a.n_wsplit = p.n_wsplit;
   a.pages_per_wave = p.pages_per_wave;
+  a.waves = p.waves;
   a.scale_log2 = s.scale * 1.4426950408889634f;
   hipError_t e = bkv::launch_attend(a, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "attention launch");
@@ -165,29 +165,15 @@ int do_project(const bkv::Shape& s, const basiskv_factors* f, const float* z, in
   return e == hipSuccess ? BASISKV_OK : hip_fail(e, "projection launch");
 }
 
-// Decode attention then output projection: the split merge is fused into
-// the projection when the matrix-core path applies, else merged first.
+// Decode attention, the merge of its splits, then the output projection.
 int attend_project(const bkv::Shape& s, const basiskv_factors* f, const basiskv_cache* cache,
                    const int32_t* seq_lens, const void* q, const int32_t* sel, const int32_t* n_sel,
                    const int32_t* sel_phys, void* ws, size_t ws_bytes, float* z_out, float* out, void* stream) {
   const WsLayout L = ws_layout(s, 0);
-  const bkv::AttendPlan p = bkv::plan_attend(s);
-  char* w = static_cast<char*>(ws);
-  float* z = z_out ? z_out : reinterpret_cast<float*>(w + L.z);
-  const bool fused = bkv::merge_project_supported(s, p.n_wsplit);
-  int rc = do_attend(s, cache, seq_lens, q, sel, n_sel, ws, ws_bytes, z, stream, sel_phys, !fused);
+  float* z = z_out ? z_out : reinterpret_cast<float*>(static_cast<char*>(ws) + L.z);
+  const int rc = do_attend(s, cache, seq_lens, q, sel, n_sel, ws, ws_bytes, z, stream, sel_phys, true);
   if (rc) return rc;
-  if (!fused) return do_project(s, f, z, s.batch, out, stream);
-  bkv::MergeProjectArgs m;
-  m.s = s;
-  m.part_acc = reinterpret_cast<const float*>(w + L.part_acc);
-  m.part_ml = reinterpret_cast<const float*>(w + L.part_ml);
-  m.n_wsplit = p.n_wsplit;
-  m.W = f->W_ofT;
-  m.out = out;
-  m.z_out = z_out;
-  const hipError_t e = bkv::launch_merge_project(m, as_stream(stream));
-  return e == hipSuccess ? BASISKV_OK : hip_fail(e, "merge + projection launch");
+  return do_project(s, f, z, s.batch, out, stream);
 }
 
 int do_write(const bkv::Shape& s, const basiskv_factors* f, const basiskv_cache* c, const int32_t* pos,

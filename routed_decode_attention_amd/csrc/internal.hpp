@@ -11,7 +11,7 @@ constexpr int MAX_GROUP = 16;      // query heads per KV head handled by one wav
 constexpr int MAX_RANK = 64;       // latent width bound
 constexpr int MAX_RESID = 64;      // residual width bound
 constexpr int MAX_PAGES = 8192;    // page-table columns the router's LDS holds
-constexpr int ATTEND_WAVES = 4;    // waves per attention workgroup
+constexpr int ATTEND_WAVES_MAX = 8;  // waves per attention workgroup (4 or 8 planned)
 
 struct Shape {
   int batch, n_q_heads, n_kv_heads, group, head_dim, rank_v, rank_k, page_size;
@@ -56,7 +56,7 @@ struct AttendArgs {
   float* part_acc;          // [pairs][n_wsplit][group][rank_v]  split partial sums
   float* part_ml;           // [pairs][n_wsplit][group][2]       split (max, denominator)
   float* z_out;             // [batch][n_q_heads][rank_v], written directly when n_wsplit == 1
-  int n_wsplit, pages_per_wave;
+  int n_wsplit, pages_per_wave, waves;
   float scale_log2;         // softmax scale * log2(e)
 };
 
@@ -66,16 +66,6 @@ struct MergeArgs {
   const float *part_acc, *part_ml;
   int n_wsplit;
   float* z_out;             // [batch][n_q_heads][rank_v]
-};
-
-// Merge fused with the output projection (decode rows = batch).
-struct MergeProjectArgs {
-  Shape s;
-  const float *part_acc, *part_ml;
-  int n_wsplit;
-  const void* W;            // [d_model][n_q_heads * rank_v] bf16
-  float* out;               // [batch][d_model]
-  float* z_out;             // nullable [batch][n_q_heads][rank_v]
 };
 
 struct ProjectArgs {
@@ -104,13 +94,12 @@ inline hipError_t allow_lds(const void* kernel, size_t dynamic_bytes) {
 
 // Host-side planning shared by workspace sizing and launches.
 struct AttendPlan {
-  int pages_per_wave, n_wsplit;
+  int pages_per_wave, n_wsplit, waves;
 };
 AttendPlan plan_attend(const Shape& s);
 
 bool attend_mfma_supported(const Shape& s);
 bool route_fits(const Shape& s, bool append);  // the router's LDS fits one CU
-bool merge_project_supported(const Shape& s, int n_wsplit);
 bool project_mfma_supported(int kdim, int n, int dtype);
 bool prefill_mfma_supported(const Shape& s);
 
@@ -119,7 +108,6 @@ hipError_t launch_write(const WriteArgs& a, hipStream_t st);
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
-hipError_t launch_merge_project(const MergeProjectArgs& a, hipStream_t st);
 hipError_t launch_project(const ProjectArgs& a, hipStream_t st);
 hipError_t launch_prefill_attend(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_zero_u32(unsigned* p, size_t n, hipStream_t st);

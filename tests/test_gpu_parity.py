@@ -369,12 +369,13 @@ def test_fused_append_route_equals_separate_calls(name):
         assert np.array_equal(x, y)
 
 
-@pytest.mark.parametrize("ppw", [1, 2, 3, 5])
-def test_pages_per_wave_plans(ppw, monkeypatch):
-    """Every split plan (one page per wave, or several with the next page's
-    loads overlapping) matches the oracle; the ragged tail of the selection
-    lands in a partly filled wave."""
+@pytest.mark.parametrize("ppw,waves", [(1, 4), (2, 4), (3, 8), (5, 8), (1, 8)])
+def test_pages_per_wave_plans(ppw, waves, monkeypatch):
+    """Every split plan (4 or 8 waves per workgroup; one page per wave, or
+    several with the next page's loads overlapping) matches the oracle; the
+    ragged tail of the selection lands in a partly filled wave."""
     monkeypatch.setenv("BASISKV_PAGES_PER_WAVE", str(ppw))
+    monkeypatch.setenv("BASISKV_ATTEND_WAVES", str(waves))
     for name in ("g4_d128_p64", "g8_2kv_r48_p32"):
         w, lengths = CASES[name]
         w = w.with_(top_k=11)
