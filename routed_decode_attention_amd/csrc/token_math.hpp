@@ -317,15 +317,20 @@ __device__ __forceinline__ void wave_page_sums(const uint16_t* Zimg, const uint1
     const int ch = 16 * nt + n, cc = min(ch, RK - 1);
     u32x4 u[2];
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
+    for (int kc = 0; kc < 2; ++kc) {
+      // every element is read (addresses clamped into the page) and then
+      // masked, so the sixteen reads issue together
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = Simg[min(32 * kc + 8 * qd + e, ps - 1) * RK + cc];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int t = 32 * kc + 8 * qd + e;
-        const uint32_t h = Simg[min(t, ps - 1) * RK + cc];
-        const uint32_t kept = (ch < RK && t < valid) ? h : 0u;
+        const uint32_t kept = h[e] & (0u - (uint32_t)(ch < RK && t < valid));
         if (e & 1) u[kc][e >> 1] |= kept << 16;
         else u[kc][e >> 1] = kept;
       }
+    }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, __builtin_bit_cast(bf16x8, u[0]), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, __builtin_bit_cast(bf16x8, u[1]), acc, 0, 0, 0);
