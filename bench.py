@@ -196,7 +196,7 @@ def main():
                                                           nsel_fixed, ws, None, sel_phys=phys_fixed), n_launch)
     t_route = time_launches(lambda i: rda.basiskv_append_route(d, f, caches[i % L], pos, k_new, v_new,
                                                                seq_lens, q, sel, n_sel, scores,
-                                                               sel_phys=sel_phys), n_launch)
+                                                               sel_phys=sel_phys, ws=ws), n_launch)
     # attention + the merge fused into the projection, as the step runs them
     t_decode = time_launches(lambda i: rda.basiskv_decode(d, f, caches[i % L], seq_lens, q, sel_fixed, nsel_fixed,
                                                           ws, out, sel_phys=phys_fixed), n_launch)

@@ -167,10 +167,14 @@ int basiskv_append(const basiskv_dims *dims, const basiskv_factors *f,
  *   sel_phys (nullable) [batch][n_kv_heads][top_k] int32: page_table entries of
  *          sel (-1 padded), which basiskv_attend/decode may take to skip the
  *          page-table lookup.
+ * ws (nullable): a workspace (basiskv_workspace_bytes) whose arrival counters
+ * let several workgroups share the scoring of one (sequence, KV head); NULL
+ * scores each (sequence, KV head) in one workgroup.  Results are identical.
  */
 int basiskv_route(const basiskv_dims *dims, const basiskv_factors *f,
                   const basiskv_cache *cache, const int32_t *seq_lens, const void *q,
-                  int32_t *sel, int32_t *n_sel, float *scores, int32_t *sel_phys, void *stream);
+                  int32_t *sel, int32_t *n_sel, float *scores, int32_t *sel_phys, void *ws,
+                  size_t ws_bytes, void *stream);
 
 /*
  * basiskv_append followed by basiskv_route, in one launch (the decode step
@@ -181,18 +185,21 @@ int basiskv_append_route(const basiskv_dims *dims, const basiskv_factors *f,
                          const basiskv_cache *cache, const int32_t *pos, const void *k_new,
                          const void *v_new, const int32_t *seq_lens, const void *q,
                          int32_t *sel, int32_t *n_sel, float *scores, int32_t *sel_phys,
-                         void *stream);
+                         void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Device workspace, in bytes, that basiskv_attend/decode/decode_step (batch
  * rows) and basiskv_prefill (up to max_prefill_tokens queries) need.  Host function.
- * It carries the attention splits' partial results and intermediate latents
- * between the launches of one call; it needs no initialisation and keeps no
- * state between calls.  Calls that share a workspace must not overlap in time.
+ * Its first 256 * ceil(batch * n_kv_heads / 64) bytes are the router's
+ * arrival counters: zero them once before the first call
+ * (basiskv_workspace_init does), and every call leaves them zero.  The rest
+ * carries the attention splits' partial results and intermediate latents
+ * between the launches of one call and needs no initialisation.  Calls that
+ * share a workspace must not overlap in time.
  */
 size_t basiskv_workspace_bytes(const basiskv_dims *dims, int32_t max_prefill_tokens);
 
-/* Zero-fill a workspace with a fill kernel (optional; safe under graph capture). */
+/* Zero-fill a workspace with a fill kernel (safe under graph capture). */
 int basiskv_workspace_init(const basiskv_dims *dims, void *ws, size_t ws_bytes, void *stream);
 
 /*
@@ -207,7 +214,8 @@ int basiskv_workspace_init(const basiskv_dims *dims, void *ws, size_t ws_bytes, 
  * The selection of each (sequence, KV head) is processed in splits whose
  * partial results are combined afterwards (flash-decoding style).  z_out may
  * be NULL: the combination is then left to the caller and the partials stay
- * at the start of ws, fp32 [batch*n_kv_heads][n_split][group][rank_v] partial
+ * in ws right after the arrival counters (at byte 256 * ceil(batch *
+ * n_kv_heads / 64)), fp32 [batch*n_kv_heads][n_split][group][rank_v] partial
  * sums sum_t 2^(s_t*log2(e) - m) z~_t, followed (at the next 256-byte
  * boundary) by [batch*n_kv_heads][n_split][group][2] pairs (m, sum_t
  * 2^(s_t*log2(e) - m)) with m the split's max of s_t*log2(e) (-inf for an

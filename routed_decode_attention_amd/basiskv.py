@@ -70,8 +70,8 @@ def _load() -> C.CDLL:
         "basiskv_fold_output": ([D, p, p, p, p], C.c_int),
         "basiskv_write": ([D, Fp, Cp, i32, i32, i32, p, p, p], C.c_int),
         "basiskv_append": ([D, Fp, Cp, p, p, p, p], C.c_int),
-        "basiskv_route": ([D, Fp, Cp, p, p, p, p, p, p, p], C.c_int),
-        "basiskv_append_route": ([D, Fp, Cp, p, p, p, p, p, p, p, p, p, p], C.c_int),
+        "basiskv_route": ([D, Fp, Cp, p, p, p, p, p, p, p, sz, p], C.c_int),
+        "basiskv_append_route": ([D, Fp, Cp, p, p, p, p, p, p, p, p, p, p, sz, p], C.c_int),
         "basiskv_decode_step": ([D, Fp, Cp, p, p, p, p, p, p, p, p, p, sz, p, p, p], C.c_int),
         "basiskv_workspace_bytes": ([D, i32], sz),
         "basiskv_workspace_init": ([D, p, sz, p], C.c_int),
@@ -237,8 +237,9 @@ basiskv_workspace_bytes = workspace_bytes
 
 
 def new_workspace(d: Dims, max_prefill_tokens: int = 0, device="cuda") -> torch.Tensor:
-    """A workspace of basiskv_workspace_bytes bytes (needs no initialisation)."""
-    return torch.empty(workspace_bytes(d, max_prefill_tokens), dtype=torch.uint8, device=device)
+    """A zero-filled workspace of basiskv_workspace_bytes bytes (its router
+    counters must start at zero)."""
+    return torch.zeros(workspace_bytes(d, max_prefill_tokens), dtype=torch.uint8, device=device)
 
 
 def basiskv_workspace_init(d: Dims, ws: torch.Tensor, stream=None) -> None:
@@ -248,7 +249,7 @@ def basiskv_workspace_init(d: Dims, ws: torch.Tensor, stream=None) -> None:
 
 def basiskv_route(d: Dims, f: Factors, cache: Cache, seq_lens: torch.Tensor, q: torch.Tensor,
                   sel: torch.Tensor, n_sel: torch.Tensor, scores: torch.Tensor, sel_phys=None,
-                  stream=None) -> None:
+                  ws=None, stream=None) -> None:
     pairs = d.batch * d.n_kv_heads
     fc, cc = f.c(d), cache.c(d)
     _check(_lib.basiskv_route(
@@ -257,13 +258,14 @@ def basiskv_route(d: Dims, f: Factors, cache: Cache, seq_lens: torch.Tensor, q: 
         _ptr(q, "q", d.torch_dtype, d.batch * d.n_q_heads * d.head_dim),
         _ptr(sel, "sel", torch.int32, pairs * d.top_k), _ptr(n_sel, "n_sel", torch.int32, pairs),
         _ptr(scores, "scores", torch.float32, pairs * d.max_pages_per_seq),
-        _ptr(sel_phys, "sel_phys", torch.int32, pairs * d.top_k), _stream(stream)))
+        _ptr(sel_phys, "sel_phys", torch.int32, pairs * d.top_k), _ptr(ws, "ws", torch.uint8),
+        0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def basiskv_append_route(d: Dims, f: Factors, cache: Cache, pos: torch.Tensor, k_new: torch.Tensor,
                          v_new: torch.Tensor, seq_lens: torch.Tensor, q: torch.Tensor,
                          sel: torch.Tensor, n_sel: torch.Tensor, scores: torch.Tensor,
-                         sel_phys=None, stream=None) -> None:
+                         sel_phys=None, ws=None, stream=None) -> None:
     pairs = d.batch * d.n_kv_heads
     need = d.batch * d.n_kv_heads * d.head_dim
     fc, cc = f.c(d), cache.c(d)
@@ -274,7 +276,8 @@ def basiskv_append_route(d: Dims, f: Factors, cache: Cache, pos: torch.Tensor, k
         _ptr(q, "q", d.torch_dtype, d.batch * d.n_q_heads * d.head_dim),
         _ptr(sel, "sel", torch.int32, pairs * d.top_k), _ptr(n_sel, "n_sel", torch.int32, pairs),
         _ptr(scores, "scores", torch.float32, pairs * d.max_pages_per_seq),
-        _ptr(sel_phys, "sel_phys", torch.int32, pairs * d.top_k), _stream(stream)))
+        _ptr(sel_phys, "sel_phys", torch.int32, pairs * d.top_k), _ptr(ws, "ws", torch.uint8),
+        0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def basiskv_decode_step(d: Dims, f: Factors, cache: Cache, pos, k_new, v_new, seq_lens, q, sel, n_sel,

@@ -52,8 +52,6 @@ __device__ __forceinline__ float& acc_at(float* acc, int w, int h, int r, int G,
   return acc[(w * G + h) * R + r];
 }
 
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
 // Merge the workgroup's waves into one partial per query head: plain stores
 // of (acc, m, l), or the normalised latent when the pair has one split.
 __device__ void finish_split(const AttendArgs& a, WaveState& ws, float* wacc, int pair, int split) {

@@ -6,6 +6,10 @@
 
 namespace bkv {
 
+// A value the same in every lane, moved to a scalar register so that the
+// compiler treats branches on it as uniform.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -44,7 +44,13 @@ struct RouteArgs {
   int32_t *sel, *n_sel;
   int32_t* sel_phys;          // optional [batch][n_kv_heads][top_k]: physical ids of sel
   float* scores;
+  uint32_t* arrive;           // [batch][n_kv_heads] zeroed arrival counters; nullptr: one workgroup per pair
 };
+
+// Workgroups per (sequence, KV head) of the router: one for the append (when
+// fused) plus enough to give each about `pages_per_wg` pages to score; 1
+// without arrival counters.
+int route_cluster(const Shape& s, bool append, bool counters);
 
 struct AttendArgs {
   Shape s;

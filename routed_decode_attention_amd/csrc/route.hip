@@ -14,19 +14,27 @@
 // Decode appends the new token before attending (machinelearning.ru
 // "KV-кэширование", "Фаза Decode"), so the fused variant writes it first.
 //
-// One 512-thread workgroup per (sequence, KV head), no cross-workgroup
-// traffic.  The kernel is a short chain of memory round trips, and its
-// serial parts are kept to few instructions:
+// A cluster of 512-thread workgroups per (sequence, KV head): with an
+// append, workgroup 0 writes the new token and the others share the scoring
+// of the remaining pages; the cluster's last workgroup to finish (an arrival
+// counter in the workspace) reads all scores back and selects.  Without
+// counters one workgroup does everything.  The kernel is a short chain of
+// memory round trips, and its serial parts are kept to few instructions:
 //   1. the page-table row, the factors, the query and the new token are
 //      copied straight into LDS together (16-byte direct loads);
-//   2. every lane requests the sums of its first page; meanwhile wave 0
-//      appends the new token (the writer's wave functions, then the page's
-//      sums from scratch over its LDS image) and the other waves project
-//      the query through P and R_dec, four lanes per output;
-//   3. one lane scores one page from its fp32 sums held in registers;
+//   2. every scoring lane requests the sums of its first pages; all waves
+//      project the query through P and R_dec (four lanes per output) and,
+//      when appending, split the new token's three products between them
+//      (partials added in LDS in the chunk writer's order);
+//   3. when appending, wave 0 stores the token and rebuilds its page's sums
+//      from the page's LDS image, then scores that page; a quad of lanes
+//      scores one page from its fp32 sums held in registers;
 //   4. an MSB-first 8-bit radix select over order-preserving keys in LDS
 //      (per-wave histograms merged once per pass) finds the k-th score, and
 //      ballots plus per-wave counts compact the selection in page order.
+#include <algorithm>
+#include <cstdlib>
+
 #include "common.hpp"
 #include "internal.hpp"
 #include "token_math.hpp"
@@ -77,7 +85,7 @@ constexpr int PPL = 4;  // pages per scoring lane and group
 // split over the four lanes of a quad (NG 16-byte channel granules per lane,
 // granule part + 4u) and summed by the quad.
 template <int NG>
-__device__ __forceinline__ void score_group(const f32x4 (&sv)[PPL][4], const float (*qc)[XMAX], int G, int part,
+__device__ __forceinline__ void score_group(const f32x4 (&sv)[PPL][NG], const float (*qc)[XMAX], int G, int part,
                                             float (&best)[PPL]) {
 #pragma unroll
   for (int i = 0; i < PPL; ++i) best[i] = -__builtin_huge_valf();
@@ -107,7 +115,7 @@ __device__ __forceinline__ f32x4 lds4(const uint16_t* p) {
 
 // Dynamic LDS layout (bytes, every part 16-byte aligned).
 struct RouteLds {
-  size_t pid, P, Rd, q, B, Re, vk, img, total;
+  size_t pid, P, Rd, q, B, Re, vk, img, keys, total;
 };
 __host__ __device__ inline size_t a16(size_t x) { return (x + 15) & ~(size_t)15; }
 __host__ __device__ inline RouteLds route_lds(int maxp, int D, int R, int RK, int G, int ps, int es, bool append) {
@@ -121,24 +129,37 @@ __host__ __device__ inline RouteLds route_lds(int maxp, int D, int R, int RK, in
   L.vk = L.Re + (append ? (size_t)D * RK * 4 : 0);
   L.img = L.vk + (append ? (size_t)2 * D * es : 0);
   L.total = L.img + (append ? (size_t)(R * ps + ps * RK) * es : 0);
-  // the score keys reuse the space from P on
-  if (L.total < L.P + (size_t)maxp * 4) L.total = L.P + (size_t)maxp * 4;
+  // the score keys reuse the factors' space (written once the query
+  // projections are done), unless they would reach the appended token and
+  // page image, which are still in use while the pages are scored
+  L.keys = L.P;
+  if (!append) {
+    if (L.total < L.P + (size_t)maxp * 4) L.total = L.P + (size_t)maxp * 4;
+  } else if (L.P + (size_t)maxp * 4 > L.vk) {
+    L.keys = a16(L.total);
+    L.total = L.keys + (size_t)maxp * 4;
+  }
   return L;
 }
 
-template <typename T, bool APPEND, int D>
+// NG: 16-byte channel granules per scoring lane, at least ceil((r + r_k) / 16)
+template <typename T, bool APPEND, int D, int NG>
 __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
   extern __shared__ float lds[];
+  static_assert(NW == CW, "one real wave per virtual wave of the token arithmetic");
   __shared__ float s_qc[MAX_GROUP][XMAX];   // scale * (P.q_h | R_dec.q_h), zero past r + r_k
-  __shared__ float s_tok[4][128];           // appended token: v, k, Key remainder; stored values
+  __shared__ float s_e[128];                // appended token's Key remainder
+  __shared__ float s_st[XMAX];              // appended token's stored values (latent, residual)
   __shared__ float s_newsum[XMAX];          // the appended page's sums
+  __shared__ float s_work[NW * 256];        // token partials, then the radix histograms
 
-  const int pair = blockIdx.x;
   const int H = a.s.n_kv_heads, G = a.s.group;
+  const int C = gridDim.x / (a.s.batch * H);  // workgroups per (sequence, KV head)
+  const int pair = blockIdx.x / C, c = blockIdx.x - pair * C;
   const int R = a.s.rank_v, RK = a.s.rank_k, RR = R + RK, ps = a.s.page_size;
   const int maxp = a.s.max_pages;
   const int b = pair / H, g = pair % H;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
   const int32_t* pt = a.page_table + (size_t)b * maxp;
   char* base = reinterpret_cast<char*>(lds);
   const RouteLds lay = route_lds(maxp, D, R, RK, G, ps, (int)sizeof(T), APPEND);
@@ -146,7 +167,7 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
   float* sP = reinterpret_cast<float*>(base + lay.P);            // [R][D] rotated
   float* sRd = reinterpret_cast<float*>(base + lay.Rd);          // [RK][D] rotated
   T* sq = reinterpret_cast<T*>(base + lay.q);                    // [G][D] the group's query heads
-  uint32_t* s_keys = reinterpret_cast<uint32_t*>(sP);            // [maxp], once the projections are done
+  uint32_t* s_keys = reinterpret_cast<uint32_t*>(base + lay.keys);  // [maxp], once the projections are done
 
   // ---- round trip 1: page-table row, sequence length, append position,
   // factors, query and new token, all requested together ----
@@ -157,8 +178,14 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
     if (pos < 0 || pos >= maxp * ps) pos = -1;
   }
   const bool app = APPEND && pos >= 0;
+  const bool app0 = app && c == 0;  // this workgroup appends the token
   const int apage = app ? pos / ps : 0, slot = app ? pos % ps : 0;
   const int npg = n > 0 ? min((n + ps - 1) / ps, maxp) : 0;
+  // pages [lo, hi) scored here: with an append in a cluster, workgroup 0
+  // appends (and scores the appended page) and the others share the pages
+  const int nsc = APPEND && C > 1 ? C - 1 : C, sidx = APPEND && C > 1 ? c - 1 : c;
+  const int per = (npg + nsc - 1) / nsc;
+  const int lo = sidx < 0 ? 0 : min(npg, sidx * per), hi = sidx < 0 ? 0 : min(npg, lo + per);
   const bool in_regs = RR <= VMAX;  // a page's sums fit one lane's registers
   const bool pt16 = (maxp & 3) == 0 && (reinterpret_cast<uintptr_t>(pt) & 15) == 0;
   {
@@ -170,7 +197,7 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
     first = dma_stage(sRd, RK * D / 4, [&](int G_) { return Rd + 16 * rot_source(G_, D); }, first, NW, wave, lane);
     first = dma_stage(sq, (int)(G * D * sizeof(T) / 16), [&](int G_) { return q + 16 * G_; }, first, NW, wave, lane);
     if (pt16) first = dma_stage(s_pid, maxp / 4, [&](int G_) { return ptc + 16 * G_; }, first, NW, wave, lane);
-    if (app) {
+    if (app0) {
       const char* B = reinterpret_cast<const char*>(a.B + (size_t)g * D * R);
       const char* Re = reinterpret_cast<const char*>(a.R_enc + (size_t)g * D * RK);
       const size_t tok = ((size_t)b * H + g) * D;
@@ -189,130 +216,202 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
 
   // ---- round trip 2: page sums for scoring, requested now.  Four lanes
   // per page: lane `part` of a quad holds channel granules part + 4u of its
-  // page's row (contiguous 64 bytes per quad and load); quad q takes pages
-  // q + 128 m, PPL of them per group ----
-  const int quad = wave * 16 + (lane >> 2), part = lane & 3;
-  f32x4 sv[PPL][4];
+  // page's row (contiguous 64 bytes per quad and load); quad q of nq takes
+  // pages lo + q + nq m, PPL of them per group.  In the appending workgroup
+  // wave 0 writes the token while waves 1.. score ----
+  const int nq = app0 ? 16 * (NW - 1) : 16 * NW;
+  const int quad = (app0 ? wave - 1 : wave) * 16 + (lane >> 2), part = lane & 3;
+  const bool scorer = !(app0 && wave == 0);
+  f32x4 sv[PPL][NG];
+  // The loads are unconditional (a page past the sequence reads page 0, a
+  // granule past the row reads the row's last one), so all of a group's
+  // requests are in flight together; mask_group() zeroes the extra ones
+  // right before the scores need them.
+  uint32_t svok = 0;  // bit 4 i + u: sv[i][u] holds real sums
   auto load_group = [&](int m0) {
+    if (npg == 0) return;
+    svok = 0;
 #pragma unroll
     for (int i = 0; i < PPL; ++i) {
-      const int j = quad + 128 * (m0 + i);
-      const f32x4* row = j < npg ? reinterpret_cast<const f32x4*>(a.summ + ((size_t)s_pid[j] * H + g) * RR) : nullptr;
+      const int jj = quad + nq * (m0 + i);  // negative on the appending wave
+      const bool ok = (unsigned)jj < (unsigned)(hi - lo);
+      const f32x4* row = reinterpret_cast<const f32x4*>(a.summ + ((size_t)s_pid[ok ? lo + jj : 0] * H + g) * RR);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < NG; ++u) {
         const int gr = part + 4 * u;
-        sv[i][u] = (row && 4 * gr < RR) ? row[gr] : f32x4{0.f, 0.f, 0.f, 0.f};
+        sv[i][u] = row[min(gr, RR / 4 - 1)];
+        svok |= (uint32_t)(ok && 4 * gr < RR) << (4 * i + u);
       }
     }
   };
-
-  if (app && wave == 0) {
-    // ---- the new token (wave 0): exact Key, rounded latent and residual,
-    // then its page's sums from scratch over slots [0, slot] ----
-    const int aphys = s_pid[apage];
-    T* Kp = static_cast<T*>(a.K) + ((size_t)aphys * H + g) * ps * D;
-    T* Zp = static_cast<T*>(a.Z) + ((size_t)aphys * H + g) * R * ps;
-    T* Sp = static_cast<T*>(a.S) + ((size_t)aphys * H + g) * ps * RK;
-    T* img = reinterpret_cast<T*>(base + lay.img);
-    PageImage pg;
-    pg.load(Zp, Sp, (int)(R * ps * sizeof(T) / 16), (int)(ps * RK * sizeof(T) / 16), lane);
-    const T* vk = reinterpret_cast<const T*>(base + lay.vk);
+  auto mask_group = [&]() {
 #pragma unroll
-    for (int i = lane; i < D; i += 64) {
-      s_tok[0][i] = ld_elem(vk, i);
-      s_tok[1][i] = ld_elem(vk, D + i);
-    }
-    if (in_regs) load_group(0);  // after the page, ahead of the arithmetic
-    wave_sync();
-    const TokenLds L{s_tok[0], s_tok[1], reinterpret_cast<const float*>(base + lay.B), sP,
-                     reinterpret_cast<const float*>(base + lay.Re), s_tok[2], s_tok[3]};
-    wave_token_values<T, D>(L, R, RK, lane);
-    pg.store(img, lane);
-    wave_sync();
-    // the new token's values replace what the page held in its slot
-    for (int x = lane; x < RR; x += 64) {
-      if (x < R) store_elem(img, (size_t)x * ps + slot, L.st[x]);
-      else store_elem(img, (size_t)R * ps + (size_t)slot * RK + (x - R), L.st[x]);
-    }
-    wave_sync();
-    wave_page_sums(img, img + (size_t)R * ps, R, RK, ps, slot + 1, s_newsum, lane);
-    wave_sync();
-    // memory writes last: the token, then the page's sums
-    wave_token_store<T, D>(L, R, RK, ps, slot, Kp + (size_t)slot * D, Zp, Sp, lane);
-    for (int x = lane; x < RR; x += 64) a.summ[((size_t)aphys * H + g) * RR + x] = s_newsum[x];
-  } else {
-    // ---- the query seen through the latent predictor P and the residual
-    // decoder R_dec: one task per (output row x, quarter c) for every head,
-    // lane c taking 16-byte pieces 4u + c of the row; a quad sums the
-    // quarters.  Outputs past r + r_k (up to VMAX) are zero ----
-    const int q0 = app ? 64 : 0;
-    for (int t = tid - q0; t < RR * 4; t += RT - q0) {
-      const int x = t >> 2, c = t & 3;
-      const int xr = x < R ? x : x - R;
-      const float* row = (x < R ? sP : sRd) + xr * D;
-      f32x4 pr[D / 16];
+    for (int i = 0; i < PPL; ++i)
 #pragma unroll
-      for (int u = 0; u < D / 16; ++u) pr[u] = lds4(row + rot_granule(xr, 4 * u + c, D) * 4);
-      for (int h = 0; h < G; ++h) {
-        const T* qh = sq + h * D;
-        float acc = 0.f;
+      for (int u = 0; u < NG; ++u) {
+        const uint32_t keep = 0u - ((svok >> (4 * i + u)) & 1u);
 #pragma unroll
-        for (int u = 0; u < D / 16; ++u) {
-          const f32x4 q4 = lds4(qh + 16 * u + 4 * c);
-          acc = fmaf(pr[u][0], q4[0], acc);
-          acc = fmaf(pr[u][1], q4[1], acc);
-          acc = fmaf(pr[u][2], q4[2], acc);
-          acc = fmaf(pr[u][3], q4[3], acc);
-        }
-        acc = quad_sum(acc);
-        if (c == 0) s_qc[h][x] = acc * a.s.scale;
+        for (int e = 0; e < 4; ++e) sv[i][u][e] = __uint_as_float(__float_as_uint(sv[i][u][e]) & keep);
       }
-    }
-    if (RR < VMAX)
-      for (int t = tid - q0; t < G * (VMAX - RR); t += RT - q0) s_qc[t / (VMAX - RR)][RR + t % (VMAX - RR)] = 0.f;
-    if (in_regs) load_group(0);  // after the LDS work, so wave 0's page goes first
-  }
-  __syncthreads();
-
-  // ---- one lane per page: score from the page's fp32 sums ----
+  };
+  auto score = [&](float (&best)[PPL]) { score_group<NG>(sv, s_qc, G, part, best); };
   auto finish = [&](int j, float best) {
     const float sc = best / (float)min(ps, n - j * ps);
     a.scores[(size_t)pair * maxp + j] = sc;
     s_keys[j] = float_key(sc);
   };
-  if (in_regs) {
-    const int ng = (RR + 15) / 16;  // channel granules per lane
-    for (int m0 = 0; 128 * m0 < npg; m0 += PPL) {
-      if (m0 > 0) load_group(m0);
-      if (app) {  // the appended page's new sums replace its loaded row
+
+  // the appended page and its LDS image (wave 0)
+  const int aphys = app0 ? s_pid[apage] : 0;
+  T* Kp = static_cast<T*>(a.K) + ((size_t)aphys * H + g) * ps * D;
+  T* Zp = static_cast<T*>(a.Z) + ((size_t)aphys * H + g) * R * ps;
+  T* Sp = static_cast<T*>(a.S) + ((size_t)aphys * H + g) * ps * RK;
+  T* img = reinterpret_cast<T*>(base + lay.img);
+  PageImage pg;
+  if (app0 && wave == 0) pg.load(Zp, Sp, (int)(R * ps * sizeof(T) / 16), (int)(ps * RK * sizeof(T) / 16), lane);
+  // every wave requests a group (unused on the appending wave), which keeps
+  // the registers of the two kinds of request apart
+  if (in_regs) load_group(0);
+
+  // the new token's three products, each split over the NW waves (wave w
+  // takes the w-th eighth of the contraction); the partials meet in LDS and
+  // are added in wave order, the chunk writer's order for the same split
+  const T* vn = reinterpret_cast<const T*>(base + lay.vk);
+  const T* kn = vn + D;
+  const float* sB = reinterpret_cast<const float*>(base + lay.B);
+  const float* sRe = reinterpret_cast<const float*>(base + lay.Re);
+  float* s_lr = s_work;            // [NW][64] latent, later residual partials
+  float* s_kp = s_work + NW * 64;  // [NW][128] Key-estimate partials
+  if (app0) {
+    f32x4 acc;
+    int gq;
+    if (part_matvec<D>(vn, sB, R, wave, lane, acc, gq))
+      *reinterpret_cast<f32x4*>(s_lr + wave * 64 + 4 * gq) = acc;
+  }
+
+  // ---- the query seen through the latent predictor P and the residual
+  // decoder R_dec: one task per (output row x, quarter c) for every head,
+  // lane c taking 16-byte pieces 4u + c of the row; a quad sums the
+  // quarters.  Outputs past r + r_k (up to VMAX) are zero ----
+  for (int t = tid; t < RR * 4; t += RT) {
+    const int x = t >> 2, c = t & 3;
+    const int xr = x < R ? x : x - R;
+    const float* row = (x < R ? sP : sRd) + xr * D;
+    f32x4 pr[D / 16];
 #pragma unroll
-        for (int i = 0; i < PPL; ++i)
-          if (quad + 128 * (m0 + i) == apage) {
+    for (int u = 0; u < D / 16; ++u) pr[u] = lds4(row + rot_granule(xr, 4 * u + c, D) * 4);
+    for (int h = 0; h < G; ++h) {
+      const T* qh = sq + h * D;
+      float acc = 0.f;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const int gr = part + 4 * u;
-              sv[i][u] = 4 * gr < RR ? *reinterpret_cast<const f32x4*>(s_newsum + 4 * gr) : f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-          }
+      for (int u = 0; u < D / 16; ++u) {
+        const f32x4 q4 = lds4(qh + 16 * u + 4 * c);
+        acc = fmaf(pr[u][0], q4[0], acc);
+        acc = fmaf(pr[u][1], q4[1], acc);
+        acc = fmaf(pr[u][2], q4[2], acc);
+        acc = fmaf(pr[u][3], q4[3], acc);
       }
-      float best[PPL];
-      switch (ng) {
-        case 1: score_group<1>(sv, s_qc, G, part, best); break;
-        case 2: score_group<2>(sv, s_qc, G, part, best); break;
-        case 3: score_group<3>(sv, s_qc, G, part, best); break;
-        default: score_group<4>(sv, s_qc, G, part, best); break;
-      }
-#pragma unroll
-      for (int i = 0; i < PPL; ++i) {
-        const int j = quad + 128 * (m0 + i);
-        if (part == 0 && j < npg) finish(j, best[i]);
-      }
+      acc = quad_sum(acc);
+      if (c == 0) s_qc[h][x] = acc * a.s.scale;
     }
+  }
+  if (RR < VMAX)
+    for (int t = tid; t < G * (VMAX - RR); t += RT) s_qc[t / (VMAX - RR)][RR + t % (VMAX - RR)] = 0.f;
+  lds_barrier();  // the scoring loads stay in flight
+
+  if (app0) {
+    // z~ rows of this wave, then its part of z~.P
+    const int RW = R / NW;
+    if (lane < RW) {
+      const int x = wave * RW + lane;
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) sum += s_lr[w * 64 + x];
+      s_st[x] = round_only(sum, static_cast<const T*>(nullptr));
+    }
+    wave_sync();
+    const f32x4 kh = part_remainder<D>(s_st, sP, R, wave, lane);
+    if (lane < D / 4) *reinterpret_cast<f32x4*>(s_kp + wave * 128 + 4 * lane) = kh;
+    lds_barrier();
+    // Key remainder rows of this wave, then its part of e.R_enc
+    if (lane < D / NW) {
+      const int i = wave * (D / NW) + lane;
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) sum += s_kp[w * 128 + i];
+      s_e[i] = lds_elem(kn, i) - sum;
+    }
+    wave_sync();
+    f32x4 acc;
+    int gq;
+    if (part_matvec<D>(s_e, sRe, RK, wave, lane, acc, gq))
+      *reinterpret_cast<f32x4*>(s_lr + wave * 64 + 4 * gq) = acc;
+    lds_barrier();
+  }
+
+  if (app0 && wave == 0) {
+    // ---- wave 0: s~, the page image with the new slot, the page's sums
+    // from scratch over slots [0, slot], the appended page's score, then
+    // the memory writes: the token, then the page's sums ----
+    if (lane < RK) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) sum += s_lr[w * 64 + lane];
+      s_st[R + lane] = round_only(sum, static_cast<const T*>(nullptr));
+    }
+    pg.store(img, lane);
+    wave_sync();
+    for (int x = lane; x < RR; x += 64) {
+      if (x < R) store_elem(img, (size_t)x * ps + slot, s_st[x]);
+      else store_elem(img, (size_t)R * ps + (size_t)slot * RK + (x - R), s_st[x]);
+    }
+    wave_sync();
+    wave_page_sums(img, img + (size_t)R * ps, R, RK, ps, slot + 1, s_newsum, lane);
+    wave_sync();
+    if (in_regs) {
+      // quad 0 scores the page from its new sums
+#pragma unroll
+      for (int i = 0; i < PPL; ++i)
+#pragma unroll
+        for (int u = 0; u < NG; ++u) {
+          const int gr = part + 4 * u;
+          sv[i][u] = (i == 0 && lane < 4 && 4 * gr < RR) ? *reinterpret_cast<const f32x4*>(s_newsum + 4 * gr)
+                                                         : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      float best[PPL];
+      score(best);
+      if (lane == 0 && apage < npg) finish(apage, best[0]);
+    }
+    const TokenLds<T> L{vn, kn, sB, sP, sRe, s_e, s_st};
+    wave_token_store<T, D>(L, R, RK, ps, slot, Kp + (size_t)slot * D, Zp, Sp, lane);
+    for (int x = lane; x < RR; x += 64) a.summ[((size_t)aphys * H + g) * RR + x] = s_newsum[x];
+  }
+
+  // ---- one quad per page: score from the page's fp32 sums ----
+  if (in_regs) {
+    if (scorer)
+      for (int m0 = 0; lo + nq * m0 < hi; m0 += PPL) {
+        if (m0 > 0) load_group(m0);
+        mask_group();
+        float best[PPL];
+        score(best);
+#pragma unroll
+        for (int i = 0; i < PPL; ++i) {
+          const int j = lo + quad + nq * (m0 + i);
+          if (part == 0 && j < hi && !(app && j == apage)) finish(j, best[i]);
+        }
+      }
   } else {
-    // wide sums (r + r_k > 64): 64 channels at a time, every head's dot kept
+    // wide sums (r + r_k > 64): 64 channels at a time, every head's dot
+    // kept; the appending workgroup scores the appended page from its new
+    // sums, the others skip it
+    if (app0) lds_barrier();  // the appended page's sums are in s_newsum
     float v[VMAX];
     float d[MAX_GROUP];
-    for (int j = tid; j < npg; j += RT) {
+    const int cnt = hi - lo + (app0 && (apage < lo || apage >= hi) && apage < npg ? 1 : 0);
+    for (int t = tid; t < cnt; t += RT) {
+      const int j = t < hi - lo ? lo + t : apage;
+      if (app && !app0 && j == apage) continue;
       const float* sm = a.summ + ((size_t)s_pid[j] * H + g) * RR;
 #pragma unroll
       for (int h = 0; h < MAX_GROUP; ++h) d[h] = 0.f;
@@ -326,7 +425,7 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
           v[4 * u + 2] = t4.z;
           v[4 * u + 3] = t4.w;
         }
-        if (app && j == apage) {
+        if (app0 && j == apage) {
 #pragma unroll
           for (int x = 0; x < VMAX; ++x)
             if (x0 + x < RR) v[x] = s_newsum[x0 + x];
@@ -348,13 +447,30 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
   }
   __syncthreads();
 
+  // ---- a cluster's last workgroup to finish scoring selects: it takes
+  // every page's score back from memory ----
+  if (C > 1) {
+    __shared__ int s_last;
+    if (tid == 0) {
+      const uint32_t old = __hip_atomic_fetch_add(a.arrive + pair, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = old == (uint32_t)(C - 1);
+      if (s_last) __hip_atomic_store(a.arrive + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    const float* sc = a.scores + (size_t)pair * maxp;
+    for (int j = tid; j < npg; j += RT)
+      s_keys[j] = float_key(__hip_atomic_load(sc + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    __syncthreads();
+  }
+
   // ---- top-k selection ----
   // MSB-first radix select over the page keys, starting at the highest bit
   // where they differ; a pass stops the search when the bucket holding the
   // k-th key is exactly what remains to be taken.  The selected pages are
   // then those whose masked key exceeds the found prefix, plus the first
   // `take_eq` (in page order) of those equal to it.
-  __shared__ int s_whist[NW][256];
+  int (*s_whist)[256] = reinterpret_cast<int (*)[256]>(s_work);  // [NW][256]
   __shared__ int s_wcnt[NW][2];
   __shared__ uint32_t s_red[NW][2];
   __shared__ int s_digit, s_krem, s_done;
@@ -482,21 +598,39 @@ size_t route_lds_bytes(const Shape& s, bool append) {
       .total;
 }
 
-template <typename T, bool APPEND, int D>
+template <typename T, bool APPEND, int D, int NG>
 hipError_t launch_t(const RouteArgs& a, hipStream_t st) {
   const size_t lds = route_lds_bytes(a.s, APPEND);
-  const hipError_t e = allow_lds((const void*)route_kernel<T, APPEND, D>, lds);
+  const hipError_t e = allow_lds((const void*)route_kernel<T, APPEND, D, NG>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((route_kernel<T, APPEND, D>), dim3(a.s.batch * a.s.n_kv_heads), dim3(RT), lds, st, a);
+  const int cl = route_cluster(a.s, APPEND, a.arrive != nullptr);
+  hipLaunchKernelGGL((route_kernel<T, APPEND, D, NG>), dim3(a.s.batch * a.s.n_kv_heads * cl), dim3(RT), lds, st, a);
   return hipGetLastError();
+}
+
+template <typename T, bool APPEND, int D>
+hipError_t launch_g(const RouteArgs& a, hipStream_t st) {
+  const int ng = (a.s.rank_v + a.s.rank_k + 15) / 16;
+  if (ng <= 2) return launch_t<T, APPEND, D, 2>(a, st);
+  if (ng == 3) return launch_t<T, APPEND, D, 3>(a, st);
+  return launch_t<T, APPEND, D, 4>(a, st);  // also wide rows, which do not use it
 }
 
 template <typename T, bool APPEND>
 hipError_t launch_d(const RouteArgs& a, hipStream_t st) {
-  return a.s.head_dim == 64 ? launch_t<T, APPEND, 64>(a, st) : launch_t<T, APPEND, 128>(a, st);
+  return a.s.head_dim == 64 ? launch_g<T, APPEND, 64>(a, st) : launch_g<T, APPEND, 128>(a, st);
 }
 
 }  // namespace
+
+int route_cluster(const Shape& s, bool append, bool counters) {
+  if (!counters) return 1;
+  int per = 128;  // pages per scoring workgroup
+  if (const char* e = getenv("BASISKV_ROUTE_PAGES_PER_WG")) per = std::max(1, std::min(4096, atoi(e)));
+  const int nsc = (s.max_pages + per - 1) / per;
+  if (nsc <= 1) return 1;  // one workgroup scores while it appends
+  return std::min(nsc + (append ? 1 : 0), 32);
+}
 
 bool route_fits(const Shape& s, bool append) {
   // the kernel's static arrays take under 24 KiB; gfx950 has 160 KiB per CU

@@ -32,6 +32,16 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Workgroup barrier that orders LDS only: the wave's LDS accesses complete
+// before it, while its global loads stay in flight across it (a plain
+// __syncthreads also waits for every outstanding global load).  Not for
+// handing off LDS written by direct global -> LDS copies.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // LDS layout of the factor P (and R_dec): row x holds D floats whose 16-byte
 // granules are rotated by x, so lanes reading the same column of different
 // rows (or different columns of one row) spread over the banks.
@@ -71,10 +81,12 @@ struct PageImage {
     s = static_cast<const u32x4*>(Spage);
     nz16 = nz;
     n16 = nz + ns;
+    // unconditional loads (granules past the image re-read its last one and
+    // are not stored), so all are in flight together
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int c = lane + 64 * u;
-      if (c < n16) v[u] = c < nz16 ? z[c] : s[c - nz16];
+      const int c = min(lane + 64 * u, n16 - 1);
+      v[u] = *(c < nz16 ? z + c : s + (c - nz16));
     }
   }
   __device__ __forceinline__ void store(void* img, int lane) const {
@@ -123,9 +135,13 @@ __device__ __forceinline__ void xor_tree(f32x4& a, int lane) {
   }
 }
 
+// Element i of an LDS operand as fp32 (storage dtype or fp32).
+__device__ __forceinline__ float lds_elem(const float* p, int i) { return p[i]; }
+__device__ __forceinline__ float lds_elem(const uint16_t* p, int i) { return bf16_to_f32(p[i]); }
+
 // acc[k] += x[i] * M[i][k] for i < ROWS in order (M rows nc floats apart).
-template <int ROWS>
-__device__ __forceinline__ void rows_fma(const float* x, const float* M, int nc, f32x4& acc) {
+template <int ROWS, typename X>
+__device__ __forceinline__ void rows_fma(const X* x, const float* M, int nc, f32x4& acc) {
   if constexpr (ROWS > 16) {  // at most 16 rows of operands in flight
     rows_fma<16>(x, M, nc, acc);
     rows_fma<ROWS - 16>(x + 16, M + (size_t)16 * nc, nc, acc);
@@ -135,7 +151,7 @@ __device__ __forceinline__ void rows_fma(const float* x, const float* M, int nc,
   f32x4 mv[ROWS];
 #pragma unroll
   for (int i = 0; i < ROWS; ++i) {
-    xv[i] = x[i];
+    xv[i] = lds_elem(x, i);
     mv[i] = *reinterpret_cast<const f32x4*>(M + (size_t)i * nc);
   }
 #pragma unroll
@@ -144,46 +160,52 @@ __device__ __forceinline__ void rows_fma(const float* x, const float* M, int nc,
     for (int k = 0; k < 4; ++k) acc[k] = fmaf(xv[i], mv[i][k], acc[k]);
 }
 
-// out[c] = sum_i x[i] * M[i][c] for c < nc (nc % 4 == 0, nc <= 64); x [D]
-// fp32 and M row-major [D][nc] fp32, both in LDS.  Lane layout: output group
-// g = lane % GP (GP = nc/4 rounded up to a power of two), row slice
-// s = lane / GP of D / (64 / GP) consecutive rows.  Returns whether this lane
-// holds outputs 4g..4g+3 (slice 0, g < nc/4) in acc.
-template <int D, int GP>
-__device__ __forceinline__ bool wave_matvec_gp(const float* x, const float* M, int nc, int lane, f32x4& acc,
+// A token's three products are split over CW "virtual waves" of 64 lanes,
+// each taking a fixed 1/CW of the contraction; their partials are combined
+// in virtual-wave order starting from 0.  The router runs the CW virtual
+// waves as its CW real waves at once (partials through LDS); the chunk
+// writer runs them in turn on one wave.  The same additions happen in the
+// same order, so both produce the same bits.
+constexpr int CW = 8;
+
+// Partial of virtual wave w for out[c] = sum_i x[i] M[i][c] (nc % 4 == 0,
+// nc <= 64; x [D], M row-major [D][nc], both in LDS): rows
+// [w D/CW, (w+1) D/CW).  Lane layout: output group g = lane % GP (GP = nc/4
+// rounded up to a power of two), slice s = lane / GP of RS consecutive rows
+// (S slices; lanes of later slices contribute 0), slices combined by the xor
+// tree.  Returns whether this lane holds outputs 4g..4g+3 in acc.
+template <int D, int GP, typename X>
+__device__ __forceinline__ bool part_matvec_gp(const X* x, const float* M, int nc, int w, int lane, f32x4& acc,
                                                int& g) {
-  constexpr int ROWS = D * GP / 64;
+  constexpr int RW = D / CW, S = (64 / GP) < RW ? 64 / GP : RW, RS = RW / S;
   const int G4 = nc >> 2;
   g = lane & (GP - 1);
   const int s = lane / GP;
+  const int r0 = w * RW + (s < S ? s : 0) * RS;
   acc = f32x4{0.f, 0.f, 0.f, 0.f};
   // lanes past the last output group read group 0 and are discarded
-  rows_fma<ROWS>(x + s * ROWS, M + (size_t)s * ROWS * nc + 4 * (g < G4 ? g : 0), nc, acc);
+  rows_fma<RS>(x + r0, M + (size_t)r0 * nc + 4 * (g < G4 ? g : 0), nc, acc);
+  if (s >= S) acc = f32x4{0.f, 0.f, 0.f, 0.f};
   xor_tree<GP>(acc, lane);
   return s == 0 && g < G4;
 }
 
-template <int D>
-__device__ __forceinline__ bool wave_matvec(const float* x, const float* M, int nc, int lane, f32x4& acc,
+template <int D, typename X>
+__device__ __forceinline__ bool part_matvec(const X* x, const float* M, int nc, int w, int lane, f32x4& acc,
                                             int& g) {
   const int G4 = nc >> 2;
   switch (G4 <= 1 ? 1 : 1 << (32 - __builtin_clz(G4 - 1))) {
-    case 1: return wave_matvec_gp<D, 1>(x, M, nc, lane, acc, g);
-    case 2: return wave_matvec_gp<D, 2>(x, M, nc, lane, acc, g);
-    case 4: return wave_matvec_gp<D, 4>(x, M, nc, lane, acc, g);
-    case 8: return wave_matvec_gp<D, 8>(x, M, nc, lane, acc, g);
-    default: return wave_matvec_gp<D, 16>(x, M, nc, lane, acc, g);
+    case 1: return part_matvec_gp<D, 1>(x, M, nc, w, lane, acc, g);
+    case 2: return part_matvec_gp<D, 2>(x, M, nc, w, lane, acc, g);
+    case 4: return part_matvec_gp<D, 4>(x, M, nc, w, lane, acc, g);
+    case 8: return part_matvec_gp<D, 8>(x, M, nc, w, lane, acc, g);
+    default: return part_matvec_gp<D, 16>(x, M, nc, w, lane, acc, g);
   }
 }
 
 // acc[q] += zt[r] * P[r][4 gi + q] over ROWS rows from r0, P rotated.
 template <int D, int ROWS>
 __device__ __forceinline__ void remainder_rows(const float* zt, const float* P, int r0, int gi, f32x4& acc) {
-  if constexpr (ROWS > 16) {  // at most 16 rows of operands in flight
-    remainder_rows<D, 16>(zt, P, r0, gi, acc);
-    remainder_rows<D, ROWS - 16>(zt, P, r0 + 16, gi, acc);
-    return;
-  }
   float zv[ROWS];
   f32x4 pv[ROWS];
 #pragma unroll
@@ -197,57 +219,80 @@ __device__ __forceinline__ void remainder_rows(const float* zt, const float* P, 
     for (int q = 0; q < 4; ++q) acc[q] = fmaf(zv[i], pv[i][q], acc[q]);
 }
 
-// e[i] = k[i] - sum_r zt[r] * P[r][i] for i < D, P in the rotated layout.
-// Lane layout: column group gi = lane % (D/4), latent slice lane / (D/4) of
-// R / (256/D) consecutive rows (R a multiple of 16).
+// Partial of virtual wave w for kh[i] = sum_r zt[r] P[r][i], i < D (P in the
+// rotated layout, R a multiple of 16): latent rows [w R/CW, (w+1) R/CW).
+// Lane layout: column group gi = lane % (D/4), slice lane / (D/4) of RS rows
+// (S slices: the largest power of two <= 256/D dividing R/CW; lanes of later
+// slices contribute 0), slices combined by the xor tree.  Lanes of slice 0
+// hold kh[4gi .. 4gi+3].
 template <int D>
-__device__ __forceinline__ void wave_key_remainder(const float* k, const float* zt, const float* P, int R,
-                                                   int lane, float* e) {
-  constexpr int GD = D / 4, SR = 64 / GD;
-  const int gi = lane % GD, sr = lane / GD, rows = R / SR;
+__device__ __forceinline__ f32x4 part_remainder(const float* zt, const float* P, int R, int w, int lane) {
+  constexpr int GD = D / 4, SL = 64 / GD;
+  const int RW = R / CW;
+  int S = SL;
+  while (RW % S) S >>= 1;
+  const int RS = RW / S;
+  const int gi = lane % GD, sr = lane / GD;
+  const int r0 = w * RW + (sr < S ? sr : 0) * RS;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const int r0 = sr * rows;
-  switch (rows) {
-    case 4: remainder_rows<D, 4>(zt, P, r0, gi, acc); break;
-    case 8: remainder_rows<D, 8>(zt, P, r0, gi, acc); break;
-    case 12: remainder_rows<D, 12>(zt, P, r0, gi, acc); break;
-    case 16: remainder_rows<D, 16>(zt, P, r0, gi, acc); break;
-    case 24: remainder_rows<D, 24>(zt, P, r0, gi, acc); break;
-    default: remainder_rows<D, 32>(zt, P, r0, gi, acc); break;
+  switch (RS) {
+    case 1: remainder_rows<D, 1>(zt, P, r0, gi, acc); break;
+    case 2: remainder_rows<D, 2>(zt, P, r0, gi, acc); break;
+    case 3: remainder_rows<D, 3>(zt, P, r0, gi, acc); break;
+    default: remainder_rows<D, 4>(zt, P, r0, gi, acc); break;
   }
+  if (sr >= S) acc = f32x4{0.f, 0.f, 0.f, 0.f};
   xor_tree<GD>(acc, lane);
-  if (sr == 0) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) e[4 * gi + q] = k[4 * gi + q] - acc[q];
-  }
+  return acc;
 }
 
 // LDS operands of one token's write.
+template <typename T>
 struct TokenLds {
-  const float *v, *k;        // [D] the token, fp32
+  const T *v, *k;            // [D] the token, storage dtype
   const float *B, *P, *Re;   // B [D][R], P rotated [R][D], R_enc [D][RK]
   float* e;                  // [D] scratch: the Key remainder
   float* st;                 // [R + RK] out: stored latent, then residual (fp32 values)
 };
 
-// One token's stored values (whole wave, LDS only): the rounded latent
-// z~ = round(v.B) and the rounded residual s~ = round((k - z~.P).R_enc) as
-// fp32 into L.st.  The caller stores them with wave_token_store, after any
-// other memory work it wants issued first.
+// One token's stored values on one wave (the chunk writer), LDS only: the
+// rounded latent z~ = round(v.B) and residual s~ = round((k - z~.P).R_enc)
+// as fp32 into L.st, the CW virtual waves of each product taken in turn.
 template <typename T, int D>
-__device__ __forceinline__ void wave_token_values(const TokenLds& L, int R, int RK, int lane) {
-  f32x4 acc;
-  int g;
-  if (wave_matvec<D>(L.v, L.B, R, lane, acc, g)) {
+__device__ __forceinline__ void wave_token_values(const TokenLds<T>& L, int R, int RK, int lane) {
+  f32x4 acc, sum = {0.f, 0.f, 0.f, 0.f};
+  int g = 0;
+  bool own = false;
+  for (int w = 0; w < CW; ++w) {
+    own = part_matvec<D>(L.v, L.B, R, w, lane, acc, g);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) L.st[4 * g + q] = round_only(acc[q], static_cast<const T*>(nullptr));
+    for (int q = 0; q < 4; ++q) sum[q] += acc[q];
+  }
+  if (own) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) L.st[4 * g + q] = round_only(sum[q], static_cast<const T*>(nullptr));
   }
   wave_sync();
-  wave_key_remainder<D>(L.k, L.st, L.P, R, lane, L.e);
-  wave_sync();
-  if (wave_matvec<D>(L.e, L.Re, RK, lane, acc, g)) {
+  f32x4 kh = {0.f, 0.f, 0.f, 0.f};
+  for (int w = 0; w < CW; ++w) {
+    const f32x4 p = part_remainder<D>(L.st, L.P, R, w, lane);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) L.st[R + 4 * g + q] = round_only(acc[q], static_cast<const T*>(nullptr));
+    for (int q = 0; q < 4; ++q) kh[q] += p[q];
+  }
+  if (lane < D / 4) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) L.e[4 * lane + q] = lds_elem(L.k, 4 * lane + q) - kh[q];
+  }
+  wave_sync();
+  sum = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int w = 0; w < CW; ++w) {
+    own = part_matvec<D>(L.e, L.Re, RK, w, lane, acc, g);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sum[q] += acc[q];
+  }
+  if (own) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) L.st[R + 4 * g + q] = round_only(sum[q], static_cast<const T*>(nullptr));
   }
   wave_sync();
 }
@@ -256,10 +301,10 @@ __device__ __forceinline__ void wave_token_values(const TokenLds& L, int R, int 
 // Zpage[r * ps + slot] and s~ into Spage[slot * RK + j] (values exactly
 // representable in T).
 template <typename T, int D>
-__device__ __forceinline__ void wave_token_store(const TokenLds& L, int R, int RK, int ps, int slot, T* Krow,
+__device__ __forceinline__ void wave_token_store(const TokenLds<T>& L, int R, int RK, int ps, int slot, T* Krow,
                                                  T* Zpage, T* Spage, int lane) {
 #pragma unroll
-  for (int i = lane; i < D; i += 64) store_elem(Krow, i, L.k[i]);
+  for (int i = lane; i < D; i += 64) Krow[i] = L.k[i];
   for (int x = lane; x < R + RK; x += 64) {
     if (x < R) store_elem(Zpage, (size_t)x * ps + slot, L.st[x]);
     else store_elem(Spage, (size_t)slot * RK + (x - R), L.st[x]);

@@ -87,14 +87,16 @@ __global__ __launch_bounds__(THREADS) void write_kernel(WriteArgs a) {
   }
   __syncthreads();
 
-  const TokenLds L{my, my + D, sB, sP, sRe, my + 2 * D, my + 3 * D};
+  T* mv = reinterpret_cast<T*>(my);  // the token's v and k, storage dtype
+  T* mk = mv + D;
+  const TokenLds<T> L{mv, mk, sB, sP, sRe, my + 2 * D, my + 3 * D};
   for (int t = t0 + wave; t < t1; t += NWAVES) {
     const int slot = t - page * ps;
     const size_t src = ((size_t)(row0 + t - t0) * H + g) * D;
 #pragma unroll
     for (int i = lane; i < D; i += 64) {
-      my[i] = ld_elem(vin, src + i);
-      my[D + i] = ld_elem(kin, src + i);
+      mv[i] = vin[src + i];
+      mk[i] = kin[src + i];
     }
     wave_sync();
     wave_token_values<T, D>(L, R, RK, lane);

@@ -96,13 +96,13 @@ def append_last(g: Dev, sc) -> None:
     rda.basiskv_append(g.d, g.f, g.cache, pos, dev(kn, g.w.dtype), dev(vn, g.w.dtype))
 
 
-def route(g: Dev, q: Optional[torch.Tensor] = None):
+def route(g: Dev, q: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
     pairs = g.d.batch * g.d.n_kv_heads
     sel = torch.full((g.d.batch, g.d.n_kv_heads, g.d.top_k), -7, dtype=torch.int32, device="cuda")
     n_sel = torch.full((g.d.batch, g.d.n_kv_heads), -7, dtype=torch.int32, device="cuda")
     scores = torch.zeros((g.d.batch, g.d.n_kv_heads, g.d.max_pages_per_seq), dtype=torch.float32,
                          device="cuda")
-    rda.basiskv_route(g.d, g.f, g.cache, g.seq_lens, g.q if q is None else q, sel, n_sel, scores)
+    rda.basiskv_route(g.d, g.f, g.cache, g.seq_lens, g.q if q is None else q, sel, n_sel, scores, ws=ws)
     torch.cuda.synchronize()
     return host(sel), host(n_sel), host(scores)
 

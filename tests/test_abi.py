@@ -67,7 +67,7 @@ def _route(lib, d, **ptrs):
     args = dict(seq_lens=FAKE, q=FAKE, sel=FAKE, n_sel=FAKE, scores=FAKE)
     args.update(ptrs)
     return raw.basiskv_route(C.byref(d.c()), C.byref(f), C.byref(c), args["seq_lens"], args["q"],
-                             args["sel"], args["n_sel"], args["scores"], None, None)
+                             args["sel"], args["n_sel"], args["scores"], None, None, 0, None)
 
 
 def _decode(lib, d, ws_bytes):
@@ -102,7 +102,7 @@ def test_null_pointers_and_small_workspace(lib):
     assert _decode(lib, _dims(lib), 0) == -4
     assert _decode(lib, _dims(lib), lib.workspace_bytes(_dims(lib)) - 1) == -4
     raw = lib.basiskv._lib
-    assert raw.basiskv_route(None, None, None, None, None, None, None, None, None, None) == -1
+    assert raw.basiskv_route(None, None, None, None, None, None, None, None, None, None, 0, None) == -1
 
 
 def test_workspace_bytes(lib):

@@ -104,12 +104,28 @@ def test_appends_equal_one_chunk_write(name):
         assert np.array_equal(ca[k], cb[k]), k
 
 
+@pytest.mark.parametrize("pages_per_wg", [None, 3])
 @pytest.mark.parametrize("name", sorted(CASES))
-def test_route_matches_oracle(name):
+def test_route_matches_oracle(name, pages_per_wg, monkeypatch):
+    """One workgroup per (sequence, KV head), and clusters of workgroups
+    sharing the scoring (a few pages each, ragged last range) that meet
+    through the workspace's arrival counters: same bits either way."""
     sc = scenario(name)
     sel, n_sel, scores = oracle.route(sc.d, sc.fac, sc.cache, sc.lengths, sc.q)
     g = gc.upload(sc, cache=True)
-    gs, gn, gscores = gc.route(g)
+    single = gc.route(g)
+    if pages_per_wg is None:
+        gs, gn, gscores = single
+    else:
+        monkeypatch.setenv("BASISKV_ROUTE_PAGES_PER_WG", str(pages_per_wg))
+        gs, gn, gscores = gc.route(g, ws=g.ws)
+        gs2, gn2, gscores2 = gc.route(g, ws=g.ws)  # the counters were left at zero
+        assert np.array_equal(gs, gs2) and np.array_equal(gn, gn2)
+        assert np.array_equal(gs, single[0]) and np.array_equal(gn, single[1])
+        for b, n in enumerate(sc.lengths):
+            npg = -(-int(n) // sc.w.page_size)
+            assert np.array_equal(gscores[b, :, :npg], single[2][b, :, :npg])
+        assert not gc.host(g.ws)[:4 * g.d.batch * g.d.n_kv_heads].any()
     assert np.array_equal(gn, n_sel)
     for b, n in enumerate(sc.lengths):
         npg = -(-int(n) // sc.w.page_size)
@@ -155,13 +171,14 @@ def test_attend_standalone_and_split_partials(name):
     rtol, atol = gc.tol(w)
     np.testing.assert_allclose(gc.host(z).astype(np.float64), z_ref, rtol=rtol, atol=atol)
 
-    g.ws.fill_(0xFF)  # NaN everywhere the kernel does not write
-    rda.basiskv_attend(d, g.cache, g.seq_lens, g.q, sel_t, nsel_t, g.ws, None)
+    ws = torch.full_like(g.ws, 0xFF)  # NaN everywhere the kernel does not write
+    rda.basiskv_attend(d, g.cache, g.seq_lens, g.q, sel_t, nsel_t, ws, None)
     torch.cuda.synchronize()
     ns, pairs, G, R = rda.attend_splits(d), d.batch * d.n_kv_heads, w.group, w.rank_v
-    raw = gc.host(g.ws).view(np.float32)
-    acc = raw[:pairs * ns * G * R].reshape(pairs, ns, G, R).astype(np.float64)
-    ml_at = (pairs * ns * G * R * 4 + 255) // 256 * 256 // 4
+    acc_at = (pairs * 4 + 255) // 256 * 256 // 4  # after the router's arrival counters
+    raw = gc.host(ws).view(np.float32)
+    acc = raw[acc_at:acc_at + pairs * ns * G * R].reshape(pairs, ns, G, R).astype(np.float64)
+    ml_at = acc_at + (pairs * ns * G * R * 4 + 255) // 256 * 256 // 4
     ml = raw[ml_at:ml_at + pairs * ns * G * 2].reshape(pairs, ns, G, 2).astype(np.float64)
     m, l = ml[..., 0], ml[..., 1]
     M = m.max(axis=1, keepdims=True)
@@ -331,9 +348,15 @@ def test_prefill_matches_oracle(name, chunks):
     compare_written(sc, gc.cache_host(g), ora)
 
 
+@pytest.mark.parametrize("pages_per_wg", [None, 5])
 @pytest.mark.parametrize("name", ["g4_d128_p64", "g8_2kv_r48_p32", "ragged_permuted", "tiny_f32"])
-def test_fused_append_route_equals_separate_calls(name):
+def test_fused_append_route_equals_separate_calls(name, pages_per_wg, monkeypatch):
+    """The decode step (append and route fused, workgroup clusters when
+    pages_per_wg is set) against append, route in one workgroup per
+    (sequence, KV head), decode: bit-identical."""
     import routed_decode_attention_amd as rda
+    if pages_per_wg is not None:
+        monkeypatch.setenv("BASISKV_ROUTE_PAGES_PER_WG", str(pages_per_wg))
     sc = scenario(name)
     outs = []
     for fused in (False, True):
