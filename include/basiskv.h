@@ -167,9 +167,10 @@ int basiskv_append(const basiskv_dims *dims, const basiskv_factors *f,
  *   sel_phys (nullable) [batch][n_kv_heads][top_k] int32: page_table entries of
  *          sel (-1 padded), which basiskv_attend/decode may take to skip the
  *          page-table lookup.
- * ws (nullable): a workspace (basiskv_workspace_bytes) whose arrival counters
- * let several workgroups share the scoring of one (sequence, KV head); NULL
- * scores each (sequence, KV head) in one workgroup.  Results are identical.
+ * ws (nullable): a workspace of basiskv_workspace_bytes(dims, 0) bytes or
+ * more, whose arrival counters let several workgroups share the scoring of
+ * one (sequence, KV head); NULL scores each (sequence, KV head) in one
+ * workgroup.  Results are identical.
  */
 int basiskv_route(const basiskv_dims *dims, const basiskv_factors *f,
                   const basiskv_cache *cache, const int32_t *seq_lens, const void *q,
@@ -190,7 +191,7 @@ int basiskv_append_route(const basiskv_dims *dims, const basiskv_factors *f,
 /*
  * Device workspace, in bytes, that basiskv_attend/decode/decode_step (batch
  * rows) and basiskv_prefill (up to max_prefill_tokens queries) need.  Host function.
- * Its first 256 * ceil(batch * n_kv_heads / 64) bytes are the router's
+ * Its first 256 * ceil(12 * batch * n_kv_heads / 256) bytes are the router's
  * arrival counters: zero them once before the first call
  * (basiskv_workspace_init does), and every call leaves them zero.  The rest
  * carries the attention splits' partial results and intermediate latents
@@ -214,8 +215,8 @@ int basiskv_workspace_init(const basiskv_dims *dims, void *ws, size_t ws_bytes, 
  * The selection of each (sequence, KV head) is processed in splits whose
  * partial results are combined afterwards (flash-decoding style).  z_out may
  * be NULL: the combination is then left to the caller and the partials stay
- * in ws right after the arrival counters (at byte 256 * ceil(batch *
- * n_kv_heads / 64)), fp32 [batch*n_kv_heads][n_split][group][rank_v] partial
+ * in ws right after the arrival counters (at byte 256 * ceil(12 * batch *
+ * n_kv_heads / 256)), fp32 [batch*n_kv_heads][n_split][group][rank_v] partial
  * sums sum_t 2^(s_t*log2(e) - m) z~_t, followed (at the next 256-byte
  * boundary) by [batch*n_kv_heads][n_split][group][2] pairs (m, sum_t
  * 2^(s_t*log2(e) - m)) with m the split's max of s_t*log2(e) (-inf for an

@@ -188,7 +188,7 @@ template <int D, int PS, int R, bool PIPE>
 __global__ __launch_bounds__(64 * ATTEND_WAVES_MAX) void attend_mfma_kernel(AttendArgs a) {
   constexpr int KS = D / 32, MT = R / 16;
   __shared__ WaveState st;
-  extern __shared__ float s_acc[];
+  extern __shared__ __attribute__((aligned(16))) float s_acc[];
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int pair = wg / a.n_wsplit, split = wg % a.n_wsplit;
@@ -282,9 +282,9 @@ __global__ __launch_bounds__(64 * ATTEND_WAVES_MAX) void attend_mfma_kernel(Atte
 template <typename T>
 __global__ __launch_bounds__(64 * ATTEND_WAVES_MAX) void attend_valu_kernel(AttendArgs a) {
   __shared__ WaveState st;
-  extern __shared__ float s_acc[];
-  __shared__ float s_q[MAX_GROUP][128];
-  __shared__ float s_p[ATTEND_WAVES_MAX][64];
+  extern __shared__ __attribute__((aligned(16))) float s_acc[];
+  __shared__ __attribute__((aligned(16))) float s_q[MAX_GROUP][128];
+  __shared__ __attribute__((aligned(16))) float s_p[ATTEND_WAVES_MAX][64];
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int pair = wg / a.n_wsplit, split = wg % a.n_wsplit;

@@ -79,25 +79,27 @@ int check_dims(const basiskv_dims* d, bkv::Shape* s) {
 }
 
 struct WsLayout {
-  size_t arrive, part_acc, part_ml, z, sel_phys, total;
+  size_t arrive, part_acc, part_ml, z, sel_phys, route_keys, route_pages, total;
 };
 
 // Workspace: the router's arrival counters (kept zero between calls), then
 // split-K partials (latent sums, then max/denominator pairs), latent rows,
-// then the router's physical page ids.
+// the router's physical page ids, then the router's partial selection.
 WsLayout ws_layout(const bkv::Shape& s, int max_prefill_tokens) {
   const size_t pairs = (size_t)s.batch * s.n_kv_heads;
   const bkv::AttendPlan p = bkv::plan_attend(s);
   const size_t splits = pairs * p.n_wsplit * s.group;
   WsLayout L;
   L.arrive = 0;
-  L.part_acc = align256(pairs * sizeof(uint32_t));
+  L.part_acc = align256(pairs * (sizeof(uint64_t) + sizeof(uint32_t)));
   L.part_ml = L.part_acc + align256(splits * s.rank_v * sizeof(float));
   L.z = L.part_ml + align256(splits * 2 * sizeof(float));
   size_t rows = (size_t)s.batch;
   if (max_prefill_tokens > 0 && (size_t)max_prefill_tokens > rows) rows = max_prefill_tokens;
   L.sel_phys = L.z + align256(rows * s.n_q_heads * s.rank_v * sizeof(float));
-  L.total = L.sel_phys + align256(pairs * s.top_k * sizeof(int32_t));
+  L.route_keys = L.sel_phys + align256(pairs * s.top_k * sizeof(int32_t));
+  L.route_pages = L.route_keys + align256(pairs * s.top_k * sizeof(uint32_t));
+  L.total = L.route_pages + align256(pairs * s.top_k * sizeof(int32_t));
   return L;
 }
 
@@ -202,7 +204,7 @@ int do_write(const bkv::Shape& s, const basiskv_factors* f, const basiskv_cache*
 
 int do_route(const bkv::Shape& s, const basiskv_factors* f, const basiskv_cache* cache, const int32_t* pos,
              const void* k_new, const void* v_new, const int32_t* seq_lens, const void* q, int32_t* sel,
-             int32_t* n_sel, float* scores, void* stream, int32_t* sel_phys, uint32_t* arrive) {
+             int32_t* n_sel, float* scores, void* stream, int32_t* sel_phys, void* ws) {
   if (!bkv::route_fits(s, pos != nullptr))
     return fail(BASISKV_E_UNSUPPORTED, "route: page table of %d pages with these factor sizes exceeds the LDS",
                 s.max_pages);
@@ -226,19 +228,28 @@ int do_route(const bkv::Shape& s, const basiskv_factors* f, const basiskv_cache*
   a.n_sel = n_sel;
   a.sel_phys = sel_phys;
   a.scores = scores;
-  a.arrive = arrive;
+  a.meet = nullptr;
+  a.arrive = nullptr;
+  a.part_keys = nullptr;
+  a.part_pages = nullptr;
+  if (ws) {
+    const WsLayout L = ws_layout(s, 0);
+    char* w = static_cast<char*>(ws);
+    a.meet = reinterpret_cast<unsigned long long*>(w + L.arrive);
+    a.arrive = reinterpret_cast<uint32_t*>(w + L.arrive + (size_t)s.batch * s.n_kv_heads * sizeof(uint64_t));
+    a.part_keys = reinterpret_cast<uint32_t*>(w + L.route_keys);
+    a.part_pages = reinterpret_cast<int32_t*>(w + L.route_pages);
+  }
   const hipError_t e = bkv::launch_route(a, as_stream(stream));
   return e == hipSuccess ? BASISKV_OK : hip_fail(e, "route launch");
 }
 
-// The router's arrival counters in an optional workspace (nullptr: none).
-int route_counters(const bkv::Shape& s, void* ws, size_t ws_bytes, uint32_t** arrive) {
-  *arrive = nullptr;
+// An optional workspace for the router: large enough for a decode step.
+int route_workspace(const bkv::Shape& s, void* ws, size_t ws_bytes) {
   if (!ws) return BASISKV_OK;
   const WsLayout L = ws_layout(s, 0);
-  if (ws_bytes < L.part_acc)
-    return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, the router needs %zu", ws_bytes, L.part_acc);
-  *arrive = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + L.arrive);
+  if (ws_bytes < L.total)
+    return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, the router needs %zu", ws_bytes, L.total);
   return BASISKV_OK;
 }
 
@@ -312,10 +323,8 @@ int basiskv_route(const basiskv_dims* dims, const basiskv_factors* f, const basi
   if ((rc = check_cache(cache, false, false, false))) return rc;
   if (!seq_lens || !q || !sel || !n_sel || !scores)
     return fail(BASISKV_E_NULL, "route: seq_lens, q, sel, n_sel and scores are required");
-  uint32_t* arrive;
-  if ((rc = route_counters(s, ws, ws_bytes, &arrive))) return rc;
-  return do_route(s, f, cache, nullptr, nullptr, nullptr, seq_lens, q, sel, n_sel, scores, stream, sel_phys,
-                  arrive);
+  if ((rc = route_workspace(s, ws, ws_bytes))) return rc;
+  return do_route(s, f, cache, nullptr, nullptr, nullptr, seq_lens, q, sel, n_sel, scores, stream, sel_phys, ws);
 }
 
 int basiskv_append_route(const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
@@ -330,9 +339,8 @@ int basiskv_append_route(const basiskv_dims* dims, const basiskv_factors* f, con
   if ((rc = check_cache(cache, true, true, true))) return rc;
   if (!pos || !k_new || !v_new || !seq_lens || !q || !sel || !n_sel || !scores)
     return fail(BASISKV_E_NULL, "append_route: pos, k_new, v_new, seq_lens, q, sel, n_sel, scores required");
-  uint32_t* arrive;
-  if ((rc = route_counters(s, ws, ws_bytes, &arrive))) return rc;
-  return do_route(s, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, stream, sel_phys, arrive);
+  if ((rc = route_workspace(s, ws, ws_bytes))) return rc;
+  return do_route(s, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, stream, sel_phys, ws);
 }
 
 size_t basiskv_workspace_bytes(const basiskv_dims* dims, int32_t max_prefill_tokens) {
@@ -414,8 +422,7 @@ int basiskv_decode_step(const basiskv_dims* dims, const basiskv_factors* f, cons
   if (ws_bytes < L.total)
     return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, decode needs %zu", ws_bytes, L.total);
   int32_t* sel_phys = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.sel_phys);
-  uint32_t* arrive = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + L.arrive);
-  if ((rc = do_route(s, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, stream, sel_phys, arrive)))
+  if ((rc = do_route(s, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, stream, sel_phys, ws)))
     return rc;
   return attend_project(s, f, cache, seq_lens, q, sel, n_sel, sel_phys, ws, ws_bytes, z_out, out, stream);
 }

@@ -121,15 +121,17 @@ __device__ __forceinline__ int wave_sum_i(int x) {
   return x;
 }
 
-// Inclusive prefix sum across the 64 lanes of a wave.
+// Inclusive prefix sum across the 64 lanes of a wave: shifts within each
+// 16-lane row on the DPP path, then the rows' totals added from scalar reads.
 __device__ __forceinline__ int wave_incl_scan(int x) {
   const int lane = threadIdx.x & (WAVE - 1);
-#pragma unroll
-  for (int o = 1; o < WAVE; o <<= 1) {
-    int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  return x;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47);
+  return x + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
 }
 
 // Order-preserving map of fp32 onto uint32 (larger float -> larger key);

@@ -44,12 +44,16 @@ struct RouteArgs {
   int32_t *sel, *n_sel;
   int32_t* sel_phys;          // optional [batch][n_kv_heads][top_k]: physical ids of sel
   float* scores;
-  uint32_t* arrive;           // [batch][n_kv_heads] zeroed arrival counters; nullptr: one workgroup per pair
+  unsigned long long* meet;   // [batch][n_kv_heads] zeroed words where the appending and selecting workgroups meet
+  uint32_t* arrive;           // [batch][n_kv_heads] zeroed arrival counters of the scorers; nullptr: one
+                              //   workgroup per pair
+  uint32_t* part_keys;        // [batch][n_kv_heads][top_k] a cluster's selection without the appended page
+  int32_t* part_pages;        //   (keys and pages), handed to whichever finishes the selection
 };
 
 // Workgroups per (sequence, KV head) of the router: one for the append (when
-// fused) plus enough to give each about `pages_per_wg` pages to score; 1
-// without arrival counters.
+// fused) plus enough to give each scoring one at most 512 pages; 1 without
+// arrival counters or for at most 128 pages.
 int route_cluster(const Shape& s, bool append, bool counters);
 
 struct AttendArgs {
@@ -112,6 +116,11 @@ bool prefill_mfma_supported(const Shape& s);
 hipError_t launch_fold(const Shape& s, const float* B, const void* W_O, void* W_ofT, hipStream_t st);
 hipError_t launch_write(const WriteArgs& a, hipStream_t st);
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+// the router's kernels by storage dtype and fusion with the append
+hipError_t launch_route_f32(const RouteArgs& a, hipStream_t st);
+hipError_t launch_route_f32_append(const RouteArgs& a, hipStream_t st);
+hipError_t launch_route_bf16(const RouteArgs& a, hipStream_t st);
+hipError_t launch_route_bf16_append(const RouteArgs& a, hipStream_t st);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
 hipError_t launch_project(const ProjectArgs& a, hipStream_t st);

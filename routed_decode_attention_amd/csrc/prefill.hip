@@ -180,9 +180,9 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
 // over keys for q.k, lanes over latent channels for the weighted sum.
 template <typename T>
 __global__ __launch_bounds__(256) void prefill_valu_kernel(PrefillArgs a) {
-  __shared__ float s_q[128];
-  __shared__ float s_red[256];
-  __shared__ float s_p[256];
+  __shared__ __attribute__((aligned(16))) float s_q[128];
+  __shared__ __attribute__((aligned(16))) float s_red[256];
+  __shared__ __attribute__((aligned(16))) float s_p[256];
   const int qi = blockIdx.x, h = blockIdx.y;
   const int G = a.s.group, H = a.s.n_kv_heads, D = a.s.head_dim, R = a.s.rank_v;
   const int PS = a.s.page_size;

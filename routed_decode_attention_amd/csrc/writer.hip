@@ -38,7 +38,7 @@ size_t writer_lds_bytes(const Shape& s) {
 
 template <typename T, int D>
 __global__ __launch_bounds__(THREADS) void write_kernel(WriteArgs a) {
-  extern __shared__ float lds[];
+  extern __shared__ __attribute__((aligned(16))) float lds[];
   const int H = a.s.n_kv_heads, R = a.s.rank_v, RK = a.s.rank_k, RR = R + RK;
   const int ps = a.s.page_size;
   const int g = blockIdx.y;

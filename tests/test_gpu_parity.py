@@ -125,7 +125,7 @@ def test_route_matches_oracle(name, pages_per_wg, monkeypatch):
         for b, n in enumerate(sc.lengths):
             npg = -(-int(n) // sc.w.page_size)
             assert np.array_equal(gscores[b, :, :npg], single[2][b, :, :npg])
-        assert not gc.host(g.ws)[:4 * g.d.batch * g.d.n_kv_heads].any()
+        assert not gc.host(g.ws)[:12 * g.d.batch * g.d.n_kv_heads].any()  # counters back at zero
     assert np.array_equal(gn, n_sel)
     for b, n in enumerate(sc.lengths):
         npg = -(-int(n) // sc.w.page_size)
@@ -175,7 +175,7 @@ def test_attend_standalone_and_split_partials(name):
     rda.basiskv_attend(d, g.cache, g.seq_lens, g.q, sel_t, nsel_t, ws, None)
     torch.cuda.synchronize()
     ns, pairs, G, R = rda.attend_splits(d), d.batch * d.n_kv_heads, w.group, w.rank_v
-    acc_at = (pairs * 4 + 255) // 256 * 256 // 4  # after the router's arrival counters
+    acc_at = (12 * pairs + 255) // 256 * 256 // 4  # after the router's arrival counters
     raw = gc.host(ws).view(np.float32)
     acc = raw[acc_at:acc_at + pairs * ns * G * R].reshape(pairs, ns, G, R).astype(np.float64)
     ml_at = acc_at + (pairs * ns * G * R * 4 + 255) // 256 * 256 // 4
@@ -348,12 +348,14 @@ def test_prefill_matches_oracle(name, chunks):
     compare_written(sc, gc.cache_host(g), ora)
 
 
-@pytest.mark.parametrize("pages_per_wg", [None, 5])
+@pytest.mark.parametrize("pages_per_wg", [None, 5, 8192])
 @pytest.mark.parametrize("name", ["g4_d128_p64", "g8_2kv_r48_p32", "ragged_permuted", "tiny_f32"])
 def test_fused_append_route_equals_separate_calls(name, pages_per_wg, monkeypatch):
-    """The decode step (append and route fused, workgroup clusters when
-    pages_per_wg is set) against append, route in one workgroup per
-    (sequence, KV head), decode: bit-identical."""
+    """The decode step (append and route fused; with pages_per_wg set, a
+    cluster of the appending workgroup and scorers of that many pages each,
+    their partial selection completed with the appended page) against
+    append, route in one workgroup per (sequence, KV head), decode:
+    bit-identical."""
     import routed_decode_attention_amd as rda
     if pages_per_wg is not None:
         monkeypatch.setenv("BASISKV_ROUTE_PAGES_PER_WG", str(pages_per_wg))
