@@ -270,9 +270,12 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
       }
   };
   auto score = [&](float (&best)[PPL]) { score_group<NG, PPL>(sv, s_qc, G, part, best); };
+  // (in a cluster the scores are read back by another workgroup: stored
+  // coherently at device scope)
   auto finish = [&](int j, float best) {
     const float sc = best / (float)min(ps, n - j * ps);
-    a.scores[(size_t)pair * maxp + j] = sc;
+    if (C > 1) __hip_atomic_store(a.scores + (size_t)pair * maxp + j, sc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else a.scores[(size_t)pair * maxp + j] = sc;
     s_keys[j] = float_key(sc);
   };
 
@@ -491,13 +494,18 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
   };
   auto agent_load = [](const auto* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
 
+  // Data handed between the cluster's workgroups is stored with device-scope
+  // atomic stores; once complete (vmcnt) they are visible to device-scope
+  // loads anywhere, so the counters need no release/acquire (which would
+  // write back and invalidate the L2).
   // whole workgroup: arrive at a counter, true for the n-th arrival (which
-  // resets it); the workgroup's earlier stores are visible to that one
+  // resets it); the workgroup's earlier device-scope stores are visible to it
   __shared__ int s_flag;
   auto last_of = [&](uint32_t* cnt, uint32_t n) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores are complete
     __syncthreads();
     if (tid == 0) {
-      const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_flag = old == n - 1;
       if (s_flag) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -705,10 +713,11 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
   // finishes the selection
   __shared__ unsigned long long s_met;
   auto meet = [&](unsigned long long mine) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores are complete
     __syncthreads();
     if (tid == 0) {
       const unsigned long long old =
-          __hip_atomic_fetch_or(a.meet + pair, mine, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_or(a.meet + pair, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (old) __hip_atomic_store(a.meet + pair, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_met = old;
     }
@@ -732,8 +741,8 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
   const bool keep_local = top_k <= 1024;
   auto emit = [&](int p, int j) {
     if (split) {
-      ppages[p] = j;
-      pkeys[p] = s_keys[j];
+      __hip_atomic_store(ppages + p, j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(pkeys + p, s_keys[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (keep_local) {
         s_Sp[p] = j;
         s_Sk[p] = s_keys[j];

@@ -189,6 +189,17 @@ def test_attend_standalone_and_split_partials(name):
     zp = zp.reshape(d.batch, d.n_kv_heads * G, R)
     np.testing.assert_allclose(zp, z_ref, rtol=rtol, atol=atol)
 
+    # merged into z: everything but the counters NaN beforehand, so a
+    # partial read before it was stored shows
+    ws.fill_(0xFF)
+    ws[:acc_at * 4].zero_()
+    for _ in range(2):
+        z2 = torch.full((d.batch, d.n_q_heads, d.rank_v), float("nan"), device="cuda")
+        rda.basiskv_attend(d, g.cache, g.seq_lens, g.q, sel_t, nsel_t, ws, z2)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(gc.host(z2).astype(np.float64), z_ref, rtol=rtol, atol=atol)
+        assert not gc.host(ws)[:acc_at * 4].any()  # counters back at zero
+
 
 @pytest.mark.parametrize("name", ["g4_d128_p64", "ragged_permuted", "g8_2kv_r48_p32"])
 def test_route_physical_ids(name):
