@@ -175,9 +175,25 @@ int attend_project(const bkv::Shape& s, const basiskv_factors* f, const basiskv_
                    const int32_t* sel_phys, void* ws, size_t ws_bytes, float* z_out, float* out, void* stream) {
   const WsLayout L = ws_layout(s, 0);
   float* z = z_out ? z_out : reinterpret_cast<float*>(static_cast<char*>(ws) + L.z);
-  const int rc = do_attend(s, cache, seq_lens, q, sel, n_sel, ws, ws_bytes, z, stream, sel_phys, true);
+  const bool fused = bkv::plan_attend(s).n_wsplit > 1 && bkv::merge_project_supported(s);
+  // fused: the splits' partials stay in the workspace for the merge-projection
+  const int rc = do_attend(s, cache, seq_lens, q, sel, n_sel, ws, ws_bytes, z, stream, sel_phys, !fused);
   if (rc) return rc;
-  return do_project(s, f, z, s.batch, out, stream);
+  if (!fused) return do_project(s, f, z, s.batch, out, stream);
+  char* w = static_cast<char*>(ws);
+  bkv::MergeProjectArgs m;
+  m.s = s;
+  m.part_acc = reinterpret_cast<const float*>(w + L.part_acc);
+  m.part_ml = reinterpret_cast<const float*>(w + L.part_ml);
+  m.n_wsplit = bkv::plan_attend(s).n_wsplit;
+  m.W = f->W_ofT;
+  m.out = out;
+  m.z_out = z_out;
+  m.rows = s.batch;
+  m.kdim = s.n_q_heads * s.rank_v;
+  m.n = s.d_model;
+  const hipError_t e = bkv::launch_merge_project(m, as_stream(stream));
+  return e == hipSuccess ? BASISKV_OK : hip_fail(e, "merge-projection launch");
 }
 
 int do_write(const bkv::Shape& s, const basiskv_factors* f, const basiskv_cache* c, const int32_t* pos,

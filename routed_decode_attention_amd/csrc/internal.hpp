@@ -78,6 +78,17 @@ struct MergeArgs {
   float* z_out;             // [batch][n_q_heads][rank_v]
 };
 
+// The split merge of AttendArgs' partials fused with the projection (decode).
+struct MergeProjectArgs {
+  Shape s;
+  const float *part_acc, *part_ml;
+  int n_wsplit;
+  const void* W;            // W_ofT [n][kdim] bf16
+  float* out;               // [rows][n]
+  float* z_out;             // optional [rows][kdim]: the merged latents
+  int rows, kdim, n;
+};
+
 struct ProjectArgs {
   const float* z;           // [rows][kdim] fp32
   const void* W;            // [n][kdim] dtype
@@ -123,6 +134,8 @@ hipError_t launch_route_bf16(const RouteArgs& a, hipStream_t st);
 hipError_t launch_route_bf16_append(const RouteArgs& a, hipStream_t st);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
+bool merge_project_supported(const Shape& s);
+hipError_t launch_merge_project(const MergeProjectArgs& a, hipStream_t st);
 hipError_t launch_project(const ProjectArgs& a, hipStream_t st);
 hipError_t launch_prefill_attend(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_zero_u32(unsigned* p, size_t n, hipStream_t st);
