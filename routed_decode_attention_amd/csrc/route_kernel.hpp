@@ -92,7 +92,71 @@ __device__ __forceinline__ uint32_t wave_uadd(uint32_t x) {
   r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
   return r[0] + r[1];
 }
+
+// The value lane (lane ^ J) holds, J in {1, 2, 4, 8, 16, 32}: DPP within a
+// 16-lane row, gfx950's lane-half swaps across rows.
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x, int lane) {
+  if constexpr (J == 1) {
+    return BKV_DPPU(x, 0xB1);
+  } else if constexpr (J == 2) {
+    return BKV_DPPU(x, 0x4E);
+  } else if constexpr (J == 4) {
+    const uint32_t up = BKV_DPPU(x, 0x104), dn = BKV_DPPU(x, 0x114);  // row_shl:4 (lane + 4), row_shr:4
+    return (lane & 4) ? dn : up;
+  } else if constexpr (J == 8) {
+    return BKV_DPPU(x, 0x128);  // row_ror:8
+  } else if constexpr (J == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? r[0] : r[1];
+  }
+}
 #undef BKV_DPPU
+
+// Bitonic sorting network over the 64 lanes of a wave on 64-bit values held
+// as (hi, lo): one compare-exchange with lane ^ J inside blocks of K lanes;
+// a whole sort (descending unless `up`), and the final merge of a bitonic
+// sequence.
+template <int J>
+__device__ __forceinline__ void bitonic_step(uint32_t& hi, uint32_t& lo, int lane, int K, bool up) {
+  const bool lower = (lane & J) == 0, first = (lane & K) == 0;
+  const bool keep_max = (lower == first) != up;
+  const uint32_t ph = lane_xor<J>(hi, lane), pl = lane_xor<J>(lo, lane);
+  const bool p_gt = ph > hi || (ph == hi && pl > lo);
+  if (keep_max == p_gt) {
+    hi = ph;
+    lo = pl;
+  }
+}
+__device__ __forceinline__ void bitonic_merge(uint32_t& hi, uint32_t& lo, int lane, bool up) {
+  bitonic_step<32>(hi, lo, lane, 64, up);
+  bitonic_step<16>(hi, lo, lane, 64, up);
+  bitonic_step<8>(hi, lo, lane, 64, up);
+  bitonic_step<4>(hi, lo, lane, 64, up);
+  bitonic_step<2>(hi, lo, lane, 64, up);
+  bitonic_step<1>(hi, lo, lane, 64, up);
+}
+__device__ __forceinline__ void bitonic_sort(uint32_t& hi, uint32_t& lo, int lane, bool up) {
+  bitonic_step<1>(hi, lo, lane, 2, up);
+  bitonic_step<2>(hi, lo, lane, 4, up);
+  bitonic_step<1>(hi, lo, lane, 4, up);
+  bitonic_step<4>(hi, lo, lane, 8, up);
+  bitonic_step<2>(hi, lo, lane, 8, up);
+  bitonic_step<1>(hi, lo, lane, 8, up);
+  bitonic_step<8>(hi, lo, lane, 16, up);
+  bitonic_step<4>(hi, lo, lane, 16, up);
+  bitonic_step<2>(hi, lo, lane, 16, up);
+  bitonic_step<1>(hi, lo, lane, 16, up);
+  bitonic_step<16>(hi, lo, lane, 32, up);
+  bitonic_step<8>(hi, lo, lane, 32, up);
+  bitonic_step<4>(hi, lo, lane, 32, up);
+  bitonic_step<2>(hi, lo, lane, 32, up);
+  bitonic_step<1>(hi, lo, lane, 32, up);
+  bitonic_merge(hi, lo, lane, up);
+}
 
 
 // best[i] = max over the group's heads h of qc[h] . sums(page i), each dot
@@ -724,9 +788,84 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
     __syncthreads();
     return s_met;
   };
+  // ---- small selections (at most 512 pages, 2 <= top_k <= 64): a sorting
+  // network.  Every wave sorts 64 keys as 64-bit values (key, ~page) —
+  // larger key first, then smaller page, the selection's own order — then
+  // three merge levels through LDS leave the top 64 in wave 0, which sorts
+  // the selected pages into page order.  The appended page is merged in by
+  // wave 0 alone: with top_k candidates already, the worst of them (kept
+  // from the key order) and the appended page compete. ----
+  const bool fast = npg <= 512 && top_k >= 2 && top_k <= 64;
+  uint32_t f_page = 0xffffffffu, f_whi = 0u, f_wlo = 0u;  // wave 0: the p-th page; the worst (hi, lo)
+  auto select_fast = [&](int ks) {
+    const int j = 64 * wave + lane;
+    uint32_t hi = 0u, lo = 0u;
+    if (j < npg && j != excl) {
+      hi = s_keys[j];
+      lo = ~(uint32_t)j;
+    }
+    bitonic_sort(hi, lo, lane, false);
+    uint32_t* xs = reinterpret_cast<uint32_t*>(s_work);  // [NW][64][2]
+#pragma unroll
+    for (int lv = 1; lv < NW; lv <<= 1) {
+      if (wave % (2 * lv) == lv) {
+        xs[(wave * 64 + lane) * 2] = hi;
+        xs[(wave * 64 + lane) * 2 + 1] = lo;
+      }
+      __syncthreads();
+      if (wave % (2 * lv) == 0) {
+        const int at = ((wave + lv) * 64 + 63 - lane) * 2;
+        const uint32_t bh = xs[at], bl = xs[at + 1];
+        if (bh > hi || (bh == hi && bl > lo)) {
+          hi = bh;
+          lo = bl;
+        }
+        bitonic_merge(hi, lo, lane, false);
+      }
+    }
+    if (wave == 0 && ks > 0) {
+      f_whi = __builtin_amdgcn_readlane(hi, ks - 1);
+      f_wlo = __builtin_amdgcn_readlane(lo, ks - 1);
+      uint32_t ph = lane < ks ? ~lo : 0xffffffffu, pl = 0u;
+      bitonic_sort(ph, pl, lane, true);
+      f_page = ph;
+    }
+  };
+  // wave 0: the final selection from the partial one (page f_page in lanes
+  // p < nS, worst (whi, wlo)) and the appended page with key ka
+  auto merge_fast = [&](uint32_t ka) {
+    const int k = min(top_k, npg);
+    const int nS = min(top_k, npg - (excl >= 0 ? 1 : 0));
+    if (lane == 0) a.n_sel[pair] = k;
+    for (int p = k + lane; p < top_k; p += 64) {
+      sel[p] = -1;
+      if (selp) selp[p] = -1;
+    }
+    const int jp = (int)f_page;
+    if (excl < 0 || (nS == top_k && (ka < f_whi || (ka == f_whi && ~(uint32_t)excl < f_wlo)))) {
+      if (lane < nS) put(lane, jp);  // the appended page stays out
+      return;
+    }
+    const int jw = nS == top_k ? (int)~f_wlo : -1;  // the entry it displaces
+    const bool keep = lane < nS && jp != jw;
+    if (keep) put(lane - (jw >= 0 && jp > jw ? 1 : 0) + (jp > excl ? 1 : 0), jp);
+    const int ins = __popcll(__ballot(keep && jp < excl));
+    if (lane == 0) put(ins, excl);
+  };
+
   if (split && c == 0) {  // the appending workgroup: its page's score is in
     const uint32_t ka = excl >= 0 ? s_keys[excl] : 0u;
-    if (meet((1ull << 63) | ka)) merge_appended(false, ka);
+    if (meet((1ull << 63) | ka)) {
+      if (!fast) {
+        merge_appended(false, ka);
+      } else if (wave == 0) {
+        const int nS = min(top_k, npg - (excl >= 0 ? 1 : 0));
+        f_page = lane < nS ? (uint32_t)agent_load(ppages + lane) : 0xffffffffu;
+        f_whi = agent_load(pkeys);
+        f_wlo = agent_load(pkeys + 1);
+        merge_fast(ka);
+      }
+    }
     return;
   }
   if (nsc > 1) {
@@ -738,6 +877,33 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
     __syncthreads();
   }
   const int ks = min(top_k, npg - (excl >= 0 ? 1 : 0));
+  if (fast) {
+    select_fast(ks);
+    if (!split) {
+      if (wave == 0) {
+        if (lane == 0) a.n_sel[pair] = ks;
+        for (int p = lane; p < top_k; p += 64) {
+          if (p < ks) {
+            put(p, (int)f_page);
+          } else {
+            sel[p] = -1;
+            if (selp) selp[p] = -1;
+          }
+        }
+      }
+      return;
+    }
+    if (wave == 0) {  // for the appending workgroup, should it finish
+      if (lane < ks) __hip_atomic_store(ppages + lane, (int)f_page, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) {
+        __hip_atomic_store(pkeys, f_whi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(pkeys + 1, f_wlo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    const unsigned long long met = meet(1ull << 62);
+    if (met && wave == 0) merge_fast((uint32_t)met);
+    return;
+  }
   const bool keep_local = top_k <= 1024;
   auto emit = [&](int p, int j) {
     if (split) {
