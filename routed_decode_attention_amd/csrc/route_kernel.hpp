@@ -234,7 +234,10 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
 
   const int H = a.s.n_kv_heads, G = a.s.group;
   const int C = gridDim.x / (a.s.batch * H);  // workgroups per (sequence, KV head)
-  const int pair = blockIdx.x / C, c = blockIdx.x - pair * C;
+  // a pair's workgroups on one XCD, the one the attention kernel gives the
+  // pair's splits, so the selection it reads back is in that XCD's L2
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int pair = L / C, c = L - pair * C;
   const int R = a.s.rank_v, RK = a.s.rank_k, RR = R + RK, ps = a.s.page_size;
   const int maxp = a.s.max_pages;
   const int b = pair / H, g = pair % H;
