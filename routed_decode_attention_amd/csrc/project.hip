@@ -91,27 +91,34 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void project_mfma_kernel(Pr
 }
 
 // Decode: the attention splits' merge and the projection in one launch.  A
-// workgroup of MP_WAVES waves owns 16 batch rows and 16 * MP_WAVES output
-// columns: it requests its weight fragments for the whole contraction first,
-// then merges the splits of its rows into LDS (one 4-channel task per
-// thread; the partials are small and read by every column group), then each
-// wave multiplies its 16 x 16 tile as project_mfma_kernel does.
+// workgroup of MP_WAVES waves owns MP_ROWS batch rows and 32 * MP_WAVES
+// output columns: it requests its weight fragments for the whole
+// contraction first, then merges the splits of its rows into LDS (one
+// 4-channel task per thread), then each wave multiplies two 16 x 16 tiles as
+// project_mfma_kernel does, its A operand padded to 16 rows with zeros.  Few
+// rows per workgroup keep the partials each one reads small (they are re-read
+// by every column group); the weights are re-read by every row group from L2.
 constexpr int MP_WAVES = 8;
-constexpr int MP_KMAX = 512;  // contraction length held in registers and LDS
+constexpr int MP_ROWS = 4;
+constexpr int MP_COLS = 32 * MP_WAVES;
+constexpr int MP_KMAX = 256;  // contraction length held in registers and LDS
 
 __global__ __launch_bounds__(64 * MP_WAVES) void merge_project_kernel(MergeProjectArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float zs[];  // [16][kdim]
+  extern __shared__ __attribute__((aligned(16))) float zs[];  // [16][kdim], rows past MP_ROWS zero
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, qd = lane >> 4;
   const int G = a.s.group, R = a.s.rank_v, H = a.s.n_kv_heads, kdim = a.kdim;
-  const int row0 = blockIdx.y * 16;
-  const int col = blockIdx.x * 16 * MP_WAVES + wave * 16 + n;
+  const int row0 = blockIdx.y * MP_ROWS;
+  const int col = blockIdx.x * MP_COLS + wave * 32 + n;  // and col + 16
   const uint16_t* W = static_cast<const uint16_t*>(a.W);
 
-  bf16x8 bfr[MP_KMAX / 32];
+  bf16x8 bfr[MP_KMAX / 32][2];
 #pragma unroll
   for (int kb = 0; kb < MP_KMAX / 32; ++kb)
-    if (32 * kb < kdim) bfr[kb] = load_bf16x8(W + (size_t)col * kdim + 32 * kb + 8 * qd);
+    if (32 * kb < kdim) {
+      bfr[kb][0] = load_bf16x8(W + (size_t)col * kdim + 32 * kb + 8 * qd);
+      bfr[kb][1] = load_bf16x8(W + (size_t)(col + 16) * kdim + 32 * kb + 8 * qd);
+    }
 
   // z rows: z[b][hq * R + r] is head h = hq % G of pair (b, hq / G)
   const int quads = kdim / 4;
@@ -119,7 +126,7 @@ __global__ __launch_bounds__(64 * MP_WAVES) void merge_project_kernel(MergeProje
     const int row = t / quads, k = 4 * (t % quads);
     const int b = row0 + row, hq = k / R, r0 = k % R;
     f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    if (b < a.rows) {
+    if (row < MP_ROWS && b < a.rows) {
       const size_t pair = (size_t)b * H + hq / G;
       z = merge_splits4(a.part_acc + pair * a.n_wsplit * G * R, a.part_ml + pair * a.n_wsplit * G * 2,
                         a.n_wsplit, G, R, hq % G, r0);
@@ -129,7 +136,7 @@ __global__ __launch_bounds__(64 * MP_WAVES) void merge_project_kernel(MergeProje
   }
   __syncthreads();
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
   for (int kb = 0; kb < MP_KMAX / 32; ++kb) {
     if (32 * kb >= kdim) break;
@@ -138,13 +145,22 @@ __global__ __launch_bounds__(64 * MP_WAVES) void merge_project_kernel(MergeProje
     const float x[8] = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
     bf16x8 af, al;
     split_bf16x8(x, af, al);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[kb], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bfr[kb], acc, 0, 0, 0);
-  }
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int row = row0 + 4 * qd + e;
-    if (row < a.rows) a.out[(size_t)row * a.n + col] = acc[e];
+    for (int j = 0; j < 2; ++j) {
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[kb][j], acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bfr[kb][j], acc[j], 0, 0, 0);
+    }
+  }
+  // tile rows 4 qd + e; only the first MP_ROWS are real
+  if (4 * qd < MP_ROWS) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = row0 + 4 * qd + e;
+      if (4 * qd + e < MP_ROWS && row < a.rows) {
+        a.out[(size_t)row * a.n + col] = acc[0][e];
+        a.out[(size_t)row * a.n + col + 16] = acc[1][e];
+      }
+    }
   }
 }
 
@@ -164,12 +180,12 @@ __global__ __launch_bounds__(256) void project_valu_kernel(ProjectArgs a) {
 
 bool merge_project_supported(const Shape& s) {
   const int kdim = s.n_q_heads * s.rank_v;
-  return s.dtype == 1 && kdim % 32 == 0 && kdim <= MP_KMAX && s.d_model % (16 * MP_WAVES) == 0;
+  return s.dtype == 1 && kdim % 32 == 0 && kdim <= MP_KMAX && s.d_model % MP_COLS == 0;
 }
 
 hipError_t launch_merge_project(const MergeProjectArgs& a, hipStream_t st) {
   if (a.rows <= 0) return hipSuccess;
-  const dim3 grid(a.n / (16 * MP_WAVES), (a.rows + 15) / 16);
+  const dim3 grid(a.n / MP_COLS, (a.rows + MP_ROWS - 1) / MP_ROWS);
   hipLaunchKernelGGL(merge_project_kernel, grid, dim3(64 * MP_WAVES), (size_t)16 * a.kdim * sizeof(float), st, a);
   return hipGetLastError();
 }
