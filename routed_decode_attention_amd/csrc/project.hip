@@ -99,7 +99,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void project_mfma_kernel(Pr
 // rows per workgroup keep the partials each one reads small (they are re-read
 // by every column group); the weights are re-read by every row group from L2.
 constexpr int MP_WAVES = 8;
-constexpr int MP_ROWS = 4;
+constexpr int MP_ROWS = 2;
 constexpr int MP_COLS = 32 * MP_WAVES;
 constexpr int MP_KMAX = 256;  // contraction length held in registers and LDS
 
