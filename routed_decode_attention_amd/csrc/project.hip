@@ -91,16 +91,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void project_mfma_kernel(Pr
 }
 
 // Decode: the attention splits' merge and the projection in one launch.  A
-// workgroup of MP_WAVES waves owns MP_ROWS batch rows and 32 * MP_WAVES
-// output columns: it requests its weight fragments for the whole
+// workgroup of MP_WAVES waves owns MP_ROWS batch rows and 16 * MP_WN *
+// MP_WAVES output columns: it requests its weight fragments for the whole
 // contraction first, then merges the splits of its rows into LDS (one
-// 4-channel task per thread), then each wave multiplies two 16 x 16 tiles as
-// project_mfma_kernel does, its A operand padded to 16 rows with zeros.  Few
-// rows per workgroup keep the partials each one reads small (they are re-read
-// by every column group); the weights are re-read by every row group from L2.
+// 4-channel task per thread), then each wave multiplies its 16 x 16 tiles as
+// project_mfma_kernel does, the A operand padded to 16 rows with zeros.  The
+// partials are re-read by every column group and the weights by every row
+// group (from L2); small tiles keep both per workgroup small.
 constexpr int MP_WAVES = 8;
 constexpr int MP_ROWS = 2;
-constexpr int MP_COLS = 32 * MP_WAVES;
+constexpr int MP_WN = 1;  // 16-column tiles per wave
+constexpr int MP_COLS = 16 * MP_WN * MP_WAVES;
 constexpr int MP_KMAX = 256;  // contraction length held in registers and LDS
 
 __global__ __launch_bounds__(64 * MP_WAVES) void merge_project_kernel(MergeProjectArgs a) {
@@ -109,15 +110,15 @@ __global__ __launch_bounds__(64 * MP_WAVES) void merge_project_kernel(MergeProje
   const int n = lane & 15, qd = lane >> 4;
   const int G = a.s.group, R = a.s.rank_v, H = a.s.n_kv_heads, kdim = a.kdim;
   const int row0 = blockIdx.y * MP_ROWS;
-  const int col = blockIdx.x * MP_COLS + wave * 32 + n;  // and col + 16
+  const int col = blockIdx.x * MP_COLS + wave * 16 * MP_WN + n;  // and col + 16 j
   const uint16_t* W = static_cast<const uint16_t*>(a.W);
 
-  bf16x8 bfr[MP_KMAX / 32][2];
+  bf16x8 bfr[MP_KMAX / 32][MP_WN];
 #pragma unroll
   for (int kb = 0; kb < MP_KMAX / 32; ++kb)
     if (32 * kb < kdim) {
-      bfr[kb][0] = load_bf16x8(W + (size_t)col * kdim + 32 * kb + 8 * qd);
-      bfr[kb][1] = load_bf16x8(W + (size_t)(col + 16) * kdim + 32 * kb + 8 * qd);
+#pragma unroll
+      for (int j = 0; j < MP_WN; ++j) bfr[kb][j] = load_bf16x8(W + (size_t)(col + 16 * j) * kdim + 32 * kb + 8 * qd);
     }
 
   // z rows: z[b][hq * R + r] is head h = hq % G of pair (b, hq / G)
@@ -136,7 +137,9 @@ __global__ __launch_bounds__(64 * MP_WAVES) void merge_project_kernel(MergeProje
   }
   __syncthreads();
 
-  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  f32x4 acc[MP_WN];
+#pragma unroll
+  for (int j = 0; j < MP_WN; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < MP_KMAX / 32; ++kb) {
     if (32 * kb >= kdim) break;
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(64 * MP_WAVES) void merge_project_kernel(MergeProje
     bf16x8 af, al;
     split_bf16x8(x, af, al);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < MP_WN; ++j) {
       acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[kb][j], acc[j], 0, 0, 0);
       acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bfr[kb][j], acc[j], 0, 0, 0);
     }
@@ -157,8 +160,8 @@ __global__ __launch_bounds__(64 * MP_WAVES) void merge_project_kernel(MergeProje
     for (int e = 0; e < 4; ++e) {
       const int row = row0 + 4 * qd + e;
       if (4 * qd + e < MP_ROWS && row < a.rows) {
-        a.out[(size_t)row * a.n + col] = acc[0][e];
-        a.out[(size_t)row * a.n + col + 16] = acc[1][e];
+#pragma unroll
+        for (int j = 0; j < MP_WN; ++j) a.out[(size_t)row * a.n + col + 16 * j] = acc[j][e];
       }
     }
   }
