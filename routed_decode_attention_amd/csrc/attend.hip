@@ -159,8 +159,7 @@ struct OnlineSoftmax {
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sv[c][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = pair_max<32>(pair_max<16>(mx));
     const float m_new = fmaxf(m, mx);
     if (m_new == NEG_INF) return;  // wave-uniform: no valid token so far
     const float alpha = exp2f(m - m_new);
@@ -262,8 +261,7 @@ __global__ __launch_bounds__(64 * ATTEND_WAVES_MAX) void attend_mfma_kernel(Atte
 
   // this wave's state into LDS: head n lives in lanes n, n+16, n+32, n+48
   float l = os.l;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = pair_sum<32>(pair_sum<16>(l));
   if (n < G) {
     if (qd == 0) {
       st.m[wave][n] = os.m;

@@ -105,6 +105,24 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Max / sum of x over lanes l and l ^ 16 (16: rows of 16 lanes) or l ^ 32
+// (32: wave halves), with gfx950's lane-half swaps instead of LDS permutes;
+// both lanes of a pair get the same bits.
+template <int M>
+__device__ __forceinline__ float pair_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = M == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                         : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <int M>
+__device__ __forceinline__ float pair_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = M == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                         : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));

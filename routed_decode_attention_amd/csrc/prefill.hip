@@ -138,8 +138,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sv[c][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = pair_max<32>(pair_max<16>(mx));
     const float m_new = fmaxf(m_run, mx);
     // rows with nothing valid yet keep a zero state (their p below is 0)
     const float alpha = m_new == NEG_INF ? 1.f : exp2f(m_run - m_new);
@@ -164,8 +163,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
     if (pg + 1 < n_pages) cur = nxt;
   }
 
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = pair_sum<32>(pair_sum<16>(l_run));
   if (row_ok) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     float* zo = a.z_out + ((size_t)qi * a.s.n_q_heads + g * G + hh) * R;
