@@ -61,7 +61,8 @@ __device__ __forceinline__ float quad_sum(float x) {
 }
 
 // Wave-wide max / min of a 32-bit key (every lane gets the result).
-#define BKV_DPPU(x, ctrl) (uint32_t) __builtin_amdgcn_update_dpp(0, (int)(x), ctrl, 0xF, 0xF, false)
+// (lanes without a source, e.g. past a row end for row_shl, read 0)
+#define BKV_DPPU(x, ctrl) (uint32_t) __builtin_amdgcn_mov_dpp((int)(x), ctrl, 0xF, 0xF, true)
 __device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
   x = max(x, BKV_DPPU(x, 0xB1));
   x = max(x, BKV_DPPU(x, 0x4E));
@@ -116,46 +117,46 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t x, int lane) {
 }
 #undef BKV_DPPU
 
-// Bitonic sorting network over the 64 lanes of a wave on 64-bit values held
-// as (hi, lo): one compare-exchange with lane ^ J inside blocks of K lanes;
-// a whole sort (descending unless `up`), and the final merge of a bitonic
-// sequence.
+// the same for a 64-bit value, one half at a time
 template <int J>
-__device__ __forceinline__ void bitonic_step(uint32_t& hi, uint32_t& lo, int lane, int K, bool up) {
-  const bool lower = (lane & J) == 0, first = (lane & K) == 0;
-  const bool keep_max = (lower == first) != up;
-  const uint32_t ph = lane_xor<J>(hi, lane), pl = lane_xor<J>(lo, lane);
-  const bool p_gt = ph > hi || (ph == hi && pl > lo);
-  if (keep_max == p_gt) {
-    hi = ph;
-    lo = pl;
-  }
+__device__ __forceinline__ uint64_t lane_xor64(uint64_t x, int lane) {
+  return (uint64_t)lane_xor<J>((uint32_t)(x >> 32), lane) << 32 | lane_xor<J>((uint32_t)x, lane);
 }
-__device__ __forceinline__ void bitonic_merge(uint32_t& hi, uint32_t& lo, int lane, bool up) {
-  bitonic_step<32>(hi, lo, lane, 64, up);
-  bitonic_step<16>(hi, lo, lane, 64, up);
-  bitonic_step<8>(hi, lo, lane, 64, up);
-  bitonic_step<4>(hi, lo, lane, 64, up);
-  bitonic_step<2>(hi, lo, lane, 64, up);
-  bitonic_step<1>(hi, lo, lane, 64, up);
+
+// Bitonic sorting network over the 64 lanes of a wave on 64-bit values: one
+// compare-exchange with lane ^ J inside blocks of K lanes; a whole sort
+// (descending unless `up`), and the final merge of a bitonic sequence.
+template <int J>
+__device__ __forceinline__ void bitonic_step(uint64_t& x, int lane, int K, bool up) {
+  const bool keep_max = (((lane & J) == 0) == ((lane & K) == 0)) != up;
+  const uint64_t p = lane_xor64<J>(x, lane);
+  if (keep_max == (p > x)) x = p;
 }
-__device__ __forceinline__ void bitonic_sort(uint32_t& hi, uint32_t& lo, int lane, bool up) {
-  bitonic_step<1>(hi, lo, lane, 2, up);
-  bitonic_step<2>(hi, lo, lane, 4, up);
-  bitonic_step<1>(hi, lo, lane, 4, up);
-  bitonic_step<4>(hi, lo, lane, 8, up);
-  bitonic_step<2>(hi, lo, lane, 8, up);
-  bitonic_step<1>(hi, lo, lane, 8, up);
-  bitonic_step<8>(hi, lo, lane, 16, up);
-  bitonic_step<4>(hi, lo, lane, 16, up);
-  bitonic_step<2>(hi, lo, lane, 16, up);
-  bitonic_step<1>(hi, lo, lane, 16, up);
-  bitonic_step<16>(hi, lo, lane, 32, up);
-  bitonic_step<8>(hi, lo, lane, 32, up);
-  bitonic_step<4>(hi, lo, lane, 32, up);
-  bitonic_step<2>(hi, lo, lane, 32, up);
-  bitonic_step<1>(hi, lo, lane, 32, up);
-  bitonic_merge(hi, lo, lane, up);
+__device__ __forceinline__ void bitonic_merge(uint64_t& x, int lane, bool up) {
+  bitonic_step<32>(x, lane, 64, up);
+  bitonic_step<16>(x, lane, 64, up);
+  bitonic_step<8>(x, lane, 64, up);
+  bitonic_step<4>(x, lane, 64, up);
+  bitonic_step<2>(x, lane, 64, up);
+  bitonic_step<1>(x, lane, 64, up);
+}
+__device__ __forceinline__ void bitonic_sort(uint64_t& x, int lane, bool up) {
+  bitonic_step<1>(x, lane, 2, up);
+  bitonic_step<2>(x, lane, 4, up);
+  bitonic_step<1>(x, lane, 4, up);
+  bitonic_step<4>(x, lane, 8, up);
+  bitonic_step<2>(x, lane, 8, up);
+  bitonic_step<1>(x, lane, 8, up);
+  bitonic_step<8>(x, lane, 16, up);
+  bitonic_step<4>(x, lane, 16, up);
+  bitonic_step<2>(x, lane, 16, up);
+  bitonic_step<1>(x, lane, 16, up);
+  bitonic_step<16>(x, lane, 32, up);
+  bitonic_step<8>(x, lane, 32, up);
+  bitonic_step<4>(x, lane, 32, up);
+  bitonic_step<2>(x, lane, 32, up);
+  bitonic_step<1>(x, lane, 32, up);
+  bitonic_merge(x, lane, up);
 }
 
 
@@ -794,49 +795,51 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
   // ---- small selections (at most 512 pages, 2 <= top_k <= 64): a sorting
   // network.  Every wave sorts 64 keys as 64-bit values (key, ~page) —
   // larger key first, then smaller page, the selection's own order — then
-  // three merge levels through LDS leave the top 64 in wave 0, which sorts
-  // the selected pages into page order.  The appended page is merged in by
-  // wave 0 alone: with top_k candidates already, the worst of them (kept
-  // from the key order) and the appended page compete. ----
+  // three merge levels through LDS leave the top 64 in wave 0, one per lane;
+  // each lane counts the selected pages below its own for its position in
+  // page order.  The appended page is merged in by wave 0 alone: with top_k
+  // candidates already, the worst of them (kept from the key order) and the
+  // appended page compete. ----
   const bool fast = npg <= 512 && top_k >= 2 && top_k <= 64;
-  uint32_t f_page = 0xffffffffu, f_whi = 0u, f_wlo = 0u;  // wave 0: the p-th page; the worst (hi, lo)
+  __shared__ __attribute__((aligned(16))) uint32_t s_fpage[64];
+  // wave 0: a selected page, its position in page order, the worst (hi, lo)
+  uint32_t f_page = 0xffffffffu, f_rank = 0u, f_whi = 0u, f_wlo = 0u;
   auto select_fast = [&](int ks) {
     const int j = 64 * wave + lane;
-    uint32_t hi = 0u, lo = 0u;
-    if (j < npg && j != excl) {
-      hi = s_keys[j];
-      lo = ~(uint32_t)j;
-    }
-    bitonic_sort(hi, lo, lane, false);
-    uint32_t* xs = reinterpret_cast<uint32_t*>(s_work);  // [NW][64][2]
+    uint64_t x = 0u;
+    if (j < npg && j != excl) x = (uint64_t)s_keys[j] << 32 | ~(uint32_t)j;
+    bitonic_sort(x, lane, false);
+    uint64_t* xs = reinterpret_cast<uint64_t*>(s_work);  // [NW][64]
 #pragma unroll
     for (int lv = 1; lv < NW; lv <<= 1) {
-      if (wave % (2 * lv) == lv) {
-        xs[(wave * 64 + lane) * 2] = hi;
-        xs[(wave * 64 + lane) * 2 + 1] = lo;
-      }
+      if (wave % (2 * lv) == lv) xs[wave * 64 + lane] = x;
       __syncthreads();
       if (wave % (2 * lv) == 0) {
-        const int at = ((wave + lv) * 64 + 63 - lane) * 2;
-        const uint32_t bh = xs[at], bl = xs[at + 1];
-        if (bh > hi || (bh == hi && bl > lo)) {
-          hi = bh;
-          lo = bl;
-        }
-        bitonic_merge(hi, lo, lane, false);
+        x = max(x, xs[(wave + lv) * 64 + 63 - lane]);
+        bitonic_merge(x, lane, false);
       }
     }
     if (wave == 0 && ks > 0) {
-      f_whi = __builtin_amdgcn_readlane(hi, ks - 1);
-      f_wlo = __builtin_amdgcn_readlane(lo, ks - 1);
-      uint32_t ph = lane < ks ? ~lo : 0xffffffffu, pl = 0u;
-      bitonic_sort(ph, pl, lane, true);
-      f_page = ph;
+      f_whi = __builtin_amdgcn_readlane((uint32_t)(x >> 32), ks - 1);
+      f_wlo = __builtin_amdgcn_readlane((uint32_t)x, ks - 1);
+      f_page = lane < ks ? ~(uint32_t)x : 0xffffffffu;
+      s_fpage[lane] = f_page;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const uint4* fp = reinterpret_cast<const uint4*>(s_fpage);
+      uint32_t r = 0u;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const uint4 q = fp[m];
+        r += (q.x < f_page) + (q.y < f_page) + (q.z < f_page) + (q.w < f_page);
+      }
+      f_rank = r;
     }
   };
-  // wave 0: the final selection from the partial one (page f_page in lanes
-  // p < nS, worst (whi, wlo)) and the appended page with key ka
-  auto merge_fast = [&](uint32_t ka) {
+  // wave 0: the final selection from the partial one (lane p < nS holds page
+  // jp at position rank, worst (whi, wlo)) and the appended page with key ka
+  auto merge_fast = [&](uint32_t ka, int jp, int rank) {
     const int k = min(top_k, npg);
     const int nS = min(top_k, npg - (excl >= 0 ? 1 : 0));
     if (lane == 0) a.n_sel[pair] = k;
@@ -844,14 +847,13 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
       sel[p] = -1;
       if (selp) selp[p] = -1;
     }
-    const int jp = (int)f_page;
     if (excl < 0 || (nS == top_k && (ka < f_whi || (ka == f_whi && ~(uint32_t)excl < f_wlo)))) {
-      if (lane < nS) put(lane, jp);  // the appended page stays out
+      if (lane < nS) put(rank, jp);  // the appended page stays out
       return;
     }
     const int jw = nS == top_k ? (int)~f_wlo : -1;  // the entry it displaces
     const bool keep = lane < nS && jp != jw;
-    if (keep) put(lane - (jw >= 0 && jp > jw ? 1 : 0) + (jp > excl ? 1 : 0), jp);
+    if (keep) put(rank - (jw >= 0 && jp > jw ? 1 : 0) + (jp > excl ? 1 : 0), jp);
     const int ins = __popcll(__ballot(keep && jp < excl));
     if (lane == 0) put(ins, excl);
   };
@@ -863,10 +865,10 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
         merge_appended(false, ka);
       } else if (wave == 0) {
         const int nS = min(top_k, npg - (excl >= 0 ? 1 : 0));
-        f_page = lane < nS ? (uint32_t)agent_load(ppages + lane) : 0xffffffffu;
+        const int jp = lane < nS ? agent_load(ppages + lane) : -1;
         f_whi = agent_load(pkeys);
         f_wlo = agent_load(pkeys + 1);
-        merge_fast(ka);
+        merge_fast(ka, jp, lane);
       }
     }
     return;
@@ -885,26 +887,23 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
     if (!split) {
       if (wave == 0) {
         if (lane == 0) a.n_sel[pair] = ks;
-        for (int p = lane; p < top_k; p += 64) {
-          if (p < ks) {
-            put(p, (int)f_page);
-          } else {
-            sel[p] = -1;
-            if (selp) selp[p] = -1;
-          }
+        if (lane < ks) put((int)f_rank, (int)f_page);
+        for (int p = ks + lane; p < top_k; p += 64) {
+          sel[p] = -1;
+          if (selp) selp[p] = -1;
         }
       }
       return;
     }
     if (wave == 0) {  // for the appending workgroup, should it finish
-      if (lane < ks) __hip_atomic_store(ppages + lane, (int)f_page, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane < ks) __hip_atomic_store(ppages + f_rank, (int)f_page, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (lane == 0) {
         __hip_atomic_store(pkeys, f_whi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(pkeys + 1, f_wlo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     const unsigned long long met = meet(1ull << 62);
-    if (met && wave == 0) merge_fast((uint32_t)met);
+    if (met && wave == 0) merge_fast((uint32_t)met, (int)f_page, (int)f_rank);
     return;
   }
   const bool keep_local = top_k <= 1024;
