@@ -895,15 +895,27 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
       }
       return;
     }
-    if (wave == 0) {  // for the appending workgroup, should it finish
+    if (wave != 0) return;
+    // wave 0 alone: should the appending workgroup have come and gone (its
+    // bit is in the word), finish here without handing the partial
+    // selection over; else hand it over and meet
+    unsigned long long met = __hip_atomic_load(a.meet + pair, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!(met >> 63)) {
       if (lane < ks) __hip_atomic_store(ppages + f_rank, (int)f_page, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (lane == 0) {
         __hip_atomic_store(pkeys, f_whi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(pkeys + 1, f_wlo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the hand-over is complete
+      unsigned long long old = 0ull;
+      if (lane == 0) old = __hip_atomic_fetch_or(a.meet + pair, 1ull << 62, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      met = (unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((int)(old >> 32)) << 32 |
+            (uint32_t)__builtin_amdgcn_readfirstlane((int)old);
     }
-    const unsigned long long met = meet(1ull << 62);
-    if (met && wave == 0) merge_fast((uint32_t)met, (int)f_page, (int)f_rank);
+    if (met) {
+      if (lane == 0) __hip_atomic_store(a.meet + pair, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      merge_fast((uint32_t)met, (int)f_page, (int)f_rank);
+    }
     return;
   }
   const bool keep_local = top_k <= 1024;
