@@ -541,7 +541,7 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
       finish(j, best);
     }
   }
-  __syncthreads();
+  lds_barrier();  // the keys are in LDS; the score stores stay in flight
 
   // ---- selection ----
   const int top_k = a.s.top_k;
@@ -687,7 +687,7 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
         s_red[wave][0] = kmax;
         s_red[wave][1] = kmin;
       }
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         kmax = max(kmax, s_red[w][0]);
@@ -708,7 +708,7 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
           const uint32_t key = s_keys[j];
           if (j != excl && (key & mask) == prefix) atomicAdd(hb + wave * 256 + ((key >> shift) & dmask), 1);
         }
-        __syncthreads();
+        lds_barrier();
         // lane owns digits 255-4*lane .. 252-4*lane (descending)
         int cd[4] = {0, 0, 0, 0};
 #pragma unroll
@@ -748,7 +748,7 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
     // take_eq)
     int gt_seen = 0, eq_seen = 0;
     for (int base0 = 0; base0 < nk; base0 += RT) {
-      if (base0 > 0) __syncthreads();  // the previous round's counts are read
+      if (base0 > 0) lds_barrier();  // the previous round's counts are read
       const int j = base0 + tid;
       const bool in = j < nk && j != excl;
       const uint32_t mk = in ? (s_keys[j] & mask) : 0u;
@@ -759,7 +759,7 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
         s_wcnt[wave][0] = __popcll(gtm);
         s_wcnt[wave][1] = __popcll(eqm);
       }
-      __syncthreads();
+      lds_barrier();
       int gt_before = gt_seen + __popcll(gtm & below), eq_before = eq_seen + __popcll(eqm & below);
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
@@ -813,7 +813,7 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
 #pragma unroll
     for (int lv = 1; lv < NW; lv <<= 1) {
       if (wave % (2 * lv) == lv) xs[wave * 64 + lane] = x;
-      __syncthreads();
+      lds_barrier();
       if (wave % (2 * lv) == 0) {
         x = max(x, xs[(wave + lv) * 64 + 63 - lane]);
         bitonic_merge(x, lane, false);
