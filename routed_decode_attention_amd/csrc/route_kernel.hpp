@@ -355,26 +355,6 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
   T* img = reinterpret_cast<T*>(base + lay.img);
   PageImage pg;
   if (app0 && wave == 0) pg.load(Zp, Sp, (int)(R * ps * sizeof(T) / 16), (int)(ps * RK * sizeof(T) / 16), lane);
-  // every wave requests a group (unused on the appending wave), which keeps
-  // the registers of the two kinds of request apart
-  if (in_regs) load_group(0);
-
-  // the new token's three products, each split over the NW waves (wave w
-  // takes the w-th eighth of the contraction); the partials meet in LDS and
-  // are added in wave order, the chunk writer's order for the same split
-  const T* vn = reinterpret_cast<const T*>(base + lay.vk);
-  const T* kn = vn + D;
-  const float* sB = reinterpret_cast<const float*>(base + lay.B);
-  const float* sRe = reinterpret_cast<const float*>(base + lay.Re);
-  float* s_lr = s_work;            // [NW][64] latent, later residual partials
-  float* s_kp = s_work + NW * 64;  // [NW][128] Key-estimate partials
-  if (app0) {
-    f32x4 acc;
-    int gq;
-    if (part_matvec<D>(vn, sB, R, wave, lane, acc, gq))
-      *reinterpret_cast<f32x4*>(s_lr + wave * 64 + 4 * gq) = acc;
-  }
-
   // ---- the query seen through the latent predictor P and the residual
   // decoder R_dec: one task per (output row x, quarter c) for every head,
   // lane c taking 16-byte pieces 4u + c of the row; a quad sums the
@@ -407,8 +387,33 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
     if (RR < VMAX)
       for (int t = t0; t < G * (VMAX - RR); t += stride) s_qc[t / (VMAX - RR)][RR + t % (VMAX - RR)] = 0.f;
   };
+  // The waves holding query-projection tasks project first and request
+  // their pages after (their requests would otherwise wait in the CU's
+  // address queue behind everyone's, holding the projection back).
   const bool late_qproj = app0 && C > 1;
-  if (!late_qproj) qproj(tid, RT);
+  const int QT = (RR * 4 + 63) & ~63;  // threads with a projection task
+  const bool q_first = !late_qproj && tid < QT;
+  if (q_first) qproj(tid, QT);
+  // every wave requests a group (unused on the appending wave), which keeps
+  // the registers of the two kinds of request apart
+  if (in_regs) load_group(0);
+
+  // the new token's three products, each split over the NW waves (wave w
+  // takes the w-th eighth of the contraction); the partials meet in LDS and
+  // are added in wave order, the chunk writer's order for the same split
+  const T* vn = reinterpret_cast<const T*>(base + lay.vk);
+  const T* kn = vn + D;
+  const float* sB = reinterpret_cast<const float*>(base + lay.B);
+  const float* sRe = reinterpret_cast<const float*>(base + lay.Re);
+  float* s_lr = s_work;            // [NW][64] latent, later residual partials
+  float* s_kp = s_work + NW * 64;  // [NW][128] Key-estimate partials
+  if (app0) {
+    f32x4 acc;
+    int gq;
+    if (part_matvec<D>(vn, sB, R, wave, lane, acc, gq))
+      *reinterpret_cast<f32x4*>(s_lr + wave * 64 + 4 * gq) = acc;
+  }
+
   lds_barrier();  // the scoring loads stay in flight
 
   if (app0) {
