@@ -157,15 +157,21 @@ def main():
     for _ in range(2):
         graph.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # an event after every sweep (events do not synchronise): the whole run
+    # gives the rate, the sweeps its spread
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(sweeps + 1)]
     t_wall = time.time()
-    e0.record()
-    for _ in range(sweeps):
+    evs[0].record()
+    for k in range(sweeps):
         graph.replay()
-    e1.record()
+        evs[k + 1].record()
     torch.cuda.synchronize()
     t_wall = time.time() - t_wall
-    ms = e0.elapsed_time(e1)
+    ms = evs[0].elapsed_time(evs[-1])
+    sweep_us = np.array([evs[k].elapsed_time(evs[k + 1]) * 1e3 / L for k in range(sweeps)])
+    sweep_stats = {"sweeps": sweeps, "median_us_per_step": round(float(np.median(sweep_us)), 3),
+                   "p10_us_per_step": round(float(np.percentile(sweep_us, 10)), 3),
+                   "p90_us_per_step": round(float(np.percentile(sweep_us, 90)), 3)}
     ms_per_step = ms / steps
     tokens_per_s = B * steps / (ms / 1e3)
     log(f"{steps} steps in {ms:.2f} ms (wall {t_wall * 1e3:.1f} ms): {ms_per_step * 1e3:.2f} us/step, "
@@ -210,6 +216,16 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "kernel": "attend_mfma_kernel<128,64,32>", "bytes_per_launch": attend_bytes,
                 "avg_launch_us": round(att_us, 3), "launches": n_launch}
+    # achievable read bandwidth: one pass over 2 GiB (8x the Infinity Cache)
+    probe = torch.zeros(2 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(2048, dtype=torch.float32, device="cuda")
+    t_read = time_launches(lambda i: rda.basiskv_stream_read(probe, sink), 10)
+    achievable = probe.numel() / (t_read * 1e-6) / 1e9
+    del probe
+    roofline["achievable_read_GBs"] = round(achievable, 1)
+    roofline["frac_of_achievable"] = round(achieved / achievable, 4)
+    log(f"achievable HBM read (stream probe, 2 GiB): {achievable:.0f} GB/s; the attention kernel reaches "
+        f"{100 * achieved / achievable:.1f}% of it")
     step_tbs = sb.total / (ms_per_step * 1e-3) / 1e12
     log(f"attend {att_us:.2f} us ({achieved:.0f} GB/s, {100 * achieved / HBM_PEAK_GBS:.1f}% of 8 TB/s); "
         f"append+route {t_route:.2f} us, merge+project {t_project:.2f} us")
@@ -274,7 +290,9 @@ def main():
                    "global_batch": B, "seq_len": int(w.ctx), "parallelism": "single GPU",
                    "layers_rotated": L, "graph_captured": True},
         "hbm_step": {"algorithmic_bytes": sb.total, "TB_per_s": round(step_tbs, 3),
-                     "frac_of_8TBs": round(step_tbs / 8.0, 4)},
+                     "frac_of_8TBs": round(step_tbs / 8.0, 4),
+                     "frac_of_achievable": round(step_tbs * 1e3 / achievable, 4)},
+        "sweep_spread": sweep_stats,
         "kernels_us": {"append_route": round(float(t_route), 3),
                        "attend": round(att_us, 3), "merge_project": round(float(t_project), 3)},
         "roofline": roofline,

@@ -274,6 +274,18 @@ int basiskv_prefill(const basiskv_dims *dims, const basiskv_factors *f,
                     const void *q, const void *k, const void *v, void *ws, size_t ws_bytes,
                     float *z_out, float *out, void *stream);
 
+/*
+ * Measurement aid beside the method: reads `bytes` bytes of src (16-byte
+ * aligned device memory; bytes a multiple of 4) once, with 16-byte loads
+ * spread over n_sink >= 1 workgroups of 256 threads, and writes each
+ * workgroup's fp32 sum of the words read as floats to sink[0 .. n_sink)
+ * (sink: device, caller-owned).  Timing it over a buffer well beyond the
+ * 256 MB Infinity Cache gives the achievable HBM read bandwidth that the
+ * attention kernel's rate is compared with.  Errors: E_NULL (src or sink
+ * NULL), E_DIMS (bytes not a multiple of 4, n_sink < 1, src misaligned).
+ */
+int basiskv_stream_read(const void *src, size_t bytes, float *sink, int32_t n_sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

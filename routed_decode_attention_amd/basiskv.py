@@ -29,7 +29,7 @@ EXPORTS = (
     "basiskv_write", "basiskv_append", "basiskv_route", "basiskv_append_route",
     "basiskv_workspace_bytes", "basiskv_workspace_init", "basiskv_attend", "basiskv_attend_splits",
     "basiskv_project",
-    "basiskv_decode", "basiskv_decode_step", "basiskv_prefill",
+    "basiskv_decode", "basiskv_decode_step", "basiskv_prefill", "basiskv_stream_read",
 )
 
 
@@ -80,6 +80,7 @@ def _load() -> C.CDLL:
         "basiskv_project": ([D, Fp, p, i32, p, p], C.c_int),
         "basiskv_decode": ([D, Fp, Cp, p, p, p, p, p, p, sz, p, p, p], C.c_int),
         "basiskv_prefill": ([D, Fp, Cp, i32, i32, i32, p, p, p, p, sz, p, p, p], C.c_int),
+        "basiskv_stream_read": ([p, sz, p, i32, p], C.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -352,3 +353,14 @@ def basiskv_prefill(d: Dims, f: Factors, cache: Cache, seq: int, start: int, q, 
         _ptr(ws, "ws", torch.uint8), ws.numel(),
         _ptr(z_out, "z_out", torch.float32, n * d.n_q_heads * d.rank_v),
         _ptr(out, "out", torch.float32, n * d.d_model), _stream(stream)))
+
+
+def basiskv_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Read every byte of the device tensor src once (a bandwidth probe);
+    sink (fp32, one per workgroup) receives each workgroup's sum of the
+    words read as fp32."""
+    if not (src.is_cuda and src.is_contiguous()):
+        raise ValueError("src: a contiguous device tensor")
+    _check(_lib.basiskv_stream_read(C.c_void_p(src.data_ptr()), src.numel() * src.element_size(),
+                                    _ptr(sink, "sink", torch.float32, sink.numel()), sink.numel(),
+                                    _stream(stream)))

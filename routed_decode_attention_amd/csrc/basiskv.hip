@@ -443,6 +443,15 @@ int basiskv_decode_step(const basiskv_dims* dims, const basiskv_factors* f, cons
   return attend_project(s, f, cache, seq_lens, q, sel, n_sel, sel_phys, ws, ws_bytes, z_out, out, stream);
 }
 
+int basiskv_stream_read(const void* src, size_t bytes, float* sink, int32_t n_sink, void* stream) {
+  if (!src || !sink) return fail(BASISKV_E_NULL, "stream_read: src and sink are required");
+  if (bytes % 4 != 0 || n_sink < 1 || (reinterpret_cast<uintptr_t>(src) & 15) != 0)
+    return fail(BASISKV_E_DIMS, "stream_read: bytes %zu (multiple of 4), n_sink %d (>= 1), src 16-byte aligned",
+                bytes, (int)n_sink);
+  const hipError_t e = bkv::launch_stream_read(src, bytes, sink, n_sink, as_stream(stream));
+  return e == hipSuccess ? BASISKV_OK : hip_fail(e, "stream-read launch");
+}
+
 int basiskv_prefill(const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
                     int32_t seq, int32_t start_pos, int32_t n_tok, const void* q, const void* k,
                     const void* v, void* ws, size_t ws_bytes, float* z_out, float* out, void* stream) {

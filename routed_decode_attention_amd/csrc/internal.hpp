@@ -139,5 +139,6 @@ hipError_t launch_merge_project(const MergeProjectArgs& a, hipStream_t st);
 hipError_t launch_project(const ProjectArgs& a, hipStream_t st);
 hipError_t launch_prefill_attend(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_zero_u32(unsigned* p, size_t n, hipStream_t st);
+hipError_t launch_stream_read(const void* src, size_t bytes, float* sink, int n_sink, hipStream_t st);
 
 }  // namespace bkv

@@ -129,3 +129,15 @@ def test_product_path_never_touches_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "liboracle" not in text, f
                 assert "ora_" not in text, f
+
+
+def test_stream_read_validates_on_the_host(lib):
+    raw = C.CDLL(LIB)
+    f = raw.basiskv_stream_read
+    f.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int32, C.c_void_p]
+    f.restype = C.c_int
+    assert f(None, 64, FAKE, 4, None) == lib.E_NULL
+    assert f(FAKE, 64, None, 4, None) == lib.E_NULL
+    assert f(FAKE, 62, FAKE, 4, None) == lib.E_DIMS           # not whole words
+    assert f(FAKE, 64, FAKE, 0, None) == lib.E_DIMS           # no workgroup
+    assert f(C.c_void_p(0x1004), 64, FAKE, 4, None) == lib.E_DIMS  # misaligned
