@@ -76,8 +76,22 @@ enum {
   BASISKV_E_UNSUPPORTED = -3, /* valid, but no kernel for this shape                  */
   BASISKV_E_WORKSPACE = -4,   /* workspace too small                                  */
   BASISKV_E_HIP = -5,         /* a HIP call or launch failed (see basiskv_last_error) */
-  BASISKV_E_DATA = -6         /* reserved: invalid device data detected               */
+  BASISKV_E_DATA = -6         /* invalid device data (debug mode only, see below)    */
 };
+
+/*
+ * Debug mode: with the environment variable BASISKV_DEBUG=1, every call that
+ * reads sequence lengths, page-table entries, append positions or a
+ * selection first checks, on the device, the values it is about to use
+ * (lengths within [0, max_pages_per_seq * page_size]; the page-table entry
+ * of every page a length, an append position or a chunk reaches within
+ * [0, num_phys_pages); selection counts within [0, top_k], selected pages
+ * below the sequence's page count and their physical ids within the pool),
+ * synchronises the stream, and returns BASISKV_E_DATA with nothing else
+ * enqueued when one is violated (basiskv_last_error says which).  Without
+ * it these values are not checked and a violation is undefined behaviour.
+ * Debug mode synchronises, so it does not suit graph capture.
+ */
 
 enum { BASISKV_F32 = 0, BASISKV_BF16 = 1 };
 

@@ -2,6 +2,7 @@
 // launches on the caller's stream.  The library keeps no device state; the
 // only global is the thread-local error text.
 #include <math.h>
+#include <stdlib.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -27,6 +28,48 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---- debug mode (environment BASISKV_DEBUG=1): before its kernels, a call
+// checks the device data it is about to read and returns BASISKV_E_DATA on a
+// violation, with nothing else enqueued.  It synchronises the stream, so it
+// is not for graph capture. ----
+__device__ unsigned g_validate_flag;
+
+bool debug_on() {
+  const char* e = getenv("BASISKV_DEBUG");
+  return e && e[0] == '1';
+}
+
+bkv::ValidateArgs validate_args(const bkv::Shape& s, const basiskv_cache* c) {
+  bkv::ValidateArgs v = {};
+  v.rows = s.batch;
+  v.max_pages = s.max_pages;
+  v.page_size = s.page_size;
+  v.num_phys = s.num_pages;
+  v.top_k = s.top_k;
+  v.n_kv_heads = s.n_kv_heads;
+  v.page_table = c->page_table;
+  return v;
+}
+
+int debug_check(bkv::ValidateArgs v, void* stream, const char* who) {
+  if (!debug_on()) return BASISKV_OK;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipGetSymbolAddress(reinterpret_cast<void**>(&v.flag), HIP_SYMBOL(g_validate_flag));
+  if (e == hipSuccess) e = bkv::launch_zero_u32(v.flag, 1, st);
+  if (e == hipSuccess) e = bkv::launch_validate(v, st);
+  unsigned bits = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&bits, v.flag, sizeof bits, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "debug check");
+  if (!bits) return BASISKV_OK;
+  return fail(BASISKV_E_DATA, "%s: invalid device data:%s%s%s%s%s", who,
+              bits & bkv::VALIDATE_SEQ_LEN ? " a sequence length out of range;" : "",
+              bits & bkv::VALIDATE_PAGE ? " a page-table entry out of range;" : "",
+              bits & bkv::VALIDATE_APPEND_PAGE ? " an append position's page unmapped;" : "",
+              bits & bkv::VALIDATE_COUNT ? " a selection count outside [0, top_k];" : "",
+              bits & bkv::VALIDATE_SELECTION ? " a selected page outside its sequence or pool;" : "");
+}
 
 // Validate dims and fill the kernels' shape.  Returns BASISKV_OK or an error.
 int check_dims(const basiskv_dims* d, bkv::Shape* s) {
@@ -315,6 +358,12 @@ int basiskv_write(const basiskv_dims* dims, const basiskv_factors* f, const basi
   if (!k || !v) return fail(BASISKV_E_NULL, "write: k and v are required");
   if ((int64_t)start + n_tok > (int64_t)s.max_pages * s.page_size)
     return fail(BASISKV_E_DIMS, "write: tokens beyond max_pages_per_seq * page_size");
+  bkv::ValidateArgs va = validate_args(s, cache);
+  va.rows = 1;
+  va.chunk_seq = seq;
+  va.chunk_first = start / s.page_size;
+  va.chunk_pages = (start + n_tok - 1) / s.page_size - va.chunk_first + 1;
+  if ((rc = debug_check(va, stream, "write"))) return rc;
   return do_write(s, f, cache, nullptr, seq, start, n_tok, k, v, stream);
 }
 
@@ -326,6 +375,9 @@ int basiskv_append(const basiskv_dims* dims, const basiskv_factors* f, const bas
   if (!f || !f->B || !f->P || !f->R_enc) return fail(BASISKV_E_NULL, "append: factors B, P, R_enc required");
   if ((rc = check_cache(cache, true, true, true))) return rc;
   if (!pos || !k_new || !v_new) return fail(BASISKV_E_NULL, "append: pos, k_new and v_new are required");
+  bkv::ValidateArgs va = validate_args(s, cache);
+  va.pos = pos;
+  if ((rc = debug_check(va, stream, "append"))) return rc;
   return do_write(s, f, cache, pos, 0, 0, 1, k_new, v_new, stream);
 }
 
@@ -340,6 +392,9 @@ int basiskv_route(const basiskv_dims* dims, const basiskv_factors* f, const basi
   if (!seq_lens || !q || !sel || !n_sel || !scores)
     return fail(BASISKV_E_NULL, "route: seq_lens, q, sel, n_sel and scores are required");
   if ((rc = route_workspace(s, ws, ws_bytes))) return rc;
+  bkv::ValidateArgs va = validate_args(s, cache);
+  va.seq_lens = seq_lens;
+  if ((rc = debug_check(va, stream, "route"))) return rc;
   return do_route(s, f, cache, nullptr, nullptr, nullptr, seq_lens, q, sel, n_sel, scores, stream, sel_phys, ws);
 }
 
@@ -356,6 +411,10 @@ int basiskv_append_route(const basiskv_dims* dims, const basiskv_factors* f, con
   if (!pos || !k_new || !v_new || !seq_lens || !q || !sel || !n_sel || !scores)
     return fail(BASISKV_E_NULL, "append_route: pos, k_new, v_new, seq_lens, q, sel, n_sel, scores required");
   if ((rc = route_workspace(s, ws, ws_bytes))) return rc;
+  bkv::ValidateArgs va = validate_args(s, cache);
+  va.seq_lens = seq_lens;
+  va.pos = pos;
+  if ((rc = debug_check(va, stream, "append_route"))) return rc;
   return do_route(s, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, stream, sel_phys, ws);
 }
 
@@ -386,6 +445,14 @@ int basiskv_attend(const basiskv_dims* dims, const basiskv_cache* cache, const i
   if ((rc = check_cache(cache, true, true, false))) return rc;
   if (!seq_lens || !q || !sel || !n_sel || !ws)
     return fail(BASISKV_E_NULL, "attend: seq_lens, q, sel, n_sel and ws are required");
+  if (ws_bytes < ws_layout(s, 0).z)
+    return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, attention needs %zu", ws_bytes, ws_layout(s, 0).z);
+  bkv::ValidateArgs va = validate_args(s, cache);
+  va.seq_lens = seq_lens;
+  va.sel = sel;
+  va.n_sel = n_sel;
+  va.sel_phys = sel_phys;
+  if ((rc = debug_check(va, stream, "attend"))) return rc;
   return do_attend(s, cache, seq_lens, q, sel, n_sel, ws, ws_bytes, z_out, stream, sel_phys, z_out != nullptr);
 }
 
@@ -419,6 +486,12 @@ int basiskv_decode(const basiskv_dims* dims, const basiskv_factors* f, const bas
   const WsLayout L = ws_layout(s, 0);
   if (ws_bytes < L.total)
     return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, decode needs %zu", ws_bytes, L.total);
+  bkv::ValidateArgs va = validate_args(s, cache);
+  va.seq_lens = seq_lens;
+  va.sel = sel;
+  va.n_sel = n_sel;
+  va.sel_phys = sel_phys;
+  if ((rc = debug_check(va, stream, "decode"))) return rc;
   return attend_project(s, f, cache, seq_lens, q, sel, n_sel, sel_phys, ws, ws_bytes, z_out, out, stream);
 }
 
@@ -438,6 +511,10 @@ int basiskv_decode_step(const basiskv_dims* dims, const basiskv_factors* f, cons
   if (ws_bytes < L.total)
     return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, decode needs %zu", ws_bytes, L.total);
   int32_t* sel_phys = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.sel_phys);
+  bkv::ValidateArgs va = validate_args(s, cache);
+  va.seq_lens = seq_lens;
+  va.pos = pos;
+  if ((rc = debug_check(va, stream, "decode_step"))) return rc;
   if ((rc = do_route(s, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, stream, sel_phys, ws)))
     return rc;
   return attend_project(s, f, cache, seq_lens, q, sel, n_sel, sel_phys, ws, ws_bytes, z_out, out, stream);
@@ -471,6 +548,12 @@ int basiskv_prefill(const basiskv_dims* dims, const basiskv_factors* f, const ba
   if (ws_bytes < L.total)
     return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, a %d-token prefill needs %zu", ws_bytes,
                 n_tok, L.total);
+  bkv::ValidateArgs va = validate_args(s, cache);
+  va.rows = 1;
+  va.chunk_seq = seq;
+  va.chunk_first = 0;  // the chunk attends to every earlier page of its row
+  va.chunk_pages = (start_pos + n_tok - 1) / s.page_size + 1;
+  if ((rc = debug_check(va, stream, "prefill"))) return rc;
   if ((rc = do_write(s, f, cache, nullptr, seq, start_pos, n_tok, k, v, stream))) return rc;
   float* z = z_out ? z_out : reinterpret_cast<float*>(static_cast<char*>(ws) + L.z);
   bkv::PrefillArgs a;

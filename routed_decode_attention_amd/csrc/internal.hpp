@@ -139,6 +139,23 @@ hipError_t launch_merge_project(const MergeProjectArgs& a, hipStream_t st);
 hipError_t launch_project(const ProjectArgs& a, hipStream_t st);
 hipError_t launch_prefill_attend(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_zero_u32(unsigned* p, size_t n, hipStream_t st);
+
+// Debug-mode check of the device data a call reads (see validate.hip).
+enum : unsigned {
+  VALIDATE_SEQ_LEN = 1,      // a sequence length outside [0, max_pages * page_size]
+  VALIDATE_PAGE = 2,         // a page-table entry a call reads outside [0, num_phys_pages)
+  VALIDATE_APPEND_PAGE = 4,  // the page-table entry of an append position
+  VALIDATE_COUNT = 8,        // a selection count outside [0, top_k]
+  VALIDATE_SELECTION = 16,   // a selected page outside the sequence, or its physical id out of range
+};
+struct ValidateArgs {
+  int rows, max_pages, page_size, num_phys, top_k, n_kv_heads;
+  const int32_t* page_table;
+  const int32_t *seq_lens, *pos, *sel, *n_sel, *sel_phys;  // each nullable
+  int chunk_seq, chunk_first, chunk_pages;                 // pages of one row (chunk_pages 0: none)
+  unsigned* flag;
+};
+hipError_t launch_validate(const ValidateArgs& v, hipStream_t st);
 hipError_t launch_stream_read(const void* src, size_t bytes, float* sink, int n_sink, hipStream_t st);
 
 }  // namespace bkv
