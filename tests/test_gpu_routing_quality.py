@@ -1,0 +1,64 @@
+"""Routing quality with factors fitted offline (PCA / least squares /
+truncated SVD of the residual) against the generator's random factors, on
+the synthetic workload whose Keys depend on the Values: the GPU router's
+selection, scored by the exact softmax mass its pages hold (recall)."""
+import numpy as np
+import pytest
+import torch
+
+from tests import cases, gpu_cases as gc
+from workloads import configs, synth
+from routed_decode_attention_amd import fit
+
+pytestmark = pytest.mark.gpu
+
+
+def _f32(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def test_fitted_factors_route_to_more_attention_mass():
+    import routed_decode_attention_amd as rda
+    w = configs.get("llama8b_32k").with_(name="fitq", cfg_id=311, batch=8, top_k=8, d_model=256)
+    n = 2048  # 32 pages per sequence, 8 selected
+    sc = cases.make_scenario(w, lengths=[n] * w.batch, write=False)
+    # calibration tokens: other sequences of the same generator
+    cal = [synth.make_sequence(w, sc.fac, 100 + i, n) for i in range(4)]
+    Kc = np.concatenate([_f32(k) for k, _ in cal])
+    Vc = np.concatenate([_f32(v) for _, v in cal])
+    fitted = fit.fit_factors(Kc, Vc, w.rank_v, w.rank_k)
+    G = w.n_q_heads // w.n_kv_heads
+    masses = [fit.page_mass(_f32(sc.K[b]), _f32(sc.q[b]), n, w.page_size, G) for b in range(w.batch)]
+    res = {}
+    for name in ("random", "fitted"):
+        g = gc.upload(sc)
+        if name == "fitted":
+            g.f = rda.Factors(B=torch.from_numpy(fitted["B"]).cuda(), P=torch.from_numpy(fitted["P"]).cuda(),
+                              R_enc=torch.from_numpy(fitted["R_enc"]).cuda(),
+                              R_dec=torch.from_numpy(fitted["R_dec"]).cuda(), W_ofT=g.f.W_ofT)
+        gc.write_all(g, sc)
+        sel, n_sel, _ = gc.route(g)
+        rec = []
+        for b in range(w.batch):
+            for h in range(w.n_kv_heads):
+                assert n_sel[b, h] == w.top_k
+                rec.append(fit.recall(masses[b][h * G:(h + 1) * G], sel[b, h]))
+        res[name] = float(np.mean(rec))
+    best = float(np.mean([fit.best_recall(masses[b][h * G:(h + 1) * G], w.top_k)
+                          for b in range(w.batch) for h in range(w.n_kv_heads)]))
+    # the same page-mean routing on the exact Keys: the ceiling of what
+    # predicted Keys can reach with this score
+    exact = []
+    for b in range(w.batch):
+        Kb, qb = _f32(sc.K[b]).astype(np.float64), _f32(sc.q[b]).astype(np.float64)
+        for h in range(w.n_kv_heads):
+            means = Kb[:, h].reshape(-1, w.page_size, w.head_dim).mean(axis=1)
+            score = (means @ qb[h * G:(h + 1) * G].T).max(axis=1)
+            top = np.argsort(-score, kind="stable")[:w.top_k]
+            exact.append(fit.recall(masses[b][h * G:(h + 1) * G], top))
+    exact = float(np.mean(exact))
+    print(f"\nrecall of {w.top_k} of {n // w.page_size} pages: random factors {res['random']:.4f}, "
+          f"fitted {res['fitted']:.4f}, page-mean routing on exact Keys {exact:.4f}, best per head "
+          f"{best:.4f}, uniform {w.top_k * w.page_size / n:.4f}")
+    assert res["fitted"] > res["random"]
+    assert res["fitted"] <= best + 1e-9
