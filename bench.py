@@ -64,6 +64,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the oracle's timed CPU work")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--kernel-launches", type=int, default=256, help="launches per kernel for per-kernel timing")
+    p.add_argument("--top-k", type=int, default=None, help="pages selected per (sequence, KV head) instead of "
+                   "the workload's (a top-k sweep; same data)")
     return p.parse_args()
 
 
@@ -81,6 +83,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = configs.get(args.workload)
+    if args.top_k is not None:
+        w = w.with_(top_k=args.top_k)
     L = args.layers
     B, H, G = w.batch, w.n_kv_heads, w.group
     t0 = time.time()
