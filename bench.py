@@ -111,6 +111,9 @@ def main():
     torch.cuda.synchronize()
     caches = [base] + [rda.Cache(K=base.K.clone(), Z=base.Z.clone(), S=base.S.clone(),
                                  summ=base.summ.clone(), page_table=page_table) for _ in range(L - 1)]
+    # every layer instance has its own factors too (W_of alone is 1 MiB a layer), as in a model
+    facs = [f] + [rda.Factors(B=f.B.clone(), P=f.P.clone(), R_enc=f.R_enc.clone(), R_dec=f.R_dec.clone(),
+                              W_ofT=f.W_ofT.clone()) for _ in range(L - 1)]
     seq_lens = torch.from_numpy(lengths.astype(np.int32)).cuda()
     pos = (seq_lens - 1).contiguous()
     k_new = gc.dev(np.stack([seqs[b][0][int(lengths[b]) - 1] for b in range(B)]), w.dtype)
@@ -127,8 +130,8 @@ def main():
         f"(K+Z) in {time.time() - t0:.1f}s")
 
     def step(i):
-        rda.basiskv_decode_step(d, f, caches[i % L], pos, k_new, v_new, seq_lens, q, sel, n_sel, scores,
-                                ws, out, z_out=z)
+        rda.basiskv_decode_step(d, facs[i % L], caches[i % L], pos, k_new, v_new, seq_lens, q, sel, n_sel,
+                                scores, ws, out, z_out=z)
 
     # the first step's selection and output, kept for the oracle comparison below
     step(0)
@@ -204,11 +207,11 @@ def main():
     # into the projection)
     t_attend = time_launches(lambda i: rda.basiskv_attend(d, caches[i % L], seq_lens, q, sel_fixed,
                                                           nsel_fixed, ws, None, sel_phys=phys_fixed), n_launch)
-    t_route = time_launches(lambda i: rda.basiskv_append_route(d, f, caches[i % L], pos, k_new, v_new,
+    t_route = time_launches(lambda i: rda.basiskv_append_route(d, facs[i % L], caches[i % L], pos, k_new, v_new,
                                                                seq_lens, q, sel, n_sel, scores,
                                                                sel_phys=sel_phys, ws=ws), n_launch)
     # attention + the merge fused into the projection, as the step runs them
-    t_decode = time_launches(lambda i: rda.basiskv_decode(d, f, caches[i % L], seq_lens, q, sel_fixed, nsel_fixed,
+    t_decode = time_launches(lambda i: rda.basiskv_decode(d, facs[i % L], caches[i % L], seq_lens, q, sel_fixed, nsel_fixed,
                                                           ws, out, sel_phys=phys_fixed), n_launch)
     t_project = t_decode - t_attend
 
