@@ -31,10 +31,13 @@
 //   3. when appending, wave 0 stores the token and rebuilds its page's sums
 //      from the page's LDS image, then scores that page; a quad of lanes
 //      scores one page from its fp32 sums held in registers;
-//   4. an MSB-first 8-bit radix select over order-preserving keys in LDS
-//      (per-wave histograms, scanned by every wave, one barrier a pass)
-//      finds the k-th score, and ballots plus per-wave counts compact the
-//      selection in page order.
+//   4. up to 512 pages and 64 selected: a sorting network on 64-bit
+//      (key, ~page) values (a wave per 64 keys, three merge levels through
+//      LDS), each selected page's slot in page order counted by its lane;
+//      larger selections: an MSB-first 8-bit radix select over
+//      order-preserving keys in LDS (per-wave histograms, scanned by every
+//      wave, one barrier a pass) finds the k-th score, and ballots plus
+//      per-wave counts compact the selection in page order.
 #pragma once
 
 #include <algorithm>
