@@ -16,8 +16,18 @@ head:
 * R_enc, R_dec: the r_k leading right singular vectors of the residual
   E = K - Z.P and their transpose, the best rank-r_k code of what is left.
 
-The joint objective across tensor-parallel partitions (fitting every GPU's
-factors together against the full attention output) is not built here.
+Fitting against the attention output instead of the Values (the pages: fit
+the factors jointly against the full attention output, the Value basis tied
+to the output projection).  A query head h's output is o_h.W_O[h] with o_h a
+convex combination of the Values, so over calibration Values X the group's
+outputs are X.W_g, W_g = [W_O[h] for the group's heads] (d_h x group*d_model).
+The rank-r map X.B.C closest to X.W_g in least squares (reduced-rank
+regression) is B = W_g.U_r, C = U_r^T with U_r the r leading right singular
+vectors of X.W_g: the latent basis B and, per head, the folded projection
+W_of[h] = C's block for h -- passed to the library as W_ofT instead of
+folding B^T.W_O (which assumes an orthonormal B).  Across several GPUs'
+partitions the same fit would run on the stacked outputs of all of them; one
+GPU's share is fitted here.
 
 Routing quality: for a query head, page j of a sequence holds the exact
 softmax mass m_j = sum over its tokens of softmax(scale * q.k)_t; a
@@ -56,6 +66,41 @@ def fit_factors(K: np.ndarray, V: np.ndarray, rank_v: int, rank_k: int) -> Dict[
         Re = _leading_right_vectors(E, rank_k)
         out["B"][g], out["P"][g], out["R_enc"][g], out["R_dec"][g] = B, P, Re, Re.T
     return out
+
+
+def fit_output_aware(K: np.ndarray, V: np.ndarray, W_O: np.ndarray, n_q_heads: int, rank_v: int,
+                     rank_k: int) -> Dict[str, np.ndarray]:
+    """Factors fitted against the attention output: per KV head g, B and the
+    group's folded projections from the reduced-rank fit of V.W_g, then P,
+    R_enc and R_dec as in fit_factors on the latents V.B.  K, V: calibration
+    tokens [n][H_kv][d_h]; W_O: [n_q_heads*d_h][d_model].  Returns fp32 B,
+    P, R_enc, R_dec in the library's layout and W_ofT [d_model][n_q_heads*r]
+    (fp32; round it to the storage dtype)."""
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    W_O = np.asarray(W_O, np.float64)
+    n, H, D = V.shape
+    G = n_q_heads // H
+    dm = W_O.shape[1]
+    if W_O.shape[0] != n_q_heads * D or n_q_heads % H:
+        raise ValueError("W_O must be [n_q_heads * d_h][d_model] with n_q_heads a multiple of n_kv_heads")
+    base = fit_factors(K, V, rank_v, rank_k)  # shapes; B, P, R_* replaced below
+    W_ofT = np.zeros((dm, n_q_heads * rank_v), np.float32)
+    for g in range(H):
+        v, k = V[:, g], K[:, g]
+        Wg = np.concatenate([W_O[(g * G + i) * D:(g * G + i + 1) * D] for i in range(G)], axis=1)
+        U = _leading_right_vectors(v @ Wg, rank_v)  # [G*dm][r]
+        B = Wg @ U
+        C = U.T                                     # [r][G*dm]
+        Z = v @ B
+        P, *_ = np.linalg.lstsq(Z, k, rcond=None)
+        Re = _leading_right_vectors(k - Z @ P, rank_k)
+        base["B"][g], base["P"][g], base["R_enc"][g], base["R_dec"][g] = B, P, Re, Re.T
+        for i in range(G):
+            h = g * G + i
+            W_ofT[:, h * rank_v:(h + 1) * rank_v] = C[:, i * dm:(i + 1) * dm].T
+    base["W_ofT"] = W_ofT
+    return base
 
 
 def page_mass(K: np.ndarray, q: np.ndarray, length: int, page_size: int, group: int,

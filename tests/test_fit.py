@@ -82,3 +82,52 @@ def test_recall_bounds():
     assert fit.recall(hot, [4, -1]) == 1.0 and fit.recall(hot, [0, 1, 2, 3, 5]) == 0.0
     for k in range(1, 10):
         assert fit.best_recall(m, k) >= fit.recall(m, rng.choice(10, k, replace=False)) - 1e-12
+
+
+def _wg(W_O, g, G, D):
+    return np.concatenate([W_O[(g * G + i) * D:(g * G + i + 1) * D] for i in range(G)], axis=1)
+
+
+def _latent_output(f, V, g, G, r, dm):
+    """V.B.C for KV head g's query heads, from the fitted B and W_ofT."""
+    B = f["B"][g].astype(np.float64)
+    C = np.concatenate([f["W_ofT"][:, (g * G + i) * r:(g * G + i + 1) * r].T for i in range(G)], axis=1)
+    return V @ B @ C.astype(np.float64)
+
+
+def test_output_fit_is_exact_for_a_low_rank_output_map():
+    """With each group's output map W_g of rank r, the reduced-rank fit
+    reproduces every output exactly, on Values it never saw."""
+    rng = np.random.default_rng(5)
+    H, G, D, r, dm, n = 2, 2, 16, 3, 10, 300
+    W_O = np.zeros((H * G * D, dm))
+    for g in range(H):
+        Wg = rng.standard_normal((D, r)) @ rng.standard_normal((r, G * dm))
+        for i in range(G):
+            W_O[(g * G + i) * D:(g * G + i + 1) * D] = Wg[:, i * dm:(i + 1) * dm]
+    V = rng.standard_normal((n, H, D))
+    K = rng.standard_normal((n, H, D))
+    f = fit.fit_output_aware(K, V, W_O, H * G, r, 2)
+    Vnew = rng.standard_normal((50, H, D))
+    for g in range(H):
+        np.testing.assert_allclose(_latent_output(f, Vnew[:, g], g, G, r, dm), Vnew[:, g] @ _wg(W_O, g, G, D),
+                                   atol=1e-4, rtol=1e-4)
+
+
+def test_output_fit_beats_the_value_basis_on_the_output():
+    """Both fits produce rank-r maps V -> output; the reduced-rank one is the
+    least-squares optimum, so its output error is never larger than that of
+    the Value basis folded into W_O (B.B^T.W_g)."""
+    rng = np.random.default_rng(6)
+    H, G, D, r, dm, n = 1, 4, 24, 5, 12, 400
+    W_O = rng.standard_normal((H * G * D, dm))
+    V = rng.standard_normal((n, H, D)) * np.linspace(2, 0.5, D)
+    K = rng.standard_normal((n, H, D))
+    f_out = fit.fit_output_aware(K, V, W_O, H * G, r, 2)
+    f_val = fit.fit_factors(K, V, r, 2)
+    Y = V[:, 0] @ _wg(W_O, 0, G, D)
+    B = f_val["B"][0].astype(np.float64)
+    err_val = np.linalg.norm(V[:, 0] @ B @ B.T @ _wg(W_O, 0, G, D) - Y)
+    err_out = np.linalg.norm(_latent_output(f_out, V[:, 0], 0, G, r, dm) - Y)
+    assert err_out <= err_val * (1 + 1e-6)
+    assert err_out < 0.95 * err_val  # strictly better on a generic map

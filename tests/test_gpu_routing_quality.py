@@ -62,3 +62,47 @@ def test_fitted_factors_route_to_more_attention_mass():
           f"{best:.4f}, uniform {w.top_k * w.page_size / n:.4f}")
     assert res["fitted"] > res["random"]
     assert res["fitted"] <= best + 1e-9
+
+
+def test_output_aware_fit_lowers_the_decode_error():
+    """The GPU decode (every page selected, so only the Value compression
+    acts) against exact dense attention through W_O, with the Value basis
+    folded into W_O against the basis and projection fitted to the output."""
+    import routed_decode_attention_amd as rda
+    w = configs.get("llama8b_32k").with_(name="fito", cfg_id=312, batch=4, top_k=16, d_model=256)
+    n = 1024  # 16 pages, all selected
+    sc = cases.make_scenario(w, lengths=[n] * w.batch, write=False)
+    cal = [synth.make_sequence(w, sc.fac, 200 + i, n) for i in range(4)]
+    Kc = np.concatenate([_f32(k) for k, _ in cal])
+    Vc = np.concatenate([_f32(v) for _, v in cal])
+    W_O = _f32(sc.fac.W_O).astype(np.float64)
+    G, D, dm = w.n_q_heads // w.n_kv_heads, w.head_dim, w.d_model
+    exact = np.zeros((w.batch, dm))
+    for b in range(w.batch):
+        Kb, Vb, qb = (_f32(x).astype(np.float64) for x in (sc.K[b], sc.V[b], sc.q[b]))
+        for h in range(w.n_q_heads):
+            s = Kb[:, h // G] @ qb[h] / np.sqrt(D)
+            p = np.exp(s - s.max())
+            exact[b] += (p / p.sum()) @ Vb[:, h // G] @ W_O[h * D:(h + 1) * D]
+    errs = {}
+    for name in ("value basis", "output fit"):
+        if name == "value basis":
+            fac = fit.fit_factors(Kc, Vc, w.rank_v, w.rank_k)
+        else:
+            fac = fit.fit_output_aware(Kc, Vc, W_O, w.n_q_heads, w.rank_v, w.rank_k)
+        g = gc.upload(sc)
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+        g.f = rda.Factors(B=dev(fac["B"]), P=dev(fac["P"]), R_enc=dev(fac["R_enc"]), R_dec=dev(fac["R_dec"]))
+        if name == "value basis":
+            g.f.W_ofT = torch.empty((dm, w.n_q_heads * w.rank_v), dtype=torch.bfloat16, device="cuda")
+            rda.basiskv_fold_output(g.d, g.f.B, gc.dev(sc.fac.W_O, w.dtype), g.f.W_ofT)
+        else:
+            g.f.W_ofT = dev(fac["W_ofT"]).to(torch.bfloat16)
+        gc.write_all(g, sc)
+        sel, n_sel, _ = gc.route(g)
+        assert (n_sel == n // w.page_size).all()
+        _, out = gc.decode(g, sel, n_sel)
+        errs[name] = float(np.linalg.norm(out - exact) / np.linalg.norm(exact))
+    print(f"\nrelative decode-output error against dense attention (r={w.rank_v} of d_h={D}): "
+          f"value basis {errs['value basis']:.4f}, output fit {errs['output fit']:.4f}")
+    assert errs["output fit"] < errs["value basis"]
