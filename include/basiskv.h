@@ -55,6 +55,10 @@
  *   score(j)   = max over the query heads h of KV head g
  *   the min(top_k, n_pg) highest scores are selected, ties to the smaller j;
  *   sel lists them in ascending j, padded with -1.
+ *   Forced pages (sink_pages, local_pages >= 0, both 0 for plain top-k): pages
+ *   j < sink_pages and j >= n_pg - local_pages rank above every score (among
+ *   themselves the smaller j first), so they are kept whenever they fit in
+ *   top_k; scores are reported unchanged.
  * ---------------------------------------------------------------------------
  */
 #ifndef BASISKV_H
@@ -67,7 +71,7 @@
 extern "C" {
 #endif
 
-#define BASISKV_VERSION 1
+#define BASISKV_VERSION 2
 
 enum {
   BASISKV_OK = 0,
@@ -110,6 +114,8 @@ typedef struct {
   int32_t num_phys_pages;     /* pages in each pool                                   */
   int32_t dtype;              /* BASISKV_F32 or BASISKV_BF16                          */
   float softmax_scale;        /* 0 -> 1/sqrt(head_dim)                                */
+  int32_t sink_pages;         /* routing: the first sink_pages pages are always kept  */
+  int32_t local_pages;        /* routing: the last local_pages pages are always kept  */
 } basiskv_dims;
 
 /* Factors.  Host struct of device pointers; read only. */

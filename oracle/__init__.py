@@ -45,7 +45,7 @@ class _Dims(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "batch", "n_q_heads", "n_kv_heads", "head_dim", "rank_v", "rank_k",
         "page_size", "d_model", "top_k", "max_pages", "num_pages", "dtype")] + [
-        ("scale", C.c_double)]
+        ("scale", C.c_double), ("sink_pages", C.c_int32), ("local_pages", C.c_int32)]
 
 
 class _Cache(C.Structure):
@@ -103,6 +103,8 @@ class Dims:
     num_pages: int
     dtype: int
     scale: float
+    sink_pages: int = 0
+    local_pages: int = 0
 
     @classmethod
     def of(cls, w: Workload, **kw) -> "Dims":
@@ -110,14 +112,15 @@ class Dims:
                     head_dim=w.head_dim, rank_v=w.rank_v, rank_k=w.rank_k,
                     page_size=w.page_size, d_model=w.d_model, top_k=w.top_k,
                     max_pages=w.max_pages_per_seq, num_pages=0, dtype=w.dtype,
-                    scale=w.softmax_scale)
+                    scale=w.softmax_scale, sink_pages=w.sink_pages, local_pages=w.local_pages)
         base.update(kw)
         return cls(**base)
 
     def c(self) -> _Dims:
         return _Dims(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim,
                      self.rank_v, self.rank_k, self.page_size, self.d_model,
-                     self.top_k, self.max_pages, self.num_pages, self.dtype, self.scale)
+                     self.top_k, self.max_pages, self.num_pages, self.dtype, self.scale,
+                     self.sink_pages, self.local_pages)
 
     @property
     def np_dtype(self):

@@ -174,12 +174,17 @@ void ora_write(const ora_dims *d, const float *B, const float *P, const float *R
 typedef struct {
   float score;
   int page;
+  int forced; /* kept whatever its score: one of the first sink_pages or last local_pages */
 } ranked;
 
+/* forced pages first, then the higher score; ties to the smaller page */
 static int by_score_then_page(const void *a, const void *b) {
   const ranked *x = a, *y = b;
-  if (x->score > y->score) return -1;
-  if (x->score < y->score) return 1;
+  if (x->forced != y->forced) return x->forced ? -1 : 1;
+  if (!x->forced) {
+    if (x->score > y->score) return -1;
+    if (x->score < y->score) return 1;
+  }
   return (x->page > y->page) - (x->page < y->page);
 }
 
@@ -232,6 +237,7 @@ void ora_route(const ora_dims *d, const float *P, const float *R_dec, const ora_
       rk[j].score = (float)best;
       if (rk[j].score == 0.0f) rk[j].score = 0.0f; /* one zero */
       rk[j].page = j;
+      rk[j].forced = j < d->sink_pages || j >= npg - d->local_pages;
       if (srow) srow[j] = rk[j].score;
     }
     if (srow)

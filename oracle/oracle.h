@@ -47,6 +47,7 @@ typedef struct {
   int32_t batch, n_q_heads, n_kv_heads, head_dim, rank_v, rank_k, page_size;
   int32_t d_model, top_k, max_pages, num_pages, dtype;
   double scale;           /* softmax scale, e.g. 1/sqrt(d_h) */
+  int32_t sink_pages, local_pages;  /* routing: pages always kept at either end */
 } ora_dims;
 
 typedef struct {

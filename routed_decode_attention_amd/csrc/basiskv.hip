@@ -90,6 +90,8 @@ int check_dims(const basiskv_dims* d, bkv::Shape* s) {
     return fail(BASISKV_E_DIMS, "unknown dtype %d", d->dtype);
   if (!(d->softmax_scale >= 0.f) || !isfinite(d->softmax_scale))
     return fail(BASISKV_E_DIMS, "softmax_scale must be finite and >= 0");
+  if (d->sink_pages < 0 || d->local_pages < 0)
+    return fail(BASISKV_E_DIMS, "sink_pages %d and local_pages %d must be >= 0", d->sink_pages, d->local_pages);
   const int group = d->n_q_heads / d->n_kv_heads;
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(BASISKV_E_UNSUPPORTED, "head_dim %d (supported: 64, 128)", d->head_dim);
@@ -261,9 +263,9 @@ int do_write(const bkv::Shape& s, const basiskv_factors* f, const basiskv_cache*
   return e == hipSuccess ? BASISKV_OK : hip_fail(e, "writer launch");
 }
 
-int do_route(const bkv::Shape& s, const basiskv_factors* f, const basiskv_cache* cache, const int32_t* pos,
-             const void* k_new, const void* v_new, const int32_t* seq_lens, const void* q, int32_t* sel,
-             int32_t* n_sel, float* scores, void* stream, int32_t* sel_phys, void* ws) {
+int do_route(const bkv::Shape& s, const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
+             const int32_t* pos, const void* k_new, const void* v_new, const int32_t* seq_lens, const void* q,
+             int32_t* sel, int32_t* n_sel, float* scores, void* stream, int32_t* sel_phys, void* ws) {
   if (!bkv::route_fits(s, pos != nullptr))
     return fail(BASISKV_E_UNSUPPORTED, "route: page table of %d pages with these factor sizes exceeds the LDS",
                 s.max_pages);
@@ -291,6 +293,8 @@ int do_route(const bkv::Shape& s, const basiskv_factors* f, const basiskv_cache*
   a.arrive = nullptr;
   a.part_keys = nullptr;
   a.part_pages = nullptr;
+  a.sink_pages = dims->sink_pages;
+  a.local_pages = dims->local_pages;
   if (ws) {
     const WsLayout L = ws_layout(s, 0);
     char* w = static_cast<char*>(ws);
@@ -395,7 +399,8 @@ int basiskv_route(const basiskv_dims* dims, const basiskv_factors* f, const basi
   bkv::ValidateArgs va = validate_args(s, cache);
   va.seq_lens = seq_lens;
   if ((rc = debug_check(va, stream, "route"))) return rc;
-  return do_route(s, f, cache, nullptr, nullptr, nullptr, seq_lens, q, sel, n_sel, scores, stream, sel_phys, ws);
+  return do_route(s, dims, f, cache, nullptr, nullptr, nullptr, seq_lens, q, sel, n_sel, scores, stream, sel_phys,
+                  ws);
 }
 
 int basiskv_append_route(const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
@@ -415,7 +420,7 @@ int basiskv_append_route(const basiskv_dims* dims, const basiskv_factors* f, con
   va.seq_lens = seq_lens;
   va.pos = pos;
   if ((rc = debug_check(va, stream, "append_route"))) return rc;
-  return do_route(s, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, stream, sel_phys, ws);
+  return do_route(s, dims, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, stream, sel_phys, ws);
 }
 
 size_t basiskv_workspace_bytes(const basiskv_dims* dims, int32_t max_prefill_tokens) {
@@ -515,7 +520,8 @@ int basiskv_decode_step(const basiskv_dims* dims, const basiskv_factors* f, cons
   va.seq_lens = seq_lens;
   va.pos = pos;
   if ((rc = debug_check(va, stream, "decode_step"))) return rc;
-  if ((rc = do_route(s, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, stream, sel_phys, ws)))
+  if ((rc = do_route(s, dims, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, stream, sel_phys,
+                     ws)))
     return rc;
   return attend_project(s, f, cache, seq_lens, q, sel, n_sel, sel_phys, ws, ws_bytes, z_out, out, stream);
 }

@@ -225,7 +225,9 @@ __host__ __device__ inline RouteLds route_lds(int maxp, int D, int R, int RK, in
 }
 
 // NG: 16-byte channel granules per scoring lane, at least ceil((r + r_k) / 16)
-template <typename T, bool APPEND, int D, int NG>
+// FORCE: pages kept at either end of the sequence (sink_pages, local_pages),
+// compiled in only when a call asks for them.
+template <typename T, bool APPEND, int D, int NG, bool FORCE>
 __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
   constexpr int PPL = 4;  // pages per scoring quad and load group
   extern __shared__ __attribute__((aligned(16))) float lds[];
@@ -866,8 +868,13 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
     if (lane == 0) put(ins, excl);
   };
 
+  // pages kept whatever their score -- the first sink_pages and the last
+  // local_pages of the sequence -- take a key above every score
+  auto forced = [&](int j) { return j < a.sink_pages || j >= npg - a.local_pages; };
   if (split && c == 0) {  // the appending workgroup: its page's score is in
-    const uint32_t ka = excl >= 0 ? s_keys[excl] : 0u;
+    uint32_t ka = excl >= 0 ? s_keys[excl] : 0u;
+    if constexpr (FORCE)
+      if (excl >= 0 && forced(excl)) ka = 0xFFFFFFFFu;
     if (meet((1ull << 63) | ka)) {
       if (!fast) {
         merge_appended(false, ka);
@@ -888,6 +895,11 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
     for (int j = tid; j < npg; j += RT)
       if (j != excl) s_keys[j] = float_key(agent_load(scp + j));
     __syncthreads();
+  }
+  if constexpr (FORCE) {
+    for (int j = tid; j < npg; j += RT)
+      if (forced(j)) s_keys[j] = 0xFFFFFFFFu;
+    lds_barrier();
   }
   const int ks = min(top_k, npg - (excl >= 0 ? 1 : 0));
   if (fast) {
@@ -958,14 +970,21 @@ size_t route_lds_bytes(const Shape& s, bool append) {
       .total;
 }
 
-template <typename T, bool APPEND, int D, int NG>
-hipError_t launch_t(const RouteArgs& a, hipStream_t st) {
+template <typename T, bool APPEND, int D, int NG, bool FORCE>
+hipError_t launch_f(const RouteArgs& a, hipStream_t st) {
   const size_t lds = route_lds_bytes(a.s, APPEND);
-  const hipError_t e = allow_lds((const void*)route_kernel<T, APPEND, D, NG>, lds);
+  const hipError_t e = allow_lds((const void*)route_kernel<T, APPEND, D, NG, FORCE>, lds);
   if (e != hipSuccess) return e;
   const int cl = route_cluster(a.s, APPEND, a.arrive != nullptr);
-  hipLaunchKernelGGL((route_kernel<T, APPEND, D, NG>), dim3(a.s.batch * a.s.n_kv_heads * cl), dim3(RT), lds, st, a);
+  hipLaunchKernelGGL((route_kernel<T, APPEND, D, NG, FORCE>), dim3(a.s.batch * a.s.n_kv_heads * cl), dim3(RT), lds,
+                     st, a);
   return hipGetLastError();
+}
+
+template <typename T, bool APPEND, int D, int NG>
+hipError_t launch_t(const RouteArgs& a, hipStream_t st) {
+  if (a.sink_pages > 0 || a.local_pages > 0) return launch_f<T, APPEND, D, NG, true>(a, st);
+  return launch_f<T, APPEND, D, NG, false>(a, st);
 }
 
 template <typename T, bool APPEND, int D>

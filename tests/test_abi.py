@@ -85,6 +85,8 @@ def _decode(lib, d, ws_bytes):
     (dict(rank_v=256), -2),
     (dict(dtype=7), -2),
     (dict(softmax_scale=-1.0), -2),
+    (dict(sink_pages=-1), -2),
+    (dict(local_pages=-3), -2),
     (dict(head_dim=96, rank_v=32), -3),
     (dict(page_size=48), -3),
     (dict(rank_v=24), -3),

@@ -50,6 +50,9 @@ CASES = {
     "bf16_p16": (small("p16", 205, batch=2, n_q_heads=2, n_kv_heads=1, head_dim=64,
                        page_size=16, rank_v=16, rank_k=8, top_k=4, d_model=64, dtype=BF16, ctx=100),
                  [100, 33]),
+    # forced pages: the first and the last two of every sequence are always kept
+    "g4_forced": (configs.get("llama8b_32k").with_(name="g4f", cfg_id=207, batch=3, top_k=6, d_model=256,
+                                                   sink_pages=1, local_pages=2), [700, 64, 130]),
     "ragged_permuted": (configs.get("ragged_mix").with_(name="rg", cfg_id=206, batch=5,
                                                         length_range=(1, 3000), top_k=16,
                                                         d_model=256),
@@ -133,7 +136,11 @@ def test_route_matches_oracle(name, pages_per_wg, monkeypatch):
             k = int(n_sel[b, h])
             np.testing.assert_allclose(gscores[b, h, :npg], scores[b, h, :npg], rtol=1e-5,
                                        atol=1e-5 * max(1.0, float(np.abs(scores[b, h, :npg]).max(initial=0))))
-            cases.check_selection_valid(scores[b, h, :npg], gs[b, h, :k], k, 1e-5)
+            forced = [j for j in range(npg) if j < sc.w.sink_pages or j >= npg - sc.w.local_pages]
+            ranked = scores[b, h, :npg].astype(np.float64).copy()
+            ranked[forced] = np.inf  # forced pages rank above every score
+            cases.check_selection_valid(ranked, gs[b, h, :k], k, 1e-5)
+            assert set(forced[:k]) <= set(gs[b, h, :k].tolist())
             assert (gs[b, h, k:] == -1).all()
 
 
@@ -248,8 +255,10 @@ def test_decode_step_end_to_end(name):
         same = True
         for h in range(sc.w.n_kv_heads):
             k = int(n_sel[b, h])
-            cases.check_selection_valid(scores[b, h, :-(-int(sc.lengths[b]) // sc.w.page_size)],
-                                        gs[b, h, :k], k, 1e-5)
+            npg = -(-int(sc.lengths[b]) // sc.w.page_size)
+            ranked = scores[b, h, :npg].astype(np.float64).copy()
+            ranked[[j for j in range(npg) if j < sc.w.sink_pages or j >= npg - sc.w.local_pages]] = np.inf
+            cases.check_selection_valid(ranked, gs[b, h, :k], k, 1e-5)
             same &= np.array_equal(gs[b, h], sel[b, h])
         if same:  # near-tie swaps change the softmax domain; compared via the decode test then
             np.testing.assert_allclose(out[b], out_ref[b], rtol=rtol, atol=atol)
@@ -360,7 +369,7 @@ def test_prefill_matches_oracle(name, chunks):
 
 
 @pytest.mark.parametrize("pages_per_wg", [None, 5, 8192])
-@pytest.mark.parametrize("name", ["g4_d128_p64", "g8_2kv_r48_p32", "ragged_permuted", "tiny_f32"])
+@pytest.mark.parametrize("name", ["g4_d128_p64", "g8_2kv_r48_p32", "ragged_permuted", "tiny_f32", "g4_forced"])
 def test_fused_append_route_equals_separate_calls(name, pages_per_wg, monkeypatch):
     """The decode step (append and route fused; with pages_per_wg set, a
     cluster of the appending workgroup and scorers of that many pages each,

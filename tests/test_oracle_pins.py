@@ -255,6 +255,34 @@ def test_topk_brute_force_with_ties(seed):
         np.testing.assert_array_equal(scores[0, 0, :npg], agg.astype(np.float32))
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_forced_pages_brute_force(seed):
+    """Pages kept at either end of the sequence (sink_pages, local_pages)
+    rank above every score, among themselves by page; the rest by score,
+    ties to the smaller page."""
+    rng = np.random.default_rng(100 + seed)
+    ps, G = 4, 1 + seed % 3
+    n = int(rng.integers(1, 60))
+    npg = -(-n // ps)
+    vals = rng.integers(-3, 4, size=(G, npg)).astype(np.float64)
+    d, fac, cache, q = _hand_cache(npg, ps, G, vals)
+    for j in range(npg):
+        cnt = min(ps, n - j * ps)
+        for h in range(G):
+            cache.summ[j, 0, h] = vals[h, j] * cnt
+    agg = vals.max(axis=0)
+    for sink, local, top_k in ((1, 0, 3), (0, 2, 3), (2, 2, 5), (3, 3, 4), (1, 1, 16), (0, 0, 5)):
+        d.top_k, d.sink_pages, d.local_pages = top_k, sink, local
+        sel, n_sel, scores = oracle.route(d, fac, cache, np.array([n], np.int32), q)
+        forced = [j for j in range(npg) if j < sink or j >= npg - local]
+        rest = sorted((j for j in range(npg) if j not in forced), key=lambda j: (-agg[j], j))
+        keff = min(top_k, npg)
+        want = sorted((forced + rest)[:keff])
+        assert n_sel[0, 0] == keff
+        assert sel[0, 0, :keff].tolist() == want, (sink, local, top_k)
+        np.testing.assert_array_equal(scores[0, 0, :npg], agg.astype(np.float32))  # scores unchanged
+
+
 def test_topk_all_equal_takes_first_pages():
     d, fac, cache, q = _hand_cache(10, 4, 1, np.zeros((1, 10)))
     cache.summ[:, 0, 0] = 8.0      # every score 2.0

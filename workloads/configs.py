@@ -60,6 +60,8 @@ class Workload:
     length_range: Optional[Tuple[int, int]] = None   # ragged: inclusive uniform range
     permuted_pages: bool = False
     prefill_chunk: Optional[int] = None               # prefill workloads: queries per chunk
+    sink_pages: int = 0         # routing: first pages always kept (0: plain top-k)
+    local_pages: int = 0        # routing: last pages always kept
 
     @property
     def group(self) -> int:
