@@ -337,6 +337,50 @@ def test_empty_and_single_token_sequences():
     np.testing.assert_allclose(out, out_ref, rtol=2e-2, atol=2e-3)
 
 
+def test_decode_step_edge_rows():
+    """The decode step (append fused into the router's cluster) over rows that
+    are empty, hold one token, start a page, append past the last page
+    (skipped), or append nothing (pos -1): against the oracle on the cache
+    those appends produce."""
+    import routed_decode_attention_amd as rda
+    w, _ = CASES["g4_d128_p64"]
+    lengths = [0, 1, 65, 700, 300]
+    pos = np.array([-1, 0, 64, 699, -1], np.int32)
+    cap = w.max_pages_per_seq * w.page_size
+    sc = cases.make_scenario(w.with_(batch=len(lengths)), lengths=lengths)  # the oracle cache holds every token
+    sel, n_sel, scores = oracle.route(sc.d, sc.fac, sc.cache, sc.lengths, sc.q)
+    z_ref, out_ref = oracle.decode(sc.d, sc.W_ofT, sc.cache, sc.lengths, sc.q, sel, n_sel)
+    g = gc.upload(sc, W_ofT=sc.W_ofT)
+    for b, n in enumerate(lengths):  # what the cache holds before the step
+        m = n - 1 if pos[b] >= 0 else n
+        if m > 0:
+            rda.basiskv_write(g.d, g.f, g.cache, b, 0, gc.dev(sc.K[b][:m], w.dtype), gc.dev(sc.V[b][:m], w.dtype))
+    B = len(lengths)
+    last = lambda X, b: X[b][max(lengths[b] - 1, 0)] if lengths[b] else np.zeros_like(sc.K[3][0])
+    kn = gc.dev(np.stack([last(sc.K, b) for b in range(B)]), w.dtype)
+    vn = gc.dev(np.stack([last(sc.V, b) for b in range(B)]), w.dtype)
+    pos_d = torch.from_numpy(pos).cuda()
+    pos_d[4] = cap  # past the last page: skipped like -1
+    gsel = torch.full((B, 1, w.top_k), -7, dtype=torch.int32, device="cuda")
+    gn = torch.full((B, 1), -7, dtype=torch.int32, device="cuda")
+    gscores = torch.zeros((B, 1, w.max_pages_per_seq), device="cuda")
+    z = torch.zeros((B, w.n_q_heads, w.rank_v), device="cuda")
+    out = torch.zeros((B, w.d_model), device="cuda")
+    rda.basiskv_decode_step(g.d, g.f, g.cache, pos_d, kn, vn, g.seq_lens, g.q, gsel, gn, gscores, g.ws, out,
+                            z_out=z)
+    torch.cuda.synchronize()
+    gs, gnn = gc.host(gsel), gc.host(gn)
+    assert np.array_equal(gnn, n_sel)
+    assert (gs[0] == -1).all() and (gc.host(out)[0] == 0).all()
+    for b, n in enumerate(lengths):
+        npg = -(-n // w.page_size)
+        k = int(n_sel[b, 0])
+        cases.check_selection_valid(scores[b, 0, :npg], gs[b, 0, :k], k, 1e-5)
+        if np.array_equal(gs[b, 0], sel[b, 0]):
+            np.testing.assert_allclose(gc.host(out)[b], out_ref[b], rtol=2e-2, atol=2e-3)
+    assert not gc.host(g.ws)[:12 * B].any()  # the router's counters are back at zero
+
+
 @pytest.mark.parametrize("name,chunks", [("g4_d128_p64", [0, 128, 300]), ("g8_2kv_r48_p32", [0, 77, 513]),
                                          ("tiny_f32", [0, 64, 200]), ("bf16_p16", [0, 40, 100])])
 def test_prefill_matches_oracle(name, chunks):
