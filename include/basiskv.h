@@ -52,7 +52,7 @@
  * Page sums, scores and selection (per sequence b and KV head g, n = seq_lens[b],
  * n_pg = ceil(n / page_size), cnt_j = min(page_size, n - j*page_size)):
  *   score_h(j) = scale * (P.q_h . sumz_j + R_dec.q_h . sums_j) / cnt_j
- *   score(j)   = max over the query heads h of KV head g
+ *   score(j)   = max over the query heads h of KV head g (their mean with group_mean)
  *   the min(top_k, n_pg) highest scores are selected, ties to the smaller j;
  *   sel lists them in ascending j, padded with -1.
  *   Forced pages (sink_pages, local_pages >= 0, both 0 for plain top-k): pages
@@ -116,6 +116,8 @@ typedef struct {
   float softmax_scale;        /* 0 -> 1/sqrt(head_dim)                                */
   int32_t sink_pages;         /* routing: the first sink_pages pages are always kept  */
   int32_t local_pages;        /* routing: the last local_pages pages are always kept  */
+  int32_t group_mean;         /* routing: 0 = a page's score is the max over the KV
+                                 head's query heads, 1 = their mean                  */
 } basiskv_dims;
 
 /* Factors.  Host struct of device pointers; read only. */

@@ -45,7 +45,8 @@ class _Dims(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "batch", "n_q_heads", "n_kv_heads", "head_dim", "rank_v", "rank_k",
         "page_size", "d_model", "top_k", "max_pages", "num_pages", "dtype")] + [
-        ("scale", C.c_double), ("sink_pages", C.c_int32), ("local_pages", C.c_int32)]
+        ("scale", C.c_double), ("sink_pages", C.c_int32), ("local_pages", C.c_int32),
+        ("group_mean", C.c_int32)]
 
 
 class _Cache(C.Structure):
@@ -105,6 +106,7 @@ class Dims:
     scale: float
     sink_pages: int = 0
     local_pages: int = 0
+    group_mean: int = 0
 
     @classmethod
     def of(cls, w: Workload, **kw) -> "Dims":
@@ -112,7 +114,8 @@ class Dims:
                     head_dim=w.head_dim, rank_v=w.rank_v, rank_k=w.rank_k,
                     page_size=w.page_size, d_model=w.d_model, top_k=w.top_k,
                     max_pages=w.max_pages_per_seq, num_pages=0, dtype=w.dtype,
-                    scale=w.softmax_scale, sink_pages=w.sink_pages, local_pages=w.local_pages)
+                    scale=w.softmax_scale, sink_pages=w.sink_pages, local_pages=w.local_pages,
+                    group_mean=w.group_mean)
         base.update(kw)
         return cls(**base)
 
@@ -120,7 +123,7 @@ class Dims:
         return _Dims(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim,
                      self.rank_v, self.rank_k, self.page_size, self.d_model,
                      self.top_k, self.max_pages, self.num_pages, self.dtype, self.scale,
-                     self.sink_pages, self.local_pages)
+                     self.sink_pages, self.local_pages, self.group_mean)
 
     @property
     def np_dtype(self):

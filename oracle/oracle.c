@@ -226,14 +226,16 @@ void ora_route(const ora_dims *d, const float *P, const float *R_dec, const ora_
     for (int j = 0; j < npg; ++j) {
       int phys = phys_of(d, c, b, j);
       int cnt = n - j * ps < ps ? n - j * ps : ps;
-      double best = -INFINITY;
+      double best = -INFINITY, sum = 0.0;
       for (int hh = 0; hh < G; ++hh) {
         double dot = 0.0;
         for (int x = 0; x < R + RK; ++x)
           dot += qz[(size_t)hh * (R + RK) + x] * (double)c->summ[summ_idx(d, phys, g, x)];
         double sc = d->scale * dot / cnt;
         if (sc > best) best = sc;
+        sum += sc;
       }
+      if (d->group_mean) best = sum / G; /* the group's mean instead of its max */
       rk[j].score = (float)best;
       if (rk[j].score == 0.0f) rk[j].score = 0.0f; /* one zero */
       rk[j].page = j;

@@ -48,6 +48,7 @@ typedef struct {
   int32_t d_model, top_k, max_pages, num_pages, dtype;
   double scale;           /* softmax scale, e.g. 1/sqrt(d_h) */
   int32_t sink_pages, local_pages;  /* routing: pages always kept at either end */
+  int32_t group_mean;               /* routing: group score = mean over its query heads (else max) */
 } ora_dims;
 
 typedef struct {

@@ -37,7 +37,8 @@ class basiskv_dims(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "batch", "n_q_heads", "n_kv_heads", "head_dim", "rank_v", "rank_k", "page_size",
         "d_model", "top_k", "max_pages_per_seq", "num_phys_pages", "dtype")] + [
-        ("softmax_scale", C.c_float), ("sink_pages", C.c_int32), ("local_pages", C.c_int32)]
+        ("softmax_scale", C.c_float), ("sink_pages", C.c_int32), ("local_pages", C.c_int32),
+        ("group_mean", C.c_int32)]
 
 
 class basiskv_factors(C.Structure):
@@ -135,12 +136,13 @@ class Dims:
     softmax_scale: float = 0.0
     sink_pages: int = 0
     local_pages: int = 0
+    group_mean: int = 0
 
     def c(self) -> basiskv_dims:
         return basiskv_dims(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim,
                             self.rank_v, self.rank_k, self.page_size, self.d_model, self.top_k,
                             self.max_pages_per_seq, self.num_phys_pages, self.dtype,
-                            self.softmax_scale, self.sink_pages, self.local_pages)
+                            self.softmax_scale, self.sink_pages, self.local_pages, self.group_mean)
 
     @property
     def torch_dtype(self):

@@ -92,6 +92,7 @@ int check_dims(const basiskv_dims* d, bkv::Shape* s) {
     return fail(BASISKV_E_DIMS, "softmax_scale must be finite and >= 0");
   if (d->sink_pages < 0 || d->local_pages < 0)
     return fail(BASISKV_E_DIMS, "sink_pages %d and local_pages %d must be >= 0", d->sink_pages, d->local_pages);
+  if (d->group_mean != 0 && d->group_mean != 1) return fail(BASISKV_E_DIMS, "group_mean %d (0 or 1)", d->group_mean);
   const int group = d->n_q_heads / d->n_kv_heads;
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(BASISKV_E_UNSUPPORTED, "head_dim %d (supported: 64, 128)", d->head_dim);
@@ -295,6 +296,7 @@ int do_route(const bkv::Shape& s, const basiskv_dims* dims, const basiskv_factor
   a.part_pages = nullptr;
   a.sink_pages = dims->sink_pages;
   a.local_pages = dims->local_pages;
+  a.group_mean = dims->group_mean;
   if (ws) {
     const WsLayout L = ws_layout(s, 0);
     char* w = static_cast<char*>(ws);

@@ -50,6 +50,7 @@ struct RouteArgs {
   uint32_t* part_keys;        // [batch][n_kv_heads][top_k] a cluster's selection without the appended page
   int32_t* part_pages;        //   (keys and pages), handed to whichever finishes the selection
   int sink_pages, local_pages;  // pages always kept at either end of a sequence (0, 0: plain top-k)
+  int group_mean;               // a page's score over the group's query heads: 0 max, 1 mean
 };
 
 // Workgroups per (sequence, KV head) of the router: one for the append (when

@@ -165,12 +165,13 @@ __device__ __forceinline__ void bitonic_sort(uint64_t& x, int lane, bool up) {
 
 // best[i] = max over the group's heads h of qc[h] . sums(page i), each dot
 // split over the four lanes of a quad (NG 16-byte channel granules per lane,
-// granule part + 4u) and summed by the quad.
-template <int NG, int PPL>
+// granule part + 4u) and summed by the quad; the group's max (MEAN: mean)
+// over its query heads.
+template <int NG, int PPL, bool MEAN>
 __device__ __forceinline__ void score_group(const f32x4 (&sv)[PPL][NG], const float (*qc)[XMAX], int G, int part,
                                             float (&best)[PPL]) {
 #pragma unroll
-  for (int i = 0; i < PPL; ++i) best[i] = -__builtin_huge_valf();
+  for (int i = 0; i < PPL; ++i) best[i] = MEAN ? 0.f : -__builtin_huge_valf();
   for (int h = 0; h < G; ++h) {
     f32x4 qg[NG];
 #pragma unroll
@@ -182,9 +183,13 @@ __device__ __forceinline__ void score_group(const f32x4 (&sv)[PPL][NG], const fl
       for (int u = 0; u < NG; ++u)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc = fmaf(qg[u][e], sv[i][u][e], acc);
-      best[i] = fmaxf(best[i], quad_sum(acc));
+      if constexpr (MEAN) best[i] += quad_sum(acc);
+      else best[i] = fmaxf(best[i], quad_sum(acc));
     }
   }
+  if constexpr (MEAN)
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) best[i] /= (float)G;
 }
 
 // Four consecutive storage-dtype elements from LDS as fp32.
@@ -225,9 +230,10 @@ __host__ __device__ inline RouteLds route_lds(int maxp, int D, int R, int RK, in
 }
 
 // NG: 16-byte channel granules per scoring lane, at least ceil((r + r_k) / 16)
-// FORCE: pages kept at either end of the sequence (sink_pages, local_pages),
-// compiled in only when a call asks for them.
-template <typename T, bool APPEND, int D, int NG, bool FORCE>
+// FORCE: pages kept at either end of the sequence (sink_pages, local_pages);
+// MEAN: a page's score is the mean over the group's query heads, not the
+// max.  Each compiled in only when a call asks for it.
+template <typename T, bool APPEND, int D, int NG, bool FORCE, bool MEAN>
 __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
   constexpr int PPL = 4;  // pages per scoring quad and load group
   extern __shared__ __attribute__((aligned(16))) float lds[];
@@ -342,7 +348,7 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
         for (int e = 0; e < 4; ++e) sv[i][u][e] = __uint_as_float(__float_as_uint(sv[i][u][e]) & keep);
       }
   };
-  auto score = [&](float (&best)[PPL]) { score_group<NG, PPL>(sv, s_qc, G, part, best); };
+  auto score = [&](float (&best)[PPL]) { score_group<NG, PPL, MEAN>(sv, s_qc, G, part, best); };
   // (in a cluster the scores are read back by another workgroup: stored
   // coherently at device scope)
   auto finish = [&](int j, float best) {
@@ -544,10 +550,11 @@ __global__ __launch_bounds__(RT) void route_kernel(RouteArgs a) {
               if (x0 + x < RR) d[h] = fmaf(s_qc[h][x0 + x], v[x], d[h]);
           }
       }
-      float best = -__builtin_huge_valf();
+      float best = MEAN ? 0.f : -__builtin_huge_valf();
 #pragma unroll
       for (int h = 0; h < MAX_GROUP; ++h)
-        if (h < G) best = fmaxf(best, d[h]);
+        if (h < G) best = MEAN ? best + d[h] : fmaxf(best, d[h]);
+      if constexpr (MEAN) best /= (float)G;
       finish(j, best);
     }
   }
@@ -970,21 +977,26 @@ size_t route_lds_bytes(const Shape& s, bool append) {
       .total;
 }
 
-template <typename T, bool APPEND, int D, int NG, bool FORCE>
+template <typename T, bool APPEND, int D, int NG, bool FORCE, bool MEAN>
 hipError_t launch_f(const RouteArgs& a, hipStream_t st) {
   const size_t lds = route_lds_bytes(a.s, APPEND);
-  const hipError_t e = allow_lds((const void*)route_kernel<T, APPEND, D, NG, FORCE>, lds);
+  const hipError_t e = allow_lds((const void*)route_kernel<T, APPEND, D, NG, FORCE, MEAN>, lds);
   if (e != hipSuccess) return e;
   const int cl = route_cluster(a.s, APPEND, a.arrive != nullptr);
-  hipLaunchKernelGGL((route_kernel<T, APPEND, D, NG, FORCE>), dim3(a.s.batch * a.s.n_kv_heads * cl), dim3(RT), lds,
-                     st, a);
+  hipLaunchKernelGGL((route_kernel<T, APPEND, D, NG, FORCE, MEAN>), dim3(a.s.batch * a.s.n_kv_heads * cl), dim3(RT),
+                     lds, st, a);
   return hipGetLastError();
 }
 
 template <typename T, bool APPEND, int D, int NG>
 hipError_t launch_t(const RouteArgs& a, hipStream_t st) {
-  if (a.sink_pages > 0 || a.local_pages > 0) return launch_f<T, APPEND, D, NG, true>(a, st);
-  return launch_f<T, APPEND, D, NG, false>(a, st);
+  const bool force = a.sink_pages > 0 || a.local_pages > 0;
+  if (a.group_mean) {
+    if (force) return launch_f<T, APPEND, D, NG, true, true>(a, st);
+    return launch_f<T, APPEND, D, NG, false, true>(a, st);
+  }
+  if (force) return launch_f<T, APPEND, D, NG, true, false>(a, st);
+  return launch_f<T, APPEND, D, NG, false, false>(a, st);
 }
 
 template <typename T, bool APPEND, int D>

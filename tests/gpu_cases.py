@@ -35,7 +35,8 @@ def dims_of(w: Workload, batch: int, num_pages: int, **kw) -> rda.Dims:
     base = dict(batch=batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
                 rank_v=w.rank_v, rank_k=w.rank_k, page_size=w.page_size, d_model=w.d_model,
                 top_k=w.top_k, max_pages_per_seq=w.max_pages_per_seq, num_phys_pages=num_pages,
-                dtype=w.dtype, softmax_scale=0.0, sink_pages=w.sink_pages, local_pages=w.local_pages)
+                dtype=w.dtype, softmax_scale=0.0, sink_pages=w.sink_pages, local_pages=w.local_pages,
+                group_mean=w.group_mean)
     base.update(kw)
     return rda.Dims(**base)
 

@@ -53,6 +53,12 @@ CASES = {
     # forced pages: the first and the last two of every sequence are always kept
     "g4_forced": (configs.get("llama8b_32k").with_(name="g4f", cfg_id=207, batch=3, top_k=6, d_model=256,
                                                    sink_pages=1, local_pages=2), [700, 64, 130]),
+    # the group's mean score instead of its max, alone and with forced pages
+    "g4_mean": (configs.get("llama8b_32k").with_(name="g4m", cfg_id=208, batch=3, top_k=5, d_model=256,
+                                                 group_mean=1), [700, 64, 130]),
+    "g8_mean_forced": (small("g8mf", 209, batch=2, n_q_heads=16, n_kv_heads=2, head_dim=128, page_size=32,
+                             rank_v=48, rank_k=16, top_k=7, d_model=192, dtype=BF16, ctx=513, group_mean=1,
+                             sink_pages=1, local_pages=1), [513, 200]),
     "ragged_permuted": (configs.get("ragged_mix").with_(name="rg", cfg_id=206, batch=5,
                                                         length_range=(1, 3000), top_k=16,
                                                         d_model=256),
@@ -413,7 +419,8 @@ def test_prefill_matches_oracle(name, chunks):
 
 
 @pytest.mark.parametrize("pages_per_wg", [None, 5, 8192])
-@pytest.mark.parametrize("name", ["g4_d128_p64", "g8_2kv_r48_p32", "ragged_permuted", "tiny_f32", "g4_forced"])
+@pytest.mark.parametrize("name", ["g4_d128_p64", "g8_2kv_r48_p32", "ragged_permuted", "tiny_f32", "g4_forced",
+                                  "g8_mean_forced"])
 def test_fused_append_route_equals_separate_calls(name, pages_per_wg, monkeypatch):
     """The decode step (append and route fused; with pages_per_wg set, a
     cluster of the appending workgroup and scorers of that many pages each,

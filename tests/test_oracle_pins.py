@@ -283,6 +283,29 @@ def test_forced_pages_brute_force(seed):
         np.testing.assert_array_equal(scores[0, 0, :npg], agg.astype(np.float32))  # scores unchanged
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_group_mean_brute_force(seed):
+    """group_mean: a page's score is the mean of its query heads' scores."""
+    rng = np.random.default_rng(200 + seed)
+    ps, G = 4, 2 + seed % 3
+    n = int(rng.integers(1, 60))
+    npg = -(-n // ps)
+    vals = rng.integers(-3, 4, size=(G, npg)).astype(np.float64)
+    d, fac, cache, q = _hand_cache(npg, ps, G, vals)
+    for j in range(npg):
+        cnt = min(ps, n - j * ps)
+        for h in range(G):
+            cache.summ[j, 0, h] = vals[h, j] * cnt
+    d.group_mean = 1
+    for top_k in (1, 3, 16):
+        d.top_k = top_k
+        sel, n_sel, scores = oracle.route(d, fac, cache, np.array([n], np.int32), q)
+        mean = vals.mean(axis=0)
+        np.testing.assert_allclose(scores[0, 0, :npg], mean, rtol=1e-6, atol=1e-6)
+        keff = min(top_k, npg)
+        assert sel[0, 0, :keff].tolist() == cases.brute_topk(scores[0, 0, :npg].astype(np.float64), keff)
+
+
 def test_topk_all_equal_takes_first_pages():
     d, fac, cache, q = _hand_cache(10, 4, 1, np.zeros((1, 10)))
     cache.summ[:, 0, 0] = 8.0      # every score 2.0

@@ -62,6 +62,7 @@ class Workload:
     prefill_chunk: Optional[int] = None               # prefill workloads: queries per chunk
     sink_pages: int = 0         # routing: first pages always kept (0: plain top-k)
     local_pages: int = 0        # routing: last pages always kept
+    group_mean: int = 0         # routing: group score = mean over its query heads (0: max)
 
     @property
     def group(self) -> int:
