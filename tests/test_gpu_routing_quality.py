@@ -30,9 +30,11 @@ def test_fitted_factors_route_to_more_attention_mass():
     G = w.n_q_heads // w.n_kv_heads
     masses = [fit.page_mass(_f32(sc.K[b]), _f32(sc.q[b]), n, w.page_size, G) for b in range(w.batch)]
     res = {}
-    for name in ("random", "fitted"):
+    for name in ("random", "fitted", "fitted, group mean"):
         g = gc.upload(sc)
-        if name == "fitted":
+        if name == "fitted, group mean":
+            g.d.group_mean = 1
+        if name != "random":
             g.f = rda.Factors(B=torch.from_numpy(fitted["B"]).cuda(), P=torch.from_numpy(fitted["P"]).cuda(),
                               R_enc=torch.from_numpy(fitted["R_enc"]).cuda(),
                               R_dec=torch.from_numpy(fitted["R_dec"]).cuda(), W_ofT=g.f.W_ofT)
@@ -58,8 +60,9 @@ def test_fitted_factors_route_to_more_attention_mass():
             exact.append(fit.recall(masses[b][h * G:(h + 1) * G], top))
     exact = float(np.mean(exact))
     print(f"\nrecall of {w.top_k} of {n // w.page_size} pages: random factors {res['random']:.4f}, "
-          f"fitted {res['fitted']:.4f}, page-mean routing on exact Keys {exact:.4f}, best per head "
-          f"{best:.4f}, uniform {w.top_k * w.page_size / n:.4f}")
+          f"fitted {res['fitted']:.4f} (group mean instead of max: {res['fitted, group mean']:.4f}), "
+          f"page-mean routing on exact Keys {exact:.4f}, best per head {best:.4f}, "
+          f"uniform {w.top_k * w.page_size / n:.4f}")
     assert res["fitted"] > res["random"]
     assert res["fitted"] <= best + 1e-9
 
