@@ -261,7 +261,7 @@ def main():
             res_o.update(sel=s_, n_sel=n_, scores=sc_, out=o_)
 
         reps, t_cpu = 0, 0.0
-        while t_cpu < args.cpu_seconds and reps < 1000:
+        while t_cpu < args.cpu_seconds and reps < 100000:
             t1 = time.perf_counter()
             ostep()
             t_cpu += time.perf_counter() - t1
