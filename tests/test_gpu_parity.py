@@ -418,6 +418,77 @@ def test_prefill_matches_oracle(name, chunks):
     compare_written(sc, gc.cache_host(g), ora)
 
 
+def test_prefill_interleaved_with_decode_steps():
+    """Serving order: sequence 0 is prefilled chunk by chunk while the other
+    rows run decode steps (row 0 inactive: length 0, no append) between the
+    chunks; then row 0 joins a decode step over its prefilled cache.  Every
+    chunk and every step against the oracle run in the same order on its own
+    cache, and the final caches against each other."""
+    import routed_decode_attention_amd as rda
+    w, _ = CASES["g4_d128_p64"]
+    final = [450, 300, 129, 64]
+    chunks = [0, 150, 300, 450]
+    B, steps = len(final), len(chunks) - 1
+    w = w.with_(batch=B)
+    sc = cases.make_scenario(w, lengths=final, write=False)
+    qp = synth.to_storage(np.random.default_rng(11).standard_normal((final[0], w.n_q_heads, w.head_dim)), w.dtype)
+    ora = oracle.Cache(sc.d, sc.page_table)
+    W = oracle.fold(sc.d, sc.fac.B, sc.fac.W_O)
+    g = gc.upload(sc, W_ofT=W, max_prefill=final[0])
+    for b in range(1, B):  # the decoding rows hold all but their last `steps` tokens
+        m = final[b] - steps
+        oracle.write(sc.d, sc.fac, ora, b, 0, sc.K[b][:m], sc.V[b][:m])
+        rda.basiskv_write(g.d, g.f, g.cache, b, 0, gc.dev(sc.K[b][:m], w.dtype), gc.dev(sc.V[b][:m], w.dtype))
+    rtol, atol = gc.tol(w)
+
+    def decode_step(lengths, pos):
+        """One decode step on both sides; rows with pos >= 0 append token pos."""
+        for b in range(B):
+            if pos[b] >= 0:
+                oracle.write(sc.d, sc.fac, ora, b, int(pos[b]), sc.K[b][pos[b]:pos[b] + 1],
+                             sc.V[b][pos[b]:pos[b] + 1])
+        lens = np.asarray(lengths, np.int32)
+        sel, n_sel, scores = oracle.route(sc.d, sc.fac, ora, lens, sc.q)
+        _, out_ref = oracle.decode(sc.d, W, ora, lens, sc.q, sel, n_sel)
+        tok = lambda X, b: X[b][max(int(pos[b]), 0)]
+        kn = gc.dev(np.stack([tok(sc.K, b)[None] for b in range(B)]), w.dtype)
+        vn = gc.dev(np.stack([tok(sc.V, b)[None] for b in range(B)]), w.dtype)
+        g.seq_lens.copy_(torch.from_numpy(lens))
+        gsel = torch.full((B, 1, w.top_k), -7, dtype=torch.int32, device="cuda")
+        gn = torch.full((B, 1), -7, dtype=torch.int32, device="cuda")
+        gscores = torch.zeros((B, 1, w.max_pages_per_seq), device="cuda")
+        out = torch.zeros((B, w.d_model), device="cuda")
+        rda.basiskv_decode_step(g.d, g.f, g.cache, torch.from_numpy(np.asarray(pos, np.int32)).cuda(), kn, vn,
+                                g.seq_lens, g.q, gsel, gn, gscores, g.ws, out)
+        torch.cuda.synchronize()
+        gs, gnn, go = gc.host(gsel), gc.host(gn), gc.host(out)
+        assert np.array_equal(gnn, n_sel)
+        for b in range(B):
+            k = int(n_sel[b, 0])
+            if lengths[b] == 0:
+                assert k == 0 and (go[b] == 0).all()
+                continue
+            npg = -(-int(lengths[b]) // w.page_size)
+            cases.check_selection_valid(scores[b, 0, :npg], gs[b, 0, :k], k, 1e-5)
+            if np.array_equal(gs[b, 0], sel[b, 0]):
+                np.testing.assert_allclose(go[b], out_ref[b], rtol=2e-2, atol=2e-3)
+
+    for i in range(steps):
+        a, e = chunks[i], chunks[i + 1]
+        z_ref, o_ref = oracle.prefill(sc.d, sc.fac, W, ora, 0, a, qp[a:e], sc.K[0][a:e], sc.V[0][a:e])
+        z = torch.empty((e - a, w.n_q_heads, w.rank_v), device="cuda")
+        out = torch.empty((e - a, w.d_model), device="cuda")
+        rda.basiskv_prefill(g.d, g.f, g.cache, 0, a, gc.dev(qp[a:e], w.dtype), gc.dev(sc.K[0][a:e], w.dtype),
+                            gc.dev(sc.V[0][a:e], w.dtype), g.ws, out, z_out=z)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(gc.host(z), z_ref, rtol=rtol, atol=atol)
+        np.testing.assert_allclose(gc.host(out), o_ref, rtol=rtol, atol=atol)
+        p = [-1] + [final[b] - steps + i for b in range(1, B)]
+        decode_step([0] + [final[b] - steps + i + 1 for b in range(1, B)], p)
+    decode_step(final, [-1] * B)  # row 0 joins: routed attention over its prefilled pages
+    compare_written(sc, gc.cache_host(g), ora)
+
+
 @pytest.mark.parametrize("pages_per_wg", [None, 5, 8192])
 @pytest.mark.parametrize("name", ["g4_d128_p64", "g8_2kv_r48_p32", "ragged_permuted", "tiny_f32", "g4_forced",
                                   "g8_mean_forced"])
