@@ -26,8 +26,8 @@ regression) is B = W_g.U_r, C = U_r^T with U_r the r leading right singular
 vectors of X.W_g: the latent basis B and, per head, the folded projection
 W_of[h] = C's block for h -- passed to the library as W_ofT instead of
 folding B^T.W_O (which assumes an orthonormal B).  Across several GPUs'
-partitions the same fit would run on the stacked outputs of all of them; one
-GPU's share is fitted here.
+partitions, fit_joint_projection refits every head's projection together
+against the layer's whole output, given the latent bases.
 
 Routing quality: for a query head, page j of a sequence holds the exact
 softmax mass m_j = sum over its tokens of softmax(scale * q.k)_t; a
@@ -101,6 +101,32 @@ def fit_output_aware(K: np.ndarray, V: np.ndarray, W_O: np.ndarray, n_q_heads: i
             W_ofT[:, h * rank_v:(h + 1) * rank_v] = C[:, i * dm:(i + 1) * dm].T
     base["W_ofT"] = W_ofT
     return base
+
+
+def fit_joint_projection(O: np.ndarray, W_O: np.ndarray, B: np.ndarray) -> np.ndarray:
+    """The folded projections of every query head fitted together against the
+    layer's whole output (the pages' joint fit across partitions, for a fixed
+    latent basis).  O: calibration attention outputs [n][H_q][d_h] (for each
+    calibration query, head h's softmax-weighted Values); W_O:
+    [H_q*d_h][d_model]; B: [H_kv][d_h][r], head h reading B[h // group].
+    Since ẑ_h = o_h.B before rounding, the layer output Σ_h o_h.W_O[h] is
+    approximated by Σ_h (o_h.B_g(h)).W_of[h]: linear in all the W_of[h] at
+    once, so one least-squares solve over the n calibration rows fits them
+    jointly, each head's block knowing every other head's error (heads on
+    other GPUs included when O and W_O hold the whole layer; a GPU keeps its
+    heads' columns).  Returns W_ofT [d_model][H_q*r] (fp32)."""
+    O = np.asarray(O, np.float64)
+    W_O = np.asarray(W_O, np.float64)
+    B = np.asarray(B, np.float64)
+    n, Hq, D = O.shape
+    H, _, r = B.shape
+    if B.shape[1] != D or Hq % H or W_O.shape[0] != Hq * D:
+        raise ValueError("O [n][H_q][d_h], W_O [H_q*d_h][d_model], B [H_kv][d_h][r] with H_q a multiple of H_kv")
+    G = Hq // H
+    Y = sum(O[:, h] @ W_O[h * D:(h + 1) * D] for h in range(Hq))        # [n][d_model]
+    X = np.concatenate([O[:, h] @ B[h // G] for h in range(Hq)], axis=1)  # [n][H_q*r]
+    W_of, *_ = np.linalg.lstsq(X, Y, rcond=None)                          # [H_q*r][d_model]
+    return np.ascontiguousarray(W_of.T, np.float32)
 
 
 def page_mass(K: np.ndarray, q: np.ndarray, length: int, page_size: int, group: int,

@@ -131,3 +131,59 @@ def test_output_fit_beats_the_value_basis_on_the_output():
     err_out = np.linalg.norm(_latent_output(f_out, V[:, 0], 0, G, r, dm) - Y)
     assert err_out <= err_val * (1 + 1e-6)
     assert err_out < 0.95 * err_val  # strictly better on a generic map
+
+
+def _joint_residual(O, W_O, B, WofT):
+    n, Hq, D = O.shape
+    G, r = Hq // B.shape[0], B.shape[2]
+    Y = sum(O[:, h] @ W_O[h * D:(h + 1) * D] for h in range(Hq))
+    Yh = sum(O[:, h] @ B[h // G] @ WofT[:, h * r:(h + 1) * r].T for h in range(Hq))
+    return np.linalg.norm(Yh - Y)
+
+
+def test_joint_projection_recovers_a_planted_map():
+    """W_O[h] = B_g(h).M_h makes the layer output exactly Σ_h (o_h.B_g).M_h:
+    the joint fit returns every M_h, which only the right head -> group map
+    and orientation can do (the two groups' bases differ)."""
+    rng = np.random.default_rng(8)
+    H, G, D, r, dm, n = 2, 2, 8, 3, 5, 200
+    B = rng.standard_normal((H, D, r))
+    M = rng.standard_normal((H * G, r, dm))
+    W_O = np.concatenate([B[h // G] @ M[h] for h in range(H * G)])
+    O = rng.standard_normal((n, H * G, D))
+    WofT = fit.fit_joint_projection(O, W_O, B)
+    assert WofT.shape == (dm, H * G * r)
+    for h in range(H * G):
+        np.testing.assert_allclose(WofT[:, h * r:(h + 1) * r], M[h].T, atol=1e-4)
+    assert _joint_residual(O, W_O, B, WofT.astype(np.float64)) < 1e-3
+
+
+def test_joint_projection_beats_per_head_and_per_partition_fits():
+    """On outputs correlated across heads, the joint least-squares fit leaves
+    a smaller error on the summed output than folding B^T.W_O per head or
+    fitting each partition (half the heads, as on another GPU) against its
+    own part of the output; never larger, as the joint optimum."""
+    rng = np.random.default_rng(9)
+    H, G, D, r, dm, n = 4, 2, 12, 3, 16, 600
+    Hq = H * G
+    shared = rng.standard_normal((n, D))  # a component every head's output carries
+    O = 0.7 * shared[:, None, :] + rng.standard_normal((n, Hq, D))
+    W_O = rng.standard_normal((Hq * D, dm))
+    B = np.stack([_orthonormal(rng, D, r) for _ in range(H)])
+    joint = fit.fit_joint_projection(O, W_O, B).astype(np.float64)
+    fold = np.concatenate([B[h // G].T @ W_O[h * D:(h + 1) * D] for h in range(Hq)]).T
+    half = Hq // 2
+    part = np.concatenate([fit.fit_joint_projection(O[:, p * half:(p + 1) * half],
+                                                    W_O[p * half * D:(p + 1) * half * D],
+                                                    B[p * H // 2:(p + 1) * H // 2]).astype(np.float64)
+                           for p in range(2)], axis=1)
+    e_joint, e_fold, e_part = (_joint_residual(O, W_O, B, x) for x in (joint, fold, part))
+    assert e_joint <= e_part * (1 + 1e-9) and e_joint <= e_fold * (1 + 1e-9)
+    assert e_joint < 0.97 * e_part and e_part < e_fold
+
+
+def test_joint_projection_rejects_bad_shapes():
+    with pytest.raises(ValueError):
+        fit.fit_joint_projection(np.zeros((10, 3, 8)), np.zeros((24, 4)), np.zeros((2, 8, 2)))  # 3 % 2
+    with pytest.raises(ValueError):
+        fit.fit_joint_projection(np.zeros((10, 4, 8)), np.zeros((30, 4)), np.zeros((2, 8, 2)))

@@ -70,7 +70,9 @@ def test_fitted_factors_route_to_more_attention_mass():
 def test_output_aware_fit_lowers_the_decode_error():
     """The GPU decode (every page selected, so only the Value compression
     acts) against exact dense attention through W_O, with the Value basis
-    folded into W_O against the basis and projection fitted to the output."""
+    folded into W_O against the basis and projection fitted to the output, and
+    against that basis with every head's projection refitted jointly to the
+    layer output of calibration queries."""
     import routed_decode_attention_amd as rda
     w = configs.get("llama8b_32k").with_(name="fito", cfg_id=312, batch=4, top_k=16, d_model=256)
     n = 1024  # 16 pages, all selected
@@ -87,12 +89,28 @@ def test_output_aware_fit_lowers_the_decode_error():
             s = Kb[:, h // G] @ qb[h] / np.sqrt(D)
             p = np.exp(s - s.max())
             exact[b] += (p / p.sum()) @ Vb[:, h // G] @ W_O[h * D:(h + 1) * D]
+    # the joint fit's calibration outputs: dense attention of 2048 queries
+    # (a seed apart from the test's) over each calibration sequence
+    nq = 2048
+    qc = _f32(synth.make_queries(w, n_rows=nq, seed=7)).astype(np.float64)
+    O = []
+    for k, v in cal:
+        Kb, Vb = _f32(k).astype(np.float64), _f32(v).astype(np.float64)
+        o = np.empty((nq, w.n_q_heads, D))
+        for h in range(w.n_q_heads):
+            s = qc[:, h] @ Kb[:, h // G].T / np.sqrt(D)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            o[:, h] = (p / p.sum(axis=1, keepdims=True)) @ Vb[:, h // G]
+        O.append(o)
+    O = np.concatenate(O)
     errs = {}
-    for name in ("value basis", "output fit"):
+    for name in ("value basis", "output fit", "joint fit"):
         if name == "value basis":
             fac = fit.fit_factors(Kc, Vc, w.rank_v, w.rank_k)
         else:
             fac = fit.fit_output_aware(Kc, Vc, W_O, w.n_q_heads, w.rank_v, w.rank_k)
+            if name == "joint fit":  # the output fit's basis, every head's projection refitted together
+                fac["W_ofT"] = fit.fit_joint_projection(O, W_O, fac["B"])
         g = gc.upload(sc)
         dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
         g.f = rda.Factors(B=dev(fac["B"]), P=dev(fac["P"]), R_enc=dev(fac["R_enc"]), R_dec=dev(fac["R_dec"]))
@@ -107,5 +125,6 @@ def test_output_aware_fit_lowers_the_decode_error():
         _, out = gc.decode(g, sel, n_sel)
         errs[name] = float(np.linalg.norm(out - exact) / np.linalg.norm(exact))
     print(f"\nrelative decode-output error against dense attention (r={w.rank_v} of d_h={D}): "
-          f"value basis {errs['value basis']:.4f}, output fit {errs['output fit']:.4f}")
-    assert errs["output fit"] < errs["value basis"]
+          f"value basis {errs['value basis']:.4f}, output fit {errs['output fit']:.4f}, "
+          f"joint fit {errs['joint fit']:.4f}")
+    assert errs["joint fit"] < errs["output fit"] < errs["value basis"]
