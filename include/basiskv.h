@@ -94,7 +94,9 @@ enum {
  * synchronises the stream, and returns BASISKV_E_DATA with nothing else
  * enqueued when one is violated (basiskv_last_error says which).  Without
  * it these values are not checked and a violation is undefined behaviour.
- * Debug mode synchronises, so it does not suit graph capture.
+ * Debug mode synchronises, so it does not suit graph capture.  The checks of
+ * calls made from several host threads run one at a time: the library holds
+ * one check flag per device.
  */
 
 enum { BASISKV_F32 = 0, BASISKV_BF16 = 1 };

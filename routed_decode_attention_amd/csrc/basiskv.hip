@@ -6,6 +6,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
+#include <mutex>
 
 
 #include "../../include/basiskv.h"
@@ -54,6 +55,9 @@ bkv::ValidateArgs validate_args(const bkv::Shape& s, const basiskv_cache* c) {
 
 int debug_check(bkv::ValidateArgs v, void* stream, const char* who) {
   if (!debug_on()) return BASISKV_OK;
+  // one flag per device: checks from several host threads take turns
+  static std::mutex mu;
+  const std::lock_guard<std::mutex> lock(mu);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipGetSymbolAddress(reinterpret_cast<void**>(&v.flag), HIP_SYMBOL(g_validate_flag));
   if (e == hipSuccess) e = bkv::launch_zero_u32(v.flag, 1, st);

@@ -144,3 +144,40 @@ def test_bad_selections(monkeypatch):
     with pytest.raises(rda.BasisKVError) as e:
         attend(s, n, phys)
     assert e.value.code == rda.E_DATA
+
+
+def test_checks_from_two_host_threads_do_not_cross(monkeypatch):
+    """Two host threads on their own streams, one with valid lengths and one
+    with a length past the cache, call the router in debug mode together:
+    every valid call succeeds and every invalid one returns BASISKV_E_DATA."""
+    import threading
+    import routed_decode_attention_amd as rda
+    monkeypatch.setenv("BASISKV_DEBUG", "1")
+    sc = _scenario()
+    g = _padded(gc.upload(sc, cache=True, W_ofT=sc.W_ofT))
+    bad = g.seq_lens.clone()
+    bad[2] = g.d.max_pages_per_seq * g.d.page_size + 1
+    torch.cuda.synchronize()
+    results = {"good": [], "bad": []}
+
+    def run(kind, lens):
+        st = torch.cuda.Stream()
+        sel = torch.zeros((sc.batch, 1, g.d.top_k), dtype=torch.int32, device="cuda")
+        n_sel = torch.zeros((sc.batch, 1), dtype=torch.int32, device="cuda")
+        scores = torch.zeros((sc.batch, 1, g.d.max_pages_per_seq), device="cuda")
+        torch.cuda.synchronize()
+        for _ in range(40):
+            try:
+                rda.basiskv_route(g.d, g.f, g.cache, lens, g.q, sel, n_sel, scores, stream=st)
+                results[kind].append(0)
+            except rda.BasisKVError as e:
+                results[kind].append(e.code)
+        st.synchronize()
+
+    threads = [threading.Thread(target=run, args=("good", g.seq_lens)), threading.Thread(target=run, args=("bad", bad))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert results["good"] == [0] * 40, results["good"]
+    assert results["bad"] == [rda.E_DATA] * 40, results["bad"]
