@@ -59,6 +59,12 @@ CASES = {
     "g8_mean_forced": (small("g8mf", 209, batch=2, n_q_heads=16, n_kv_heads=2, head_dim=128, page_size=32,
                              rank_v=48, rank_k=16, top_k=7, d_model=192, dtype=BF16, ctx=513, group_mean=1,
                              sink_pages=1, local_pages=1), [513, 200]),
+    # one page per pair (below the sorting network's range), and more pages
+    # than one wave's network keeps (the router's radix selection) at <= 512 pages
+    "g4_k1": (configs.get("llama8b_32k").with_(name="g4k1", cfg_id=210, batch=3, top_k=1, d_model=256),
+              [700, 64, 130]),
+    "g4_k100": (configs.get("llama8b_32k").with_(name="g4k100", cfg_id=211, batch=3, top_k=100, d_model=256),
+                [8000, 64, 6500]),
     "ragged_permuted": (configs.get("ragged_mix").with_(name="rg", cfg_id=206, batch=5,
                                                         length_range=(1, 3000), top_k=16,
                                                         d_model=256),
