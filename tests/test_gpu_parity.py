@@ -65,6 +65,10 @@ CASES = {
               [700, 64, 130]),
     "g4_k100": (configs.get("llama8b_32k").with_(name="g4k100", cfg_id=211, batch=3, top_k=100, d_model=256),
                 [8000, 64, 6500]),
+    # many pairs: 96 rows x 2 KV heads, lengths from the generator up to 600
+    "wide_b96": (small("wb96", 212, batch=96, n_q_heads=8, n_kv_heads=2, head_dim=128, page_size=64,
+                       rank_v=32, rank_k=16, top_k=4, d_model=256, dtype=BF16, ctx=600),
+                 [(37 * i * i + 11 * i) % 600 + 1 for i in range(96)]),
     "ragged_permuted": (configs.get("ragged_mix").with_(name="rg", cfg_id=206, batch=5,
                                                         length_range=(1, 3000), top_k=16,
                                                         d_model=256),
