@@ -379,9 +379,11 @@ AttendPlan plan_attend(const Shape& s) {
   if (ppw > 8) ppw = 8;
   const char* env = getenv("BASISKV_PAGES_PER_WAVE");
   if (env && atoi(env) > 0) ppw = atoi(env) < 32 ? atoi(env) : 32;
-  // Four waves per workgroup (eight halve the split partials but measured
-  // slower on the headline shape).
-  int waves = 4;
+  // Four waves per workgroup; eight when four would leave more splits than
+  // the merge requests in one round (their merge then costs a second round
+  // trip: at top_k 128, 16 splits of 8 waves measured faster than 32 of 4,
+  // while at top_k 64 the 16 splits of 4 waves are faster).
+  int waves = (s.top_k + 4 * ppw - 1) / (4 * ppw) > MERGE_CHUNK ? 8 : 4;
   const char* wenv = getenv("BASISKV_ATTEND_WAVES");
   if (wenv && (atoi(wenv) == 4 || atoi(wenv) == 8)) waves = atoi(wenv);
   AttendPlan p;
