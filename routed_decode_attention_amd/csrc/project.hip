@@ -102,7 +102,7 @@ constexpr int MP_WAVES = 8;
 constexpr int MP_ROWS = 2;
 constexpr int MP_WN = 1;  // 16-column tiles per wave
 constexpr int MP_COLS = 16 * MP_WN * MP_WAVES;
-constexpr int MP_KMAX = 256;  // contraction length held in registers and LDS
+constexpr int MP_KMAX = 512;  // contraction length held in registers and LDS
 
 __global__ __launch_bounds__(64 * MP_WAVES) void merge_project_kernel(MergeProjectArgs a) {
   extern __shared__ __attribute__((aligned(16))) float zs[];  // [16][kdim], rows past MP_ROWS zero
