@@ -36,6 +36,7 @@ def gc():
 
 
 def _decode_full(gc, name, sample):
+    print(f"[fullsize] {name}: rows {sample}", flush=True)
     import routed_decode_attention_amd as rda
     w = configs.get(name)
     B, H = w.batch, w.n_kv_heads
@@ -68,7 +69,7 @@ def _decode_full(gc, name, sample):
     rda.basiskv_decode_step(d, f, cache, pos, gc.dev(np.stack(kn), w.dtype), gc.dev(np.stack(vn), w.dtype),
                             seq_lens, q, sel, n_sel, scores, ws, out, z_out=z)
     torch.cuda.synchronize()
-    e2e_sel, e2e_out = gc.host(sel), gc.host(out).astype(np.float64)
+    e2e_sel, e2e_nsel, e2e_out = gc.host(sel), gc.host(n_sel), gc.host(out).astype(np.float64)
 
     # the oracle on the sampled sequences only (its own placement of their pages)
     sc = cases.make_scenario(w, rows=sample)
@@ -116,24 +117,30 @@ def _decode_full(gc, name, sample):
     for i, b in enumerate(sample):
         np.testing.assert_allclose(got[b], out_ref[i], rtol=2e-2, atol=2e-3)
         np.testing.assert_allclose(got_z[b], z_ref[i], rtol=2e-2, atol=2e-3)
-        # 3. end to end on the GPU's own cache, when its selection is the oracle's
-        if np.array_equal(e2e_sel[b], o_sel[i]):
-            np.testing.assert_allclose(e2e_out[b], out_ref[i], rtol=2e-2, atol=2e-3)
+    # 3. end to end on the GPU's own cache and selection: against the oracle
+    # re-run on that selection (its own cache), every sampled row
+    _, out_e2e = oracle.decode(sc.d, sc.W_ofT, sc.cache, sc.lengths, sc.q,
+                               np.ascontiguousarray(e2e_sel[sample]), np.ascontiguousarray(e2e_nsel[sample]))
+    for i, b in enumerate(sample):
+        np.testing.assert_allclose(e2e_out[b], out_e2e[i], rtol=2e-2, atol=2e-3)
+    same = sum(np.array_equal(e2e_sel[b], o_sel[i]) for i, b in enumerate(sample))
+    print(f"[fullsize] {name}: {len(sample)} sampled rows, {same} with the oracle's own selection", flush=True)
 
 
 def test_llama8b_share_32k_full(gc):
-    _decode_full(gc, "llama8b_32k", [0, 7, 15])
+    _decode_full(gc, "llama8b_32k", [0, 2, 5, 7, 9, 11, 13, 15])
 
 
 def test_llama70b_share_128k_full(gc):
-    _decode_full(gc, "llama70b_128k", [0, 31])
+    # the first and last rows and six between (eight of 32)
+    _decode_full(gc, "llama70b_128k", [0, 4, 9, 13, 18, 22, 27, 31])
 
 
 def test_ragged_mix_full(gc):
     w = configs.get("ragged_mix")
     lengths = synth.make_lengths(w)
-    # the shortest and the longest sequence, and one more
-    sample = sorted({int(np.argmin(lengths)), int(np.argmax(lengths)), 17})
+    # the shortest and the longest sequence, and six more across the batch
+    sample = sorted({int(np.argmin(lengths)), int(np.argmax(lengths)), 0, 9, 21, 34, 47, 63})
     _decode_full(gc, "ragged_mix", sample)
 
 
