@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define BASISKV_VERSION 2
+#define BASISKV_VERSION 3
 
 enum {
   BASISKV_OK = 0,
@@ -284,6 +284,28 @@ int basiskv_decode_step(const basiskv_dims *dims, const basiskv_factors *f,
                         const void *v_new, const int32_t *seq_lens, const void *q,
                         int32_t *sel, int32_t *n_sel, float *scores, void *ws, size_t ws_bytes,
                         float *z_out, float *out, void *stream);
+
+/*
+ * basiskv_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, allocation-free serving
+ * loops, harnesses that forbid hipMalloc).  Arguments and results as in
+ * basiskv_decode_step.  Its scratch (what basiskv_decode_step keeps in the
+ * workspace) is a file-scope device array of BASISKV_NOALLOC_SCRATCH_BYTES
+ * bytes that the library holds on each device it runs on until the process
+ * ends; dims whose workspace (basiskv_workspace_bytes(dims, 0)) exceeds it are
+ * rejected with BASISKV_E_WORKSPACE before anything is enqueued.  The call
+ * allocates nothing: it clears the router's counters in the array with a
+ * fill kernel, then runs basiskv_decode_step's kernels on it.  Every call on
+ * a device shares that device's array, which keeps the last call's contents:
+ * calls that overlap in time on one device (other streams or threads) race
+ * and their results are undefined.
+ */
+#define BASISKV_NOALLOC_SCRATCH_BYTES (4u << 20)
+int basiskv_decode_step_noalloc(const basiskv_dims *dims, const basiskv_factors *f,
+                                const basiskv_cache *cache, const int32_t *pos, const void *k_new,
+                                const void *v_new, const int32_t *seq_lens, const void *q,
+                                int32_t *sel, int32_t *n_sel, float *scores, float *z_out, float *out,
+                                void *stream);
 
 /*
  * Prefill chunk of one sequence: basiskv_write of tokens [start_pos,

@@ -29,7 +29,8 @@ EXPORTS = (
     "basiskv_write", "basiskv_append", "basiskv_route", "basiskv_append_route",
     "basiskv_workspace_bytes", "basiskv_workspace_init", "basiskv_attend", "basiskv_attend_splits",
     "basiskv_project",
-    "basiskv_decode", "basiskv_decode_step", "basiskv_prefill", "basiskv_stream_read",
+    "basiskv_decode", "basiskv_decode_step", "basiskv_decode_step_noalloc", "basiskv_prefill",
+    "basiskv_stream_read",
 )
 
 
@@ -74,6 +75,7 @@ def _load() -> C.CDLL:
         "basiskv_route": ([D, Fp, Cp, p, p, p, p, p, p, p, sz, p], C.c_int),
         "basiskv_append_route": ([D, Fp, Cp, p, p, p, p, p, p, p, p, p, p, sz, p], C.c_int),
         "basiskv_decode_step": ([D, Fp, Cp, p, p, p, p, p, p, p, p, p, sz, p, p, p], C.c_int),
+        "basiskv_decode_step_noalloc": ([D, Fp, Cp, p, p, p, p, p, p, p, p, p, p, p], C.c_int),
         "basiskv_workspace_bytes": ([D, i32], sz),
         "basiskv_workspace_init": ([D, p, sz, p], C.c_int),
         "basiskv_attend_splits": ([D], C.c_int),
@@ -298,6 +300,23 @@ def basiskv_decode_step(d: Dims, f: Factors, cache: Cache, pos, k_new, v_new, se
         _ptr(sel, "sel", torch.int32, pairs * d.top_k), _ptr(n_sel, "n_sel", torch.int32, pairs),
         _ptr(scores, "scores", torch.float32, pairs * d.max_pages_per_seq),
         _ptr(ws, "ws", torch.uint8), ws.numel(),
+        _ptr(z_out, "z_out", torch.float32, d.batch * d.n_q_heads * d.rank_v),
+        _ptr(out, "out", torch.float32, d.batch * d.d_model), _stream(stream)))
+
+
+def basiskv_decode_step_noalloc(d: Dims, f: Factors, cache: Cache, pos, k_new, v_new, seq_lens, q, sel, n_sel,
+                                scores, out, z_out=None, stream=None) -> None:
+    """basiskv_decode_step on the library's own per-device scratch (no workspace)."""
+    pairs = d.batch * d.n_kv_heads
+    need = d.batch * d.n_kv_heads * d.head_dim
+    fc, cc = f.c(d), cache.c(d)
+    _check(_lib.basiskv_decode_step_noalloc(
+        C.byref(d.c()), C.byref(fc), C.byref(cc), _ptr(pos, "pos", torch.int32, d.batch),
+        _ptr(k_new, "k_new", d.torch_dtype, need), _ptr(v_new, "v_new", d.torch_dtype, need),
+        _ptr(seq_lens, "seq_lens", torch.int32, d.batch),
+        _ptr(q, "q", d.torch_dtype, d.batch * d.n_q_heads * d.head_dim),
+        _ptr(sel, "sel", torch.int32, pairs * d.top_k), _ptr(n_sel, "n_sel", torch.int32, pairs),
+        _ptr(scores, "scores", torch.float32, pairs * d.max_pages_per_seq),
         _ptr(z_out, "z_out", torch.float32, d.batch * d.n_q_heads * d.rank_v),
         _ptr(out, "out", torch.float32, d.batch * d.d_model), _stream(stream)))
 

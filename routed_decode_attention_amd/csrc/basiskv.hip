@@ -322,6 +322,63 @@ int route_workspace(const bkv::Shape& s, void* ws, size_t ws_bytes) {
   return BASISKV_OK;
 }
 
+int check_step_args(const bkv::Shape& s, const basiskv_factors* f, const basiskv_cache* cache, const int32_t* pos,
+                    const void* k_new, const void* v_new, const int32_t* seq_lens, const void* q, int32_t* sel,
+                    int32_t* n_sel, float* scores, float* out, const char* who) {
+  (void)s;
+  if (!f || !f->B || !f->P || !f->R_enc || !f->R_dec || !f->W_ofT)
+    return fail(BASISKV_E_NULL, "%s: every factor is required", who);
+  int rc = check_cache(cache, true, true, true);
+  if (rc) return rc;
+  if (!pos || !k_new || !v_new || !seq_lens || !q || !sel || !n_sel || !scores || !out)
+    return fail(BASISKV_E_NULL, "%s: a required pointer is NULL", who);
+  return BASISKV_OK;
+}
+
+// The decode layer step on a checked workspace of ws_bytes >= ws_layout(s, 0).total.
+int decode_step(const bkv::Shape& s, const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
+                const int32_t* pos, const void* k_new, const void* v_new, const int32_t* seq_lens, const void* q,
+                int32_t* sel, int32_t* n_sel, float* scores, void* ws, size_t ws_bytes, float* z_out, float* out,
+                void* stream) {
+  const WsLayout L = ws_layout(s, 0);
+  int32_t* sel_phys = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.sel_phys);
+  bkv::ValidateArgs va = validate_args(s, cache);
+  va.seq_lens = seq_lens;
+  va.pos = pos;
+  int rc = debug_check(va, stream, "decode_step");
+  if (rc) return rc;
+  if ((rc = do_route(s, dims, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, stream, sel_phys,
+                     ws)))
+    return rc;
+  return attend_project(s, f, cache, seq_lens, q, sel, n_sel, sel_phys, ws, ws_bytes, z_out, out, stream);
+}
+
+// ---- scratch of the no-allocation decode step: one array per device, for
+// callers that cannot allocate (graph capture, allocation-free serving
+// loops).  In host code `scratch` is only a stand-in for the device symbol:
+// its device address is looked up once per device and used everywhere. ----
+static __device__ __align__(256) unsigned char scratch[BASISKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+
+int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[MAX_DEVICES] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "decode_step_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(BASISKV_E_UNSUPPORTED, "device %d (at most %d)", dev, MAX_DEVICES);
+  const std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "decode_step_noalloc: hipGetSymbolAddress(scratch)");
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return BASISKV_OK;
+}
+
 }  // namespace
 
 #pragma GCC visibility push(default)
@@ -513,23 +570,40 @@ int basiskv_decode_step(const basiskv_dims* dims, const basiskv_factors* f, cons
   bkv::Shape s;
   int rc = check_dims(dims, &s);
   if (rc) return rc;
-  if (!f || !f->B || !f->P || !f->R_enc || !f->R_dec || !f->W_ofT)
-    return fail(BASISKV_E_NULL, "decode_step: every factor is required");
-  if ((rc = check_cache(cache, true, true, true))) return rc;
-  if (!pos || !k_new || !v_new || !seq_lens || !q || !sel || !n_sel || !scores || !ws || !out)
-    return fail(BASISKV_E_NULL, "decode_step: a required pointer is NULL");
+  if ((rc = check_step_args(s, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, out, "decode_step")))
+    return rc;
+  if (!ws) return fail(BASISKV_E_NULL, "decode_step: ws is required");
   const WsLayout L = ws_layout(s, 0);
   if (ws_bytes < L.total)
     return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, decode needs %zu", ws_bytes, L.total);
-  int32_t* sel_phys = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.sel_phys);
-  bkv::ValidateArgs va = validate_args(s, cache);
-  va.seq_lens = seq_lens;
-  va.pos = pos;
-  if ((rc = debug_check(va, stream, "decode_step"))) return rc;
-  if ((rc = do_route(s, dims, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, stream, sel_phys,
-                     ws)))
+  return decode_step(s, dims, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, ws, ws_bytes, z_out,
+                     out, stream);
+}
+
+int basiskv_decode_step_noalloc(const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
+                                const int32_t* pos, const void* k_new, const void* v_new, const int32_t* seq_lens,
+                                const void* q, int32_t* sel, int32_t* n_sel, float* scores, float* z_out,
+                                float* out, void* stream) {
+  bkv::Shape s;
+  int rc = check_dims(dims, &s);
+  if (rc) return rc;
+  if ((rc = check_step_args(s, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, out,
+                            "decode_step_noalloc")))
     return rc;
-  return attend_project(s, f, cache, seq_lens, q, sel, n_sel, sel_phys, ws, ws_bytes, z_out, out, stream);
+  const WsLayout L = ws_layout(s, 0);
+  if (L.total > BASISKV_NOALLOC_SCRATCH_BYTES)
+    return fail(BASISKV_E_WORKSPACE, "decode_step_noalloc: these dims need %zu bytes of scratch, the library "
+                "holds %zu per device (use basiskv_decode_step with a workspace)", L.total,
+                (size_t)BASISKV_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  // the router's counters must start at zero; the array keeps whatever the
+  // last call on this device left, so they are cleared here (a fill kernel)
+  const hipError_t e = bkv::launch_zero_u32(static_cast<unsigned*>(ws), L.part_acc / sizeof(unsigned),
+                                            as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode_step_noalloc: clearing the counters");
+  return decode_step(s, dims, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, ws, L.total, z_out,
+                     out, stream);
 }
 
 int basiskv_stream_read(const void* src, size_t bytes, float* sink, int32_t n_sink, void* stream) {
