@@ -3,21 +3,28 @@
 One step is one decode layer step of the whole hot path over the batch:
 append the new token (cache writer), route (page scores + top-k), gathered
 exact-QK attention over the selected pages, and the folded output projection.
-The workload is the Llama-3-8B tensor-parallel-8 share at 32K context:
-16 sequences, 4 query heads on 1 KV head, head_dim 128, pages of 64, r=32,
-r_k=16, top-k 64 of 512 pages, d_model 4096, bf16 storage, synthetic seeded
-data.  The cache of one layer (177.5 MiB) fits in the 256 MB Infinity Cache,
-so the timed steps rotate over L distinct layer instances (a 32-layer
+The headline workload is the Llama-3-8B tensor-parallel-8 share at 32K
+context: 16 sequences, 4 query heads on 1 KV head, head_dim 128, pages of 64,
+r=32, r_k=16, top-k 64 of 512 pages, d_model 4096, bf16 storage, synthetic
+seeded data.  The cache of one layer (177.5 MiB) fits in the 256 MB Infinity
+Cache, so the timed steps rotate over L distinct layer instances (a 32-layer
 attention stack) and every step reads its cache from HBM.
 
-Prints one JSON line (rank 0, one GPU).  See --help.
+After the headline, the other workloads are measured as extra records, each
+after its own parity check against the oracle on sampled rows: the
+Llama-3-70B share at 128K context, the ragged serving mix, and the 8192-token
+causal prefill (TFLOP/s against the bf16 matrix-core peak).
+
+Prints one JSON line (one GPU).  See --help.
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
-import math
 import os
+import re
 import sys
 import time
 
@@ -28,118 +35,142 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "routed decode tokens/s per GPU + achieved HBM TB/s (% peak) at 32K ctx"
-HBM_PEAK_GBS = 8000.0
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix cores, published
+
+DESC = {
+    "llama8b_32k": "Llama-3-8B TP=8 share decode",
+    "llama70b_128k": "Llama-3-70B TP=8 share long-context decode",
+    "ragged_mix": "ragged paged serving mix decode (lengths U[1024, 65536], scattered pages)",
+    "prefill_8k": "causal prefill of one 8192-token prompt in chunks of 2048",
+}
+LAYERS = {"llama8b_32k": 32, "llama70b_128k": 8, "ragged_mix": 10}
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def measured_traffic():
-    """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary (FETCH_SIZE x its measured copy scale + WRITE_SIZE), or None when
-    the attention kernel's source has changed since the counters were taken."""
-    import hashlib
-    import re
-    path = os.path.join(ROOT, "profiles", "attend_llama8b_32k_counters.md")
-    src = os.path.join(ROOT, "routed_decode_attention_amd", "csrc", "attend.hip")
+def source_hash() -> str:
+    """sha256 over the library's kernel and host sources (a counter summary
+    is valid only for the sources it was taken with)."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "routed_decode_attention_amd", "csrc", "*"))):
+        h.update(os.path.basename(p).encode())
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter summary profiles/<kernel>_<workload>_counters.md
+    (FETCH_SIZE x the copy-calibrated scale + WRITE_SIZE), or None when there
+    is none or the sources have changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.md")
     try:
         text = open(path).read()
-        want = re.search(r"attend\.hip sha256: ([0-9a-f]{64})", text).group(1)
+        want = re.search(r"sources sha256: ([0-9a-f]{64})", text).group(1)
         traffic = int(re.search(r"traffic bytes per launch: (\d+)", text).group(1))
     except (OSError, AttributeError):
         return None
-    have = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    return traffic if have == want else None
+    return traffic if source_hash() == want else None
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=1024, help="timed layer steps (rounded up to whole sweeps)")
-    p.add_argument("--warmup", type=int, default=64)
+    p.add_argument("--steps", type=int, default=256, help="timed layer steps (exactly)")
+    p.add_argument("--warmup", type=int, default=16, help="untimed warm-up layer steps")
+    p.add_argument("--repeats", type=int, default=20, help="further timed replays of the steps, for the spread")
     p.add_argument("--workload", default="llama8b_32k")
-    p.add_argument("--layers", type=int, default=32, help="distinct cache instances rotated over")
+    p.add_argument("--layers", type=int, default=None, help="distinct cache instances rotated over")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the oracle's timed CPU work")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-extra", action="store_true", help="skip the extra workloads")
     p.add_argument("--kernel-launches", type=int, default=256, help="launches per kernel for per-kernel timing")
     p.add_argument("--top-k", type=int, default=None, help="pages selected per (sequence, KV head) instead of "
                    "the workload's (a top-k sweep; same data)")
     return p.parse_args()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU sharding is "
-                          "described in the design notes but not built", "n_gpus": args.gpus}))
-        sys.exit(2)
+class Decode:
+    """One decode workload on the GPU: L layer instances of its cache and
+    factors, written by the GPU writer (tokens [0, n-1)); a step appends
+    token n-1 and runs the whole path on one instance."""
 
+    def __init__(self, w, L, seed):
+        import torch
+        import routed_decode_attention_amd as rda
+        from tests import gpu_cases as gc
+        from workloads import synth
+        self.w, self.L = w, L
+        t0 = time.time()
+        B, H = w.batch, w.n_kv_heads
+        self.fac = fac = synth.make_factors(w, seed)
+        self.lengths = lengths = synth.make_lengths(w, seed)
+        pt, total = synth.make_page_table(w, lengths, seed)
+        self.d = d = gc.dims_of(w, B, total)
+        f = rda.Factors(B=gc.dev(fac.B, 0), P=gc.dev(fac.P, 0), R_enc=gc.dev(fac.R_enc, 0),
+                        R_dec=gc.dev(fac.R_dec, 0))
+        f.W_ofT = torch.empty((w.d_model, w.n_q_heads * w.rank_v), dtype=d.torch_dtype, device="cuda")
+        rda.basiskv_fold_output(d, f.B, gc.dev(fac.W_O, w.dtype), f.W_ofT)
+        page_table = torch.from_numpy(pt).cuda()
+        base = rda.Cache.empty(d, page_table)
+        kn, vn = [], []
+        for b in range(B):
+            n = int(lengths[b])
+            K, V = synth.make_sequence(w, fac, b, n, seed)
+            rda.basiskv_write(d, f, base, b, 0, gc.dev(K[:n - 1], w.dtype), gc.dev(V[:n - 1], w.dtype))
+            kn.append(K[n - 1])
+            vn.append(V[n - 1])
+            del K, V
+        torch.cuda.synchronize()
+        self.caches = [base] + [rda.Cache(K=base.K.clone(), Z=base.Z.clone(), S=base.S.clone(),
+                                          summ=base.summ.clone(), page_table=page_table) for _ in range(L - 1)]
+        # every layer instance has its own factors too (W_of alone is 1 MiB a layer), as in a model
+        self.facs = [f] + [rda.Factors(B=f.B.clone(), P=f.P.clone(), R_enc=f.R_enc.clone(), R_dec=f.R_dec.clone(),
+                                       W_ofT=f.W_ofT.clone()) for _ in range(L - 1)]
+        self.seq_lens = torch.from_numpy(lengths.astype(np.int32)).cuda()
+        self.pos = (self.seq_lens - 1).contiguous()
+        self.k_new = gc.dev(np.stack(kn), w.dtype)
+        self.v_new = gc.dev(np.stack(vn), w.dtype)
+        self.q_host = synth.make_queries(w, seed=seed)
+        self.q = gc.dev(self.q_host, w.dtype)
+        self.ws = rda.new_workspace(d)
+        self.sel = torch.zeros((B, H, w.top_k), dtype=torch.int32, device="cuda")
+        self.n_sel = torch.zeros((B, H), dtype=torch.int32, device="cuda")
+        self.scores = torch.zeros((B, H, w.max_pages_per_seq), dtype=torch.float32, device="cuda")
+        self.z = torch.zeros((B, w.n_q_heads, w.rank_v), dtype=torch.float32, device="cuda")
+        self.out = torch.zeros((B, w.d_model), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        mib = (base.K.numel() + base.Z.numel()) * 2 / 2 ** 20
+        log(f"{w.name}: {L} cache instances of {mib:.0f} MiB (K+Z), built in {time.time() - t0:.1f}s")
+
+    def step(self, i):
+        import routed_decode_attention_amd as rda
+        j = i % self.L
+        rda.basiskv_decode_step(self.d, self.facs[j], self.caches[j], self.pos, self.k_new, self.v_new,
+                                self.seq_lens, self.q, self.sel, self.n_sel, self.scores, self.ws, self.out,
+                                z_out=self.z)
+
+
+def time_steps(step, K, W, repeats, out):
+    """W eager warm-up steps, then a graph of exactly K steps (layer i mod L);
+    the graph's replay is checked against eager execution, timed once between
+    events on its stream (the rate), then `repeats` more times (the spread)."""
     import torch
-    import routed_decode_attention_amd as rda
-    from tests import gpu_cases as gc
-    from workloads import accounting, configs, synth
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    w = configs.get(args.workload)
-    if args.top_k is not None:
-        w = w.with_(top_k=args.top_k)
-    L = args.layers
-    B, H, G = w.batch, w.n_kv_heads, w.group
-    t0 = time.time()
-
-    # ---- inputs: seeded synthetic data of the workload's shape --------------------
-    fac = synth.make_factors(w, args.seed)
-    lengths = synth.make_lengths(w, args.seed)
-    pt, total = synth.make_page_table(w, lengths, args.seed)
-    seqs = [synth.make_sequence(w, fac, b, int(lengths[b]), args.seed) for b in range(B)]
-    q_host = synth.make_queries(w, seed=args.seed)
-    log(f"generated inputs in {time.time() - t0:.1f}s")
-
-    d = gc.dims_of(w, B, total)
-    f = rda.Factors(B=gc.dev(fac.B, 0), P=gc.dev(fac.P, 0), R_enc=gc.dev(fac.R_enc, 0),
-                    R_dec=gc.dev(fac.R_dec, 0))
-    f.W_ofT = torch.empty((w.d_model, w.n_q_heads * w.rank_v), dtype=d.torch_dtype, device="cuda")
-    rda.basiskv_fold_output(d, f.B, gc.dev(fac.W_O, w.dtype), f.W_ofT)
-    page_table = torch.from_numpy(pt).cuda()
-    base = rda.Cache.empty(d, page_table)
-    # the GPU writer fills tokens [0, n-1); the step appends token n-1
-    for b in range(B):
-        n = int(lengths[b]) - 1
-        rda.basiskv_write(d, f, base, b, 0, gc.dev(seqs[b][0][:n], w.dtype), gc.dev(seqs[b][1][:n], w.dtype))
-    torch.cuda.synchronize()
-    caches = [base] + [rda.Cache(K=base.K.clone(), Z=base.Z.clone(), S=base.S.clone(),
-                                 summ=base.summ.clone(), page_table=page_table) for _ in range(L - 1)]
-    # every layer instance has its own factors too (W_of alone is 1 MiB a layer), as in a model
-    facs = [f] + [rda.Factors(B=f.B.clone(), P=f.P.clone(), R_enc=f.R_enc.clone(), R_dec=f.R_dec.clone(),
-                              W_ofT=f.W_ofT.clone()) for _ in range(L - 1)]
-    seq_lens = torch.from_numpy(lengths.astype(np.int32)).cuda()
-    pos = (seq_lens - 1).contiguous()
-    k_new = gc.dev(np.stack([seqs[b][0][int(lengths[b]) - 1] for b in range(B)]), w.dtype)
-    v_new = gc.dev(np.stack([seqs[b][1][int(lengths[b]) - 1] for b in range(B)]), w.dtype)
-    q = gc.dev(q_host, w.dtype)
-    ws = rda.new_workspace(d)
-    sel = torch.zeros((B, H, w.top_k), dtype=torch.int32, device="cuda")
-    n_sel = torch.zeros((B, H), dtype=torch.int32, device="cuda")
-    scores = torch.zeros((B, H, w.max_pages_per_seq), dtype=torch.float32, device="cuda")
-    z = torch.zeros((B, w.n_q_heads, w.rank_v), dtype=torch.float32, device="cuda")
-    out = torch.zeros((B, w.d_model), dtype=torch.float32, device="cuda")
-    torch.cuda.synchronize()
-    log(f"built {L} cache instances of {base.K.numel() * 2 / 2**20 + base.Z.numel() * 2 / 2**20:.0f} MiB "
-        f"(K+Z) in {time.time() - t0:.1f}s")
-
-    def step(i):
-        rda.basiskv_decode_step(d, facs[i % L], caches[i % L], pos, k_new, v_new, seq_lens, q, sel, n_sel,
-                                scores, ws, out, z_out=z)
-
-    # the first step's selection and output, kept for the oracle comparison below
-    step(0)
-    torch.cuda.synchronize()
-    g_sel, g_nsel = gc.host(sel), gc.host(n_sel)
-
-    # ---- throughput: graph-captured sweeps of L layer steps -------------------------
-    for i in range(args.warmup):
+    for i in range(W):
         step(i)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
@@ -147,168 +178,400 @@ def main():
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         with torch.cuda.graph(graph, stream=s):
-            for i in range(L):
+            for i in range(K):
                 step(i)
     torch.cuda.current_stream().wait_stream(s)
-    # replayed sweep == eager sweep
+    torch.cuda.synchronize()
+    # replayed steps == eager steps
     graph.replay()
     torch.cuda.synchronize()
     g_out = out.clone()
-    for i in range(L):
+    for i in range(K):
         step(i)
     torch.cuda.synchronize()
     assert torch.equal(g_out, out), "graph replay differs from eager execution"
-
-    sweeps = max(1, math.ceil(args.steps / L))
-    steps = sweeps * L
-    for _ in range(2):
-        graph.replay()
+    graph.replay()
     torch.cuda.synchronize()
-    # an event after every sweep (events do not synchronise): the whole run
-    # gives the rate, the sweeps its spread
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(sweeps + 1)]
-    t_wall = time.time()
-    evs[0].record()
-    for k in range(sweeps):
-        graph.replay()
-        evs[k + 1].record()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
     torch.cuda.synchronize()
-    t_wall = time.time() - t_wall
-    ms = evs[0].elapsed_time(evs[-1])
-    sweep_us = np.array([evs[k].elapsed_time(evs[k + 1]) * 1e3 / L for k in range(sweeps)])
-    sweep_stats = {"sweeps": sweeps, "median_us_per_step": round(float(np.median(sweep_us)), 3),
-                   "p10_us_per_step": round(float(np.percentile(sweep_us, 10)), 3),
-                   "p90_us_per_step": round(float(np.percentile(sweep_us, 90)), 3)}
-    ms_per_step = ms / steps
-    tokens_per_s = B * steps / (ms / 1e3)
-    log(f"{steps} steps in {ms:.2f} ms (wall {t_wall * 1e3:.1f} ms): {ms_per_step * 1e3:.2f} us/step, "
-        f"{tokens_per_s / 1e6:.3f} M tokens/s per layer step")
-
-    # ---- per-kernel launch durations, live: n back-to-back launches between two
-    # events on the stream they run on, queued while the GPU spins so that no
-    # host gap enters (the mean agrees with rocprofv3's kernel durations) ----
-    def time_launches(fn, n):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ms = e0.elapsed_time(e1)
+    rep = []
+    for _ in range(repeats):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b.record()
         torch.cuda.synchronize()
-        torch.cuda._sleep(int(2.0e8))  # ~0.1 s of GPU spin while the launches are queued
-        e0.record()
-        for i in range(n):
-            fn(i)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / n  # us per launch
+        rep.append(a.elapsed_time(b) * 1e3 / K)
+    return ms, np.array(rep)
 
-    sel_phys = torch.zeros_like(sel)
-    rda.basiskv_route(d, f, caches[0], seq_lens, q, sel, n_sel, scores, sel_phys=sel_phys)
-    sel_fixed, nsel_fixed, phys_fixed = sel.clone(), n_sel.clone(), sel_phys.clone()
-    n_launch = args.kernel_launches
+
+def time_launches(fn, n):
+    """us per launch: n back-to-back launches between two events on the
+    stream they run on, queued while the GPU spins so that no host gap enters
+    (the mean agrees with rocprofv3's kernel durations)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.0e8))
+    e0.record()
+    for i in range(n):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def decode_kernels(st, launches):
+    """Live per-kernel launch durations of the decode step's three kernels and
+    their algorithmic bytes per launch.  Returns {name: record}."""
+    import torch
+    import routed_decode_attention_amd as rda
+    from tests import gpu_cases as gc
+    from workloads import accounting
+    w, L, d = st.w, st.L, st.d
+    sel_phys = torch.zeros_like(st.sel)
+    rda.basiskv_route(d, st.facs[0], st.caches[0], st.seq_lens, st.q, st.sel, st.n_sel, st.scores,
+                      sel_phys=sel_phys)
+    sel, nsel, phys = st.sel.clone(), st.n_sel.clone(), sel_phys.clone()
+    t_route = time_launches(lambda i: rda.basiskv_append_route(
+        d, st.facs[i % L], st.caches[i % L], st.pos, st.k_new, st.v_new, st.seq_lens, st.q, st.sel, st.n_sel,
+        st.scores, sel_phys=sel_phys), launches)
     # the attention kernel as the decode step runs it: physical page ids from
     # the router, split partials left in the workspace (their merge is fused
     # into the projection)
-    t_attend = time_launches(lambda i: rda.basiskv_attend(d, caches[i % L], seq_lens, q, sel_fixed,
-                                                          nsel_fixed, ws, None, sel_phys=phys_fixed), n_launch)
-    t_route = time_launches(lambda i: rda.basiskv_append_route(d, facs[i % L], caches[i % L], pos, k_new, v_new,
-                                                               seq_lens, q, sel, n_sel, scores,
-                                                               sel_phys=sel_phys, ws=ws), n_launch)
-    # attention + the merge fused into the projection, as the step runs them
-    t_decode = time_launches(lambda i: rda.basiskv_decode(d, facs[i % L], caches[i % L], seq_lens, q, sel_fixed, nsel_fixed,
-                                                          ws, out, sel_phys=phys_fixed), n_launch)
-    t_project = t_decode - t_attend
+    t_attend = time_launches(lambda i: rda.basiskv_attend(d, st.caches[i % L], st.seq_lens, st.q, sel, nsel,
+                                                          st.ws, None, sel_phys=phys), launches)
+    t_decode = time_launches(lambda i: rda.basiskv_decode(d, st.facs[i % L], st.caches[i % L], st.seq_lens, st.q,
+                                                          sel, nsel, st.ws, st.out, sel_phys=phys), launches)
+    sb = accounting.decode_step_bytes(w, st.lengths, selections=gc.host(sel), n_selected=gc.host(nsel))
+    b_route = sb.summaries + sb.page_table + sb.queries + sb.append + sb.factors
+    b_attend = sb.attend_kernel
+    b_mp = sb.w_of + sb.out
+    recs = {}
+    for name, kern, us, by in (("append_route", "route_kernel", t_route, b_route),
+                               ("attend", "attend_mfma_kernel", t_attend, b_attend),
+                               ("merge_project", "merge_project_kernel", t_decode - t_attend, b_mp)):
+        gbs = by / (us * 1e-6) / 1e9
+        recs[name] = {"kernel": kern, "avg_launch_us": round(us, 3), "bytes_per_launch": int(by),
+                      "GBs": round(gbs, 1), "frac_of_8TBs": round(gbs / HBM_PEAK_GBS, 4),
+                      "traffic": measured_traffic(kern, w.name), "launches": launches,
+                      "timing": "events" if name != "merge_project" else "events (decode minus attention)"}
+    return recs, sb
 
-    sb = accounting.decode_step_bytes(w, lengths, selections=gc.host(sel_fixed), n_selected=gc.host(nsel_fixed))
-    attend_bytes = sb.attend_kernel
-    att_us = float(t_attend)
-    achieved = attend_bytes / (att_us * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                "kernel": "attend_mfma_kernel<128,64,32>", "bytes_per_launch": attend_bytes,
-                "avg_launch_us": round(att_us, 3), "launches": n_launch}
-    # achievable read bandwidth: passes over 4 GiB (16x the Infinity Cache),
-    # the best of a few grid sizes
+
+def roofline_of(recs):
+    """The dominant kernel's roofline record (the one with the longest launch)."""
+    name = max(recs, key=lambda k: recs[k]["avg_launch_us"])
+    r = recs[name]
+    return {"bound": "hbm", "achieved": r["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": r["frac_of_8TBs"], "traffic": r["traffic"], "kernel": r["kernel"], "step_part": name,
+            "bytes_per_launch": r["bytes_per_launch"], "avg_launch_us": r["avg_launch_us"],
+            "launches": r["launches"]}
+
+
+def achievable_read():
+    """Achievable HBM read bandwidth: passes over 4 GiB (16x the Infinity
+    Cache), the best of a few grid sizes."""
+    import torch
+    import routed_decode_attention_amd as rda
     probe = torch.zeros(4 << 30, dtype=torch.uint8, device="cuda")
     best = (0.0, 0)
     for n_wg in (256, 512, 1024, 4096, 8192, 16384):
         sink = torch.empty(n_wg, dtype=torch.float32, device="cuda")
         t_read = time_launches(lambda i: rda.basiskv_stream_read(probe, sink), 8)
         best = max(best, (probe.numel() / (t_read * 1e-6) / 1e9, n_wg))
-    achievable = best[0]
     del probe
-    roofline["achievable_read_GBs"] = round(achievable, 1)
-    roofline["frac_of_achievable"] = round(achieved / achievable, 4)
-    log(f"achievable HBM read (stream probe, 4 GiB, best grid {best[1]} workgroups): {achievable:.0f} GB/s; "
-        f"the attention kernel reaches {100 * achieved / achievable:.1f}% of it")
-    step_tbs = sb.total / (ms_per_step * 1e-3) / 1e12
-    log(f"attend {att_us:.2f} us ({achieved:.0f} GB/s, {100 * achieved / HBM_PEAK_GBS:.1f}% of 8 TB/s); "
-        f"append+route {t_route:.2f} us, merge+project {t_project:.2f} us")
+    torch.cuda.empty_cache()
+    return best
 
-    # ---- CPU baseline: the oracle timed on the same workload; its outputs are
-    # also the parity reference of the GPU step ----------------------------------
-    cpu, parity = None, None
-    if not args.no_cpu:
-        import oracle
-        from tests import cases
-        cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
-        full = cases.make_scenario(w, seed=args.seed, upto_last=True)
-        kn = np.stack([full.K[b][int(lengths[b]) - 1:int(lengths[b])] for b in range(B)])
-        vn = np.stack([full.V[b][int(lengths[b]) - 1:int(lengths[b])] for b in range(B)])
-        res_o = {}
 
-        def ostep():
-            for b in range(B):
-                oracle.write(full.d, full.fac, full.cache, b, int(lengths[b]) - 1, kn[b], vn[b])
-            s_, n_, sc_ = oracle.route(full.d, full.fac, full.cache, full.lengths, full.q)
-            z_, o_ = oracle.decode(full.d, full.W_ofT, full.cache, full.lengths, full.q, s_, n_)
-            res_o.update(sel=s_, n_sel=n_, scores=sc_, out=o_)
+def sampled_parity(st, rows):
+    """The first decode step's outputs on sampled rows against the oracle (its
+    own writer and cache for those rows): selections valid top-k sets, and the
+    output against the oracle's decode over the GPU's selection."""
+    import torch
+    import oracle
+    from tests import cases
+    from tests import gpu_cases as gc
+    w = st.w
+    sc = cases.make_scenario(w, rows=rows)
+    o_sel, o_nsel, o_scores = oracle.route(sc.d, sc.fac, sc.cache, sc.lengths, sc.q)
+    st.step(0)
+    torch.cuda.synchronize()
+    g_sel, g_nsel, g_out = gc.host(st.sel), gc.host(st.n_sel), gc.host(st.out).astype(np.float64)
+    sel = np.ascontiguousarray(g_sel[rows])
+    nsel = np.ascontiguousarray(g_nsel[rows])
+    assert np.array_equal(nsel, o_nsel)
+    for i in range(len(rows)):
+        npg = -(-int(sc.lengths[i]) // w.page_size)
+        for g in range(w.n_kv_heads):
+            k = int(o_nsel[i, g])
+            cases.check_selection_valid(o_scores[i, g, :npg], sel[i, g, :k], k, 1e-5)
+    _, out_ref = oracle.decode(sc.d, sc.W_ofT, sc.cache, sc.lengths, sc.q, sel, nsel)
+    np.testing.assert_allclose(g_out[rows], out_ref, rtol=2e-2, atol=2e-3)
+    same = int(sum(np.array_equal(sel[i], o_sel[i]) for i in range(len(rows))))
+    return {"rows": [int(r) for r in rows], "max_abs_err": float(np.abs(g_out[rows] - out_ref).max()),
+            "selection_identical_rows": same,
+            "tolerance": "selection valid top-k up to 1e-5 relative swaps; out vs oracle on the GPU's "
+                         "selection, rtol 2e-2 atol 2e-3"}
 
-        reps, t_cpu = 0, 0.0
-        while t_cpu < args.cpu_seconds and reps < 100000:
+
+def run_decode(w, L, K, W, repeats, launches, seed, parity_rows):
+    st = Decode(w, L, seed)
+    parity = sampled_parity(st, parity_rows) if parity_rows else None
+    if parity:
+        log(f"{w.name}: parity ok on rows {parity['rows']} (max |out - oracle| {parity['max_abs_err']:.2e})")
+    ms, rep = time_steps(st.step, K, W, repeats, st.out)
+    recs, sb = decode_kernels(st, launches)
+    us = ms * 1e3 / K
+    B = w.batch
+    rec = {"tokens_per_s": round(B * K / (ms / 1e3), 1), "us_per_step": round(us, 3), "steps": K,
+           "layers_rotated": L, "algorithmic_bytes": sb.total,
+           "TB_per_s": round(sb.total / (us * 1e-6) / 1e12, 3),
+           "frac_of_8TBs": round(sb.total / (us * 1e-6) / 1e12 / 8.0, 4),
+           "spread": {"repeats": int(len(rep)), "median_us_per_step": round(float(np.median(rep)), 3),
+                      "p10_us_per_step": round(float(np.percentile(rep, 10)), 3),
+                      "p90_us_per_step": round(float(np.percentile(rep, 90)), 3)},
+           "kernels": recs, "roofline": roofline_of(recs), "parity": parity}
+    return st, rec
+
+
+def run_prefill(seed, repeats=5):
+    """The 8192-token prompt in chunks of 2048 (write, causal attention,
+    projection per chunk), after a parity check on sampled query rows."""
+    import torch
+    import oracle
+    import routed_decode_attention_amd as rda
+    from tests import gpu_cases as gc
+    from workloads import accounting, configs, synth
+    w = configs.get("prefill_8k")
+    n, chunk = w.ctx, w.prefill_chunk
+    fac = synth.make_factors(w, seed)
+    lengths = np.array([n], np.int32)
+    pt, total = synth.make_page_table(w, lengths, seed)
+    K, V = synth.make_sequence(w, fac, 0, n, seed)
+    qp = synth.make_queries(w, n_rows=n, seed=seed)
+    d = gc.dims_of(w, 1, total)
+    f = rda.Factors(B=gc.dev(fac.B, 0), P=gc.dev(fac.P, 0), R_enc=gc.dev(fac.R_enc, 0), R_dec=gc.dev(fac.R_dec, 0))
+    f.W_ofT = torch.empty((w.d_model, w.n_q_heads * w.rank_v), dtype=d.torch_dtype, device="cuda")
+    rda.basiskv_fold_output(d, f.B, gc.dev(fac.W_O, w.dtype), f.W_ofT)
+    cache = rda.Cache.empty(d, torch.from_numpy(pt))
+    ws = rda.new_workspace(d, chunk)
+    qd, kd, vd = gc.dev(qp, w.dtype), gc.dev(K, w.dtype), gc.dev(V, w.dtype)
+    z = torch.empty((n, w.n_q_heads, w.rank_v), device="cuda")
+    out = torch.empty((n, w.d_model), device="cuda")
+
+    def prompt():
+        for a in range(0, n, chunk):
+            rda.basiskv_prefill(d, f, cache, 0, a, qd[a:a + chunk], kd[a:a + chunk], vd[a:a + chunk], ws,
+                                out[a:a + chunk], z_out=z[a:a + chunk])
+
+    prompt()
+    torch.cuda.synchronize()
+    # parity on sampled query rows of every chunk
+    od = oracle.Dims.of(w, batch=1, num_pages=total)
+    ora = oracle.Cache(od, pt)
+    oracle.write(od, fac, ora, 0, 0, K, V)
+    W_ofT = oracle.fold(od, fac.B, fac.W_O)
+    rows = sorted(set(synth.sample_rows(n, 24, seed=5)) | {0, chunk - 1, chunk, n - 1})
+    _, out_ref = oracle.attend_causal(od, W_ofT, ora, 0, rows, qp[rows])
+    got = gc.host(out).astype(np.float64)[rows]
+    np.testing.assert_allclose(got, out_ref, rtol=2e-2, atol=2e-3)
+    log(f"prefill_8k: parity ok on {len(rows)} query rows (max |out - oracle| {np.abs(got - out_ref).max():.2e})")
+    # timing: whole prompts, then the writer and the projection alone
+    t = []
+    for _ in range(repeats + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        prompt()
+        e1.record()
+        torch.cuda.synchronize()
+        t.append(e0.elapsed_time(e1) * 1e3)
+    t = np.array(t[1:])
+    t_write = time_launches(lambda i: rda.basiskv_write(d, f, cache, 0, (i % 4) * chunk, kd[(i % 4) * chunk:(i % 4 + 1)
+                                                                                          * chunk],
+                                                        vd[(i % 4) * chunk:(i % 4 + 1) * chunk]), 8)
+    zf = z.view(n, -1)
+    t_proj = time_launches(lambda i: rda.basiskv_project(d, f, zf[(i % 4) * chunk:], chunk,
+                                                         out[(i % 4) * chunk:]), 8)
+    fl = [accounting.prefill_flops(w, a, chunk) for a in range(0, n, chunk)]
+    total_fl = sum(x["total"] for x in fl)
+    attn_fl = sum(x["attention"] for x in fl)
+    proj_fl = sum(x["projection"] for x in fl)
+    us = float(np.median(t))
+    t_attn = us - 4 * (t_write + t_proj)
+    rec = {"tokens_per_s": round(n / (us * 1e-6), 1), "us_per_prompt": round(us, 1),
+           "TFLOP_per_s": round(total_fl / (us * 1e-6) / 1e12, 1),
+           "frac_of_bf16_mfma_peak": round(total_fl / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+           "flops_per_prompt": int(total_fl),
+           "attention": {"us": round(t_attn, 1), "flops": int(attn_fl),
+                         "TFLOP_per_s": round(attn_fl / (t_attn * 1e-6) / 1e12, 1),
+                         "frac_of_bf16_mfma_peak": round(attn_fl / (t_attn * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+                         "timing": "prompt minus 4 x (writer + projection)"},
+           "projection": {"us_per_chunk": round(t_proj, 1), "flops_per_chunk": int(proj_fl // 4),
+                          "TFLOP_per_s": round(proj_fl / 4 / (t_proj * 1e-6) / 1e12, 1),
+                          "frac_of_bf16_mfma_peak": round(proj_fl / 4 / (t_proj * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS,
+                                                          4)},
+           "writer": {"us_per_chunk": round(t_write, 1)},
+           "repeats": repeats,
+           "parity": {"query_rows": len(rows), "max_abs_err": float(np.abs(got - out_ref).max()),
+                      "tolerance": "rtol 2e-2 atol 2e-3"}}
+    return rec
+
+
+def cpu_baseline(st, seconds, seed):
+    """The oracle's whole decode step (append + route + decode + project over
+    the batch) timed on the host: all threads for `seconds`, then one thread
+    for a third of that.  Its results are also the full-batch parity
+    reference of the GPU step."""
+    import oracle
+    from tests import cases
+    w, lengths, B = st.w, st.lengths, st.w.batch
+    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    full = cases.make_scenario(w, seed=seed, upto_last=True)
+    kn = np.stack([full.K[b][int(lengths[b]) - 1:int(lengths[b])] for b in range(B)])
+    vn = np.stack([full.V[b][int(lengths[b]) - 1:int(lengths[b])] for b in range(B)])
+    res = {}
+
+    def ostep():
+        for b in range(B):
+            oracle.write(full.d, full.fac, full.cache, b, int(lengths[b]) - 1, kn[b], vn[b])
+        s_, n_, sc_ = oracle.route(full.d, full.fac, full.cache, full.lengths, full.q)
+        _, o_ = oracle.decode(full.d, full.W_ofT, full.cache, full.lengths, full.q, s_, n_)
+        res.update(sel=s_, n_sel=n_, scores=sc_, out=o_)
+
+    def timed(bound):
+        reps, t = 0, 0.0
+        while t < bound and reps < 100000:
             t1 = time.perf_counter()
             ostep()
-            t_cpu += time.perf_counter() - t1
+            t += time.perf_counter() - t1
             reps += 1
-        cpu = {"value": round(B * reps / t_cpu, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-               "sample": f"{reps} full decode layer steps (append+route+decode+project, batch {B}) "
-                         f"of the same workload, {t_cpu:.1f} s",
-               "ms_per_step": round(t_cpu / reps * 1e3, 2)}
-        log(f"oracle: {cpu['value']} tokens/s on {cores} threads ({reps} steps)")
+        return reps, t
 
-        # parity of the GPU step against the oracle's, every row
-        for b in range(B):
-            k = int(res_o["n_sel"][b, 0])
-            assert int(g_nsel[b, 0]) == k
-            npg = -(-int(lengths[b]) // w.page_size)
-            cases.check_selection_valid(res_o["scores"][b, 0, :npg], g_sel[b, 0, :k], k, 1e-5)
-        rda.basiskv_decode(d, f, caches[0], seq_lens, q, torch.from_numpy(res_o["sel"]).cuda(),
-                           torch.from_numpy(res_o["n_sel"]).cuda(), ws, out, z_out=z)
+    oracle.set_threads(cores)
+    reps, t_cpu = timed(seconds)
+    oracle.set_threads(1)
+    reps1, t1 = timed(seconds / 3)
+    oracle.set_threads(cores)
+    cpu = {"value": round(B * reps / t_cpu, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": f"{reps} full decode layer steps (append+route+decode+project, batch {B}) of the same "
+                     f"workload, {t_cpu:.1f} s on {cores} threads; {reps1} steps, {t1:.1f} s on 1 thread",
+           "ms_per_step": round(t_cpu / reps * 1e3, 2), "cpu_model": cpu_model(),
+           "value_1thread": round(B * reps1 / t1, 1), "ms_per_step_1thread": round(t1 / reps1 * 1e3, 2)}
+    return cpu, full, res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the build has one GPU's share of "
+                          "the tensor-parallel layer and no collectives; how the path would shard is described "
+                          "in the design notes", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import routed_decode_attention_amd as rda
+    from tests import cases
+    from tests import gpu_cases as gc
+    from workloads import configs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = configs.get(args.workload)
+    if args.top_k is not None:
+        w = w.with_(top_k=args.top_k)
+    L = args.layers or LAYERS.get(w.name, 8)
+    B = w.batch
+
+    st, head = run_decode(w, L, args.steps, args.warmup, args.repeats, args.kernel_launches, args.seed,
+                          parity_rows=None)
+    log(f"{w.name}: {head['steps']} steps, {head['us_per_step']:.2f} us/step, "
+        f"{head['tokens_per_s'] / 1e6:.3f} M tokens/s per layer step; kernels (us): " +
+        ", ".join(f"{k} {v['avg_launch_us']:.2f}" for k, v in head["kernels"].items()))
+    best = achievable_read()
+    rf = head["roofline"]
+    rf["achievable_read_GBs"] = round(best[0], 1)
+    rf["frac_of_achievable"] = round(rf["achieved"] / best[0], 4)
+    log(f"achievable HBM read (stream probe, 4 GiB, best grid {best[1]} workgroups): {best[0]:.0f} GB/s; "
+        f"dominant kernel {rf['kernel']} ({rf['step_part']}) at {100 * rf['frac']:.1f}% of 8 TB/s")
+
+    # ---- CPU baseline; its outputs are the full-batch parity reference --------
+    cpu, parity = None, None
+    if not args.no_cpu:
+        cpu, full, res_o = cpu_baseline(st, args.cpu_seconds, args.seed)
+        log(f"oracle: {cpu['value']} tokens/s on {cpu['cores']} threads, {cpu['value_1thread']} on 1 "
+            f"({cpu['cpu_model']})")
+        st.step(0)
         torch.cuda.synchronize()
-        got = gc.host(out).astype(np.float64)
-        np.testing.assert_allclose(got, res_o["out"], rtol=2e-2, atol=2e-3)
+        g_sel, g_nsel = gc.host(st.sel), gc.host(st.n_sel)
+        assert np.array_equal(g_nsel, res_o["n_sel"])
+        for b in range(B):
+            for g in range(w.n_kv_heads):
+                k = int(res_o["n_sel"][b, g])
+                npg = -(-int(st.lengths[b]) // w.page_size)
+                cases.check_selection_valid(res_o["scores"][b, g, :npg], g_sel[b, g, :k], k, 1e-5)
+        import oracle
+        _, out_gsel = oracle.decode(full.d, full.W_ofT, full.cache, full.lengths, full.q, g_sel, g_nsel)
+        got = gc.host(st.out).astype(np.float64)
+        np.testing.assert_allclose(got, out_gsel, rtol=2e-2, atol=2e-3)
         same = int(sum(np.array_equal(g_sel[b], res_o["sel"][b]) for b in range(B)))
-        parity = {"rows": B, "max_abs_err": float(np.abs(got - res_o["out"]).max()),
+        parity = {"rows": B, "max_abs_err": float(np.abs(got - out_gsel).max()),
                   "selection_identical_rows": same,
-                  "tolerance": "selection valid top-k up to 1e-5 relative swaps; out rtol 2e-2 atol 2e-3"}
+                  "tolerance": "selection valid top-k up to 1e-5 relative swaps; out vs the oracle's decode over "
+                               "the GPU's selection, rtol 2e-2 atol 2e-3"}
         log(f"parity ok: max |out - oracle| = {parity['max_abs_err']:.2e}, identical selections {same}/{B}")
+    del st
+    torch.cuda.empty_cache()
+
+    # ---- extra workloads, each after its own parity check -------------------
+    extra = {}
+    if not args.no_extra and args.workload == "llama8b_32k" and args.top_k is None:
+        for name, rows in (("llama70b_128k", [0, 31]), ("ragged_mix", None)):
+            we = configs.get(name)
+            if rows is None:
+                from workloads import synth
+                ln = synth.make_lengths(we, args.seed)
+                rows = sorted({int(np.argmin(ln)), int(np.argmax(ln)), 17})
+            ste, rec = run_decode(we, LAYERS[name], 4 * LAYERS[name], 2 * LAYERS[name], 10,
+                                  min(args.kernel_launches, 64), args.seed, parity_rows=rows)
+            rec["workload"] = f"{name}: {DESC[name]}"
+            extra[name] = rec
+            log(f"{name}: {rec['us_per_step']:.2f} us/step, {rec['tokens_per_s'] / 1e6:.3f} M tokens/s, "
+                f"{100 * rec['frac_of_8TBs']:.1f}% of 8 TB/s; kernels (us): " +
+                ", ".join(f"{k} {v['avg_launch_us']:.2f}" for k, v in rec["kernels"].items()))
+            del ste
+            torch.cuda.empty_cache()
+        pre = run_prefill(args.seed)
+        pre["workload"] = f"prefill_8k: {DESC['prefill_8k']}"
+        extra["prefill_8k"] = pre
+        log(f"prefill_8k: {pre['us_per_prompt']:.0f} us per prompt, {pre['TFLOP_per_s']} TFLOP/s "
+            f"({100 * pre['frac_of_bf16_mfma_peak']:.1f}% of the bf16 matrix-core peak); attention "
+            f"{pre['attention']['TFLOP_per_s']} TFLOP/s")
 
     res = {
-        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": head["steps"], "warmup": args.warmup, "ms_per_step": round(head["us_per_step"] / 1e3, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: Llama-3-8B TP=8 share decode, batch {B}, {w.n_q_heads}q:{H}kv "
-                               f"heads, head_dim {w.head_dim}, context {w.ctx}, pages of {w.page_size}, "
+        "config": {"workload": f"{w.name}: {DESC.get(w.name, w.name)}, batch {B}, {w.n_q_heads}q:{w.n_kv_heads}kv "
+                               f"heads, head_dim {w.head_dim}, context {w.max_ctx}, pages of {w.page_size}, "
                                f"r={w.rank_v}, r_k={w.rank_k}, top-k {w.top_k}, d_model {w.d_model}; "
                                f"one step = one attention layer; {L} layer instances rotated",
-                   "global_batch": B, "seq_len": int(w.ctx), "parallelism": "single GPU",
+                   "global_batch": B, "seq_len": int(w.max_ctx), "parallelism": "single GPU",
                    "layers_rotated": L, "graph_captured": True},
-        "hbm_step": {"algorithmic_bytes": sb.total, "TB_per_s": round(step_tbs, 3),
-                     "frac_of_8TBs": round(step_tbs / 8.0, 4),
-                     "frac_of_achievable": round(step_tbs * 1e3 / achievable, 4)},
-        "sweep_spread": sweep_stats,
-        "kernels_us": {"append_route": round(float(t_route), 3),
-                       "attend": round(att_us, 3), "merge_project": round(float(t_project), 3)},
-        "roofline": roofline,
+        "hbm_step": {"algorithmic_bytes": head["algorithmic_bytes"], "TB_per_s": head["TB_per_s"],
+                     "frac_of_8TBs": head["frac_of_8TBs"],
+                     "frac_of_achievable": round(head["TB_per_s"] * 1e3 / best[0], 4)},
+        "sweep_spread": head["spread"],
+        "kernels": head["kernels"],
+        "roofline": rf,
         "cpu_baseline": cpu,
         "parity": parity,
+        "extra": extra,
     }
     print(json.dumps(res), flush=True)
 

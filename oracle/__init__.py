@@ -156,6 +156,12 @@ class Cache:
         return new
 
 
+def set_threads(n: int) -> None:
+    """OpenMP threads the oracle's loops use from now on (calling thread)."""
+    _load()
+    C.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+
+
 def round_bf16(x: float) -> int:
     return int(_load().ora_round_bf16(float(x)))
 
