@@ -226,40 +226,45 @@ def time_launches(fn, n):
 
 
 def decode_kernels(st, launches):
-    """Live per-kernel launch durations of the decode step's three kernels and
-    their algorithmic bytes per launch.  Returns {name: record}."""
+    """Live per-kernel launch durations of the decode step's three kernels
+    (append + scores, attention with its selection prologue, merge +
+    projection) and their algorithmic bytes per launch.  The scoring launch
+    is timed alone (the scores-only form of append_route); the projection as
+    the decode call minus the attention it starts with; the attention with
+    its selection as the whole step minus the other two.  Returns {name:
+    record}."""
     import torch
     import routed_decode_attention_amd as rda
     from tests import gpu_cases as gc
     from workloads import accounting
     w, L, d = st.w, st.L, st.d
-    sel_phys = torch.zeros_like(st.sel)
-    rda.basiskv_route(d, st.facs[0], st.caches[0], st.seq_lens, st.q, st.sel, st.n_sel, st.scores,
-                      sel_phys=sel_phys)
-    sel, nsel, phys = st.sel.clone(), st.n_sel.clone(), sel_phys.clone()
-    t_route = time_launches(lambda i: rda.basiskv_append_route(
-        d, st.facs[i % L], st.caches[i % L], st.pos, st.k_new, st.v_new, st.seq_lens, st.q, st.sel, st.n_sel,
-        st.scores, sel_phys=sel_phys), launches)
-    # the attention kernel as the decode step runs it: physical page ids from
-    # the router, split partials left in the workspace (their merge is fused
-    # into the projection)
+    st.step(0)
+    sel, nsel = st.sel.clone(), st.n_sel.clone()
+    phys = torch.zeros_like(sel)
+    rda.basiskv_route(d, st.facs[0], st.caches[0], st.seq_lens, st.q, torch.empty_like(sel),
+                      torch.empty_like(nsel), torch.empty_like(st.scores), sel_phys=phys)
+    t_step = time_launches(st.step, launches)
+    t_score = time_launches(lambda i: rda.basiskv_append_route(
+        d, st.facs[i % L], st.caches[i % L], st.pos, st.k_new, st.v_new, st.seq_lens, st.q, None, None,
+        st.scores), launches)
     t_attend = time_launches(lambda i: rda.basiskv_attend(d, st.caches[i % L], st.seq_lens, st.q, sel, nsel,
                                                           st.ws, None, sel_phys=phys), launches)
     t_decode = time_launches(lambda i: rda.basiskv_decode(d, st.facs[i % L], st.caches[i % L], st.seq_lens, st.q,
                                                           sel, nsel, st.ws, st.out, sel_phys=phys), launches)
+    t_mp = t_decode - t_attend
     sb = accounting.decode_step_bytes(w, st.lengths, selections=gc.host(sel), n_selected=gc.host(nsel))
-    b_route = sb.summaries + sb.page_table + sb.queries + sb.append + sb.factors
-    b_attend = sb.attend_kernel
-    b_mp = sb.w_of + sb.out
+    b_score = sb.summaries + sb.page_table + sb.queries + sb.append + sb.factors
     recs = {}
-    for name, kern, us, by in (("append_route", "route_kernel", t_route, b_route),
-                               ("attend", "attend_mfma_kernel", t_attend, b_attend),
-                               ("merge_project", "merge_project_kernel", t_decode - t_attend, b_mp)):
+    for name, kern, us, by, how in (
+            ("append_score", "score_kernel", t_score, b_score, "events"),
+            ("attend_select", "attend_mfma_kernel", t_step - t_score - t_mp, sb.attend_kernel,
+             "events (step minus scoring minus merge-projection)"),
+            ("merge_project", "merge_project_kernel", t_mp, sb.w_of + sb.out,
+             "events (decode minus attention)")):
         gbs = by / (us * 1e-6) / 1e9
         recs[name] = {"kernel": kern, "avg_launch_us": round(us, 3), "bytes_per_launch": int(by),
                       "GBs": round(gbs, 1), "frac_of_8TBs": round(gbs / HBM_PEAK_GBS, 4),
-                      "traffic": measured_traffic(kern, w.name), "launches": launches,
-                      "timing": "events" if name != "merge_project" else "events (decode minus attention)"}
+                      "traffic": measured_traffic(kern, w.name), "launches": launches, "timing": how}
     return recs, sb
 
 

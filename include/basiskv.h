@@ -191,40 +191,41 @@ int basiskv_append(const basiskv_dims *dims, const basiskv_factors *f,
  *   sel_phys (nullable) [batch][n_kv_heads][top_k] int32: page_table entries of
  *          sel (-1 padded), which basiskv_attend/decode may take to skip the
  *          page-table lookup.
- * ws (nullable): a workspace of basiskv_workspace_bytes(dims, 0) bytes or
- * more, whose arrival counters let several workgroups share the scoring of
- * one (sequence, KV head); NULL scores each (sequence, KV head) in one
- * workgroup.  Results are identical.
+ * sel and n_sel are both given or both NULL; NULL asks for the scores alone
+ * (sel_phys must then be NULL too).
+ * Two launches: the scores (a cluster of workgroups per (sequence, KV head),
+ * each scoring a few dozen pages), then the selection (a workgroup per
+ * (sequence, KV head)), which the scores-only form leaves out.  Needs no
+ * workspace.
  */
 int basiskv_route(const basiskv_dims *dims, const basiskv_factors *f,
                   const basiskv_cache *cache, const int32_t *seq_lens, const void *q,
-                  int32_t *sel, int32_t *n_sel, float *scores, int32_t *sel_phys, void *ws,
-                  size_t ws_bytes, void *stream);
+                  int32_t *sel, int32_t *n_sel, float *scores, int32_t *sel_phys, void *stream);
 
 /*
- * basiskv_append followed by basiskv_route, in one launch (the decode step
- * appends its token before attending).  Arguments as in the two calls; the
- * factors B, P, R_enc and R_dec are all required.
+ * basiskv_append followed by basiskv_route: the append is fused into the
+ * scoring launch (the decode step appends its token before attending).
+ * Arguments as in the two calls; the factors B, P, R_enc and R_dec are all
+ * required.
  */
 int basiskv_append_route(const basiskv_dims *dims, const basiskv_factors *f,
                          const basiskv_cache *cache, const int32_t *pos, const void *k_new,
                          const void *v_new, const int32_t *seq_lens, const void *q,
                          int32_t *sel, int32_t *n_sel, float *scores, int32_t *sel_phys,
-                         void *ws, size_t ws_bytes, void *stream);
+                         void *stream);
 
 /*
  * Device workspace, in bytes, that basiskv_attend/decode/decode_step (batch
- * rows) and basiskv_prefill (up to max_prefill_tokens queries) need.  Host function.
- * Its first 256 * ceil(12 * batch * n_kv_heads / 256) bytes are the router's
- * arrival counters: zero them once before the first call
- * (basiskv_workspace_init does), and every call leaves them zero.  The rest
- * carries the attention splits' partial results and intermediate latents
- * between the launches of one call and needs no initialisation.  Calls that
+ * rows) and basiskv_prefill (up to max_prefill_tokens queries) need.  Host
+ * function.  It carries the attention splits' partial results and
+ * intermediate latents between the launches of one call; nothing in it
+ * carries over between calls and it needs no initialisation.  Calls that
  * share a workspace must not overlap in time.
  */
 size_t basiskv_workspace_bytes(const basiskv_dims *dims, int32_t max_prefill_tokens);
 
-/* Zero-fill a workspace with a fill kernel (safe under graph capture). */
+/* Zero-fill a workspace with a fill kernel (safe under graph capture); not
+ * needed before use. */
 int basiskv_workspace_init(const basiskv_dims *dims, void *ws, size_t ws_bytes, void *stream);
 
 /*
@@ -239,8 +240,7 @@ int basiskv_workspace_init(const basiskv_dims *dims, void *ws, size_t ws_bytes, 
  * The selection of each (sequence, KV head) is processed in splits whose
  * partial results are combined afterwards (flash-decoding style).  z_out may
  * be NULL: the combination is then left to the caller and the partials stay
- * in ws right after the arrival counters (at byte 256 * ceil(12 * batch *
- * n_kv_heads / 256)), fp32 [batch*n_kv_heads][n_split][group][rank_v] partial
+ * at the start of ws, fp32 [batch*n_kv_heads][n_split][group][rank_v] partial
  * sums sum_t 2^(s_t*log2(e) - m) z~_t, followed (at the next 256-byte
  * boundary) by [batch*n_kv_heads][n_split][group][2] pairs (m, sum_t
  * 2^(s_t*log2(e) - m)) with m the split's max of s_t*log2(e) (-inf for an
@@ -275,9 +275,11 @@ int basiskv_decode(const basiskv_dims *dims, const basiskv_factors *f,
                    size_t ws_bytes, float *z_out, float *out, void *stream);
 
 /*
- * The whole decode layer step in three launches: append + route (one kernel),
- * attend, project.  sel, n_sel and scores are written as by basiskv_route;
- * z_out may be NULL.
+ * The whole decode layer step in three launches: the append fused with the
+ * page scores; the attention, whose workgroups each select their pair's
+ * top-k pages from the scores before reading the selected pages; the split
+ * merge fused with the projection.  sel, n_sel and scores are written as by
+ * basiskv_route; z_out may be NULL.
  */
 int basiskv_decode_step(const basiskv_dims *dims, const basiskv_factors *f,
                         const basiskv_cache *cache, const int32_t *pos, const void *k_new,
@@ -294,9 +296,10 @@ int basiskv_decode_step(const basiskv_dims *dims, const basiskv_factors *f,
  * bytes that the library holds on each device it runs on until the process
  * ends; dims whose workspace (basiskv_workspace_bytes(dims, 0)) exceeds it are
  * rejected with BASISKV_E_WORKSPACE before anything is enqueued.  The call
- * allocates nothing: it clears the router's counters in the array with a
- * fill kernel, then runs basiskv_decode_step's kernels on it.  Every call on
- * a device shares that device's array, which keeps the last call's contents:
+ * allocates nothing: it runs basiskv_decode_step's kernels on the array
+ * (every byte a call reads there it has written earlier in the same call, so
+ * nothing needs clearing).  Every call on a device shares that device's
+ * array, which keeps the last call's contents:
  * calls that overlap in time on one device (other streams or threads) race
  * and their results are undefined.
  */

@@ -35,6 +35,7 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "select.hpp"
 #include "split_merge.hpp"
 
 namespace bkv {
@@ -50,6 +51,83 @@ struct WaveState {  // LDS image of every wave's online-softmax state
 // ... and of their latent accumulators: dynamic LDS [waves][group][rank_v]
 __device__ __forceinline__ float& acc_at(float* acc, int w, int h, int r, int G, int R) {
   return acc[(w * G + h) * R + r];
+}
+
+// Dynamic LDS of a workgroup that selects its pages itself: after the
+// waves' latent accumulators, the pair's keys and page-table row, this
+// workgroup's share of the selection (logical and physical ids) and the
+// selection's scratch.
+struct SelLds {
+  SelectPages pg;
+  int32_t *pt, *mine_j, *mine_p;
+  SelectShared* sh;
+};
+__host__ __device__ inline size_t attend_acc_bytes(int waves, int G, int R) {
+  return ((size_t)waves * G * R * sizeof(float) + 15) & ~(size_t)15;
+}
+__host__ __device__ inline size_t sel_a16(size_t x) { return (x + 15) & ~(size_t)15; }
+// keys and page-table row (4 bytes a page each), bins and picks (a byte each)
+__host__ __device__ inline size_t sel_page_bytes(int maxp) { return 2 * sel_a16((size_t)maxp * 4) + sel_a16((size_t)maxp * 2); }
+__host__ __device__ inline size_t attend_sel_bytes(int maxp, int waves, int ppw) {
+  return sel_page_bytes(maxp) + sel_a16((size_t)waves * ppw * 8) + sizeof(SelectShared);
+}
+__device__ inline SelLds sel_lds(float* dyn, int waves, int G, int R, int maxp, int ppw) {
+  char* p = reinterpret_cast<char*>(dyn) + attend_acc_bytes(waves, G, R);
+  const size_t kb = sel_a16((size_t)maxp * 4);
+  SelLds L;
+  L.pg.keys = reinterpret_cast<uint32_t*>(p);
+  L.pt = reinterpret_cast<int32_t*>(p + kb);
+  L.pg.bin = reinterpret_cast<uint8_t*>(p + 2 * kb);
+  L.pg.pick = L.pg.bin + maxp;
+  L.mine_j = reinterpret_cast<int32_t*>(p + sel_page_bytes(maxp));
+  L.mine_p = L.mine_j + waves * ppw;
+  L.sh = reinterpret_cast<SelectShared*>(p + sel_page_bytes(maxp) + sel_a16((size_t)waves * ppw * 8));
+  return L;
+}
+
+// Selection in the prologue (the decode step): every workgroup of a pair
+// ranks the pair's pages from the router's scores itself (select.hpp) and
+// keeps the positions [split * waves * ppw, +waves * ppw) of the selection
+// in page order, with their physical ids; split 0 also writes the selection
+// (sel, n_sel) for the caller.  Returns the selection count.
+__device__ int select_prologue(const AttendArgs& a, int pair, int split, const SelLds& L) {
+  const int b = pair / a.s.n_kv_heads, ps = a.s.page_size, maxp = a.s.max_pages, top_k = a.s.top_k;
+  const int n = a.seq_lens[b];
+  const int npg = n > 0 ? min((n + ps - 1) / ps, maxp) : 0;
+  const int ks = min(top_k, npg);
+  const float* sc = a.scores + (size_t)pair * maxp;
+  const int32_t* pt = a.page_table + (size_t)b * maxp;
+  uint32_t kmax = 0u, kmin = 0xffffffffu;  // the range of the keys of pages that are not forced
+  for (int j = threadIdx.x; j < npg; j += blockDim.x) {
+    const uint32_t k = select_key(sc[j], j < a.sink_pages || j >= npg - a.local_pages);
+    L.pg.keys[j] = k;
+    L.pt[j] = pt[j];
+    if (k != 0xFFFFFFFFu) {
+      kmax = max(kmax, k);
+      kmin = min(kmin, k);
+    }
+  }
+  int32_t* sel = a.sel_out + (size_t)pair * top_k;
+  if (split == 0) {
+    for (int p = ks + threadIdx.x; p < top_k; p += blockDim.x) sel[p] = -1;
+    if (threadIdx.x == 0) a.n_sel_out[pair] = ks;
+  }
+  if (ks == 0) return 0;
+  key_range_publish(kmax, kmin, *L.sh);
+  topk_clear(*L.sh);
+  lds_barrier();
+  const TopK t = topk_find(L.pg, npg, ks, *L.sh);
+  const int base = split * a.waves * a.pages_per_wave, cnt = a.waves * a.pages_per_wave;
+  topk_emit(L.pg, npg, t, *L.sh, [&](int p, int j) {
+    if (p >= ks) return;  // (never: the selection keeps exactly ks pages)
+    if (split == 0) sel[p] = j;
+    if (p >= base && p < base + cnt) {
+      L.mine_j[p - base] = j;
+      L.mine_p[p - base] = L.pt[j];
+    }
+  });
+  lds_barrier();
+  return ks;
 }
 
 // Merge the workgroup's waves into one partial per query head: plain stores
@@ -183,7 +261,7 @@ struct OnlineSoftmax {
   }
 };
 
-template <int D, int PS, int R, bool PIPE>
+template <int D, int PS, int R, bool PIPE, bool SEL>
 __global__ __launch_bounds__(64 * ATTEND_WAVES_MAX) void attend_mfma_kernel(AttendArgs a) {
   constexpr int KS = D / 32, MT = R / 16;
   __shared__ WaveState st;
@@ -197,33 +275,44 @@ __global__ __launch_bounds__(64 * ATTEND_WAVES_MAX) void attend_mfma_kernel(Atte
   const int n = lane & 15, qd = lane >> 4;
 
   const int first = (split * a.waves + wave) * a.pages_per_wave;
-  // this wave's slice of the selection is read in the same round trip as the
-  // sequence length and the selection count (every slot < top_k is in bounds;
-  // slots past the count are masked below)
-  int my_j = 0, my_phys = 0;
-  const bool in_list = lane < a.pages_per_wave && first + lane < a.s.top_k;
-  if (in_list) {
-    const size_t at = (size_t)pair * a.s.top_k + first + lane;
-    my_j = a.sel[at];
-    if (a.sel_phys) my_phys = a.sel_phys[at];
-  }
   const int seq_len = a.seq_lens[b];
-  const int nsel = seq_len > 0 ? a.n_sel[pair] : 0;
-  const int np = max(0, min(first + a.pages_per_wave, nsel) - first);  // pages of this wave
-  // page ids and valid-token counts of this wave's pages, lane u holds page u
-  int my_cnt = 0;
-  if (lane < np) {
-    if (!a.sel_phys) my_phys = a.page_table[(size_t)b * a.s.max_pages + my_j];
-    my_cnt = min(PS, seq_len - my_j * PS);
-  } else {
-    my_phys = 0;
-  }
   bf16x8 qb[KS];
   {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
                          ((size_t)b * a.s.n_q_heads + g * G + (n < G ? n : 0)) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s) qb[s] = n < G ? load_bf16x8(qp + 8 * qd + 32 * s) : zero_bf16x8();
+  }
+  int my_j = 0, my_phys = 0, nsel;
+  if constexpr (SEL) {
+    // the queries stay in flight while the workgroup selects
+    const SelLds L = sel_lds(s_acc, a.waves, G, R, a.s.max_pages, a.pages_per_wave);
+    nsel = select_prologue(a, pair, split, L);
+    const int u = wave * a.pages_per_wave + lane;
+    if (lane < a.pages_per_wave && first + lane < nsel) {
+      my_j = L.mine_j[u];
+      my_phys = L.mine_p[u];
+    }
+  } else {
+    // this wave's slice of the selection is read in the same round trip as
+    // the sequence length and the selection count (every slot < top_k is in
+    // bounds; slots past the count are masked below)
+    const bool in_list = lane < a.pages_per_wave && first + lane < a.s.top_k;
+    if (in_list) {
+      const size_t at = (size_t)pair * a.s.top_k + first + lane;
+      my_j = a.sel[at];
+      if (a.sel_phys) my_phys = a.sel_phys[at];
+    }
+    nsel = seq_len > 0 ? a.n_sel[pair] : 0;
+  }
+  const int np = max(0, min(first + a.pages_per_wave, nsel) - first);  // pages of this wave
+  // page ids and valid-token counts of this wave's pages, lane u holds page u
+  int my_cnt = 0;
+  if (lane < np) {
+    if (!SEL && !a.sel_phys) my_phys = a.page_table[(size_t)b * a.s.max_pages + my_j];
+    my_cnt = min(PS, seq_len - my_j * PS);
+  } else {
+    my_phys = 0;
   }
   const uint16_t* Kp = static_cast<const uint16_t*>(a.K);
   const uint16_t* Zp = static_cast<const uint16_t*>(a.Z);
@@ -277,7 +366,7 @@ __global__ __launch_bounds__(64 * ATTEND_WAVES_MAX) void attend_mfma_kernel(Atte
 
 // Plain VALU kernel: one lane per token for q.k, one lane per latent channel
 // for the weighted sum.  Any storage dtype and any supported shape.
-template <typename T>
+template <typename T, bool SEL>
 __global__ __launch_bounds__(64 * ATTEND_WAVES_MAX) void attend_valu_kernel(AttendArgs a) {
   __shared__ WaveState st;
   extern __shared__ __attribute__((aligned(16))) float s_acc[];
@@ -299,7 +388,15 @@ __global__ __launch_bounds__(64 * ATTEND_WAVES_MAX) void attend_valu_kernel(Atte
   __syncthreads();
 
   const int seq_len = a.seq_lens[b];
-  const int nsel = seq_len > 0 ? a.n_sel[pair] : 0;
+  SelLds L{};
+  int nsel;
+  if constexpr (SEL) {
+    L = sel_lds(s_acc, a.waves, G, R, a.s.max_pages, a.pages_per_wave);
+    nsel = select_prologue(a, pair, split, L);
+  } else {
+    nsel = seq_len > 0 ? a.n_sel[pair] : 0;
+  }
+  const int base = split * a.waves * a.pages_per_wave;
   const int first = (split * a.waves + wave) * a.pages_per_wave;
   const int last = min(first + a.pages_per_wave, nsel);
 
@@ -310,8 +407,8 @@ __global__ __launch_bounds__(64 * ATTEND_WAVES_MAX) void attend_valu_kernel(Atte
     acc[h] = 0.f;
   }
   for (int i = first; i < last; ++i) {
-    const int j = a.sel[(size_t)pair * a.s.top_k + i];
-    const int phys = a.page_table[(size_t)b * a.s.max_pages + j];
+    const int j = SEL ? L.mine_j[i - base] : a.sel[(size_t)pair * a.s.top_k + i];
+    const int phys = SEL ? L.mine_p[i - base] : a.page_table[(size_t)b * a.s.max_pages + j];
     const int cnt = min(PS, seq_len - j * PS);
     const size_t kbase = ((size_t)phys * H + g) * PS * D;
     const size_t zbase = ((size_t)phys * H + g) * R * PS;
@@ -393,18 +490,20 @@ AttendPlan plan_attend(const Shape& s) {
   return p;
 }
 
-hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
+template <bool SEL>
+hipError_t launch_attend_t(const AttendArgs& a, hipStream_t st) {
   const int pairs = a.s.batch * a.s.n_kv_heads;
   const dim3 grid(pairs * a.n_wsplit), block(64 * a.waves);
-  const size_t lds = (size_t)a.waves * a.s.group * a.s.rank_v * sizeof(float);
+  size_t lds = attend_acc_bytes(a.waves, a.s.group, a.s.rank_v);
+  if (SEL) lds += attend_sel_bytes(a.s.max_pages, a.waves, a.pages_per_wave);
+  const void* kern = nullptr;
   if (attend_mfma_supported(a.s)) {
     const bool pipe = a.pages_per_wave > 1;
     const int key = a.s.head_dim * 10000 + a.s.page_size * 100 + a.s.rank_v;
     switch (key) {
 #define BKV_CASE(D, PS, R) \
-  case D * 10000 + PS * 100 + R:                                                                 \
-    if (pipe) hipLaunchKernelGGL((attend_mfma_kernel<D, PS, R, true>), grid, block, lds, st, a);   \
-    else hipLaunchKernelGGL((attend_mfma_kernel<D, PS, R, false>), grid, block, lds, st, a);       \
+  case D * 10000 + PS * 100 + R:                                                                          \
+    kern = pipe ? (const void*)attend_mfma_kernel<D, PS, R, true, SEL> : (const void*)attend_mfma_kernel<D, PS, R, false, SEL>; \
     break;
       BKV_CASE(128, 64, 16) BKV_CASE(128, 64, 32) BKV_CASE(128, 64, 48) BKV_CASE(128, 64, 64)
       BKV_CASE(128, 32, 16) BKV_CASE(128, 32, 32) BKV_CASE(128, 32, 48) BKV_CASE(128, 32, 64)
@@ -414,11 +513,25 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
       default: return hipErrorInvalidValue;
     }
   } else if (a.s.dtype == 0) {
-    hipLaunchKernelGGL((attend_valu_kernel<float>), grid, block, lds, st, a);
+    kern = (const void*)attend_valu_kernel<float, SEL>;
   } else {
-    hipLaunchKernelGGL((attend_valu_kernel<uint16_t>), grid, block, lds, st, a);
+    kern = (const void*)attend_valu_kernel<uint16_t, SEL>;
   }
-  return hipGetLastError();
+  hipError_t e = allow_lds(kern, lds);
+  if (e != hipSuccess) return e;
+  void* args[] = {const_cast<AttendArgs*>(&a)};
+  return hipLaunchKernel(kern, grid, block, args, lds, st);
+}
+
+hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
+  return a.scores ? launch_attend_t<true>(a, st) : launch_attend_t<false>(a, st);
+}
+
+size_t attend_lds_bytes(const Shape& s, bool select) {
+  const AttendPlan p = plan_attend(s);
+  size_t lds = attend_acc_bytes(p.waves, s.group, s.rank_v);
+  if (select) lds += attend_sel_bytes(s.max_pages, p.waves, p.pages_per_wave);
+  return lds;
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {

@@ -129,27 +129,23 @@ int check_dims(const basiskv_dims* d, bkv::Shape* s) {
 }
 
 struct WsLayout {
-  size_t arrive, part_acc, part_ml, z, sel_phys, route_keys, route_pages, total;
+  size_t part_acc, part_ml, z, total;
 };
 
-// Workspace: the router's arrival counters (kept zero between calls), then
-// split-K partials (latent sums, then max/denominator pairs), latent rows,
-// the router's physical page ids, then the router's partial selection.
+// Workspace: the attention splits' partials (latent sums, then max /
+// denominator pairs), then latent rows (decode batch or prefill chunk).
+// Nothing in it carries over between calls.
 WsLayout ws_layout(const bkv::Shape& s, int max_prefill_tokens) {
   const size_t pairs = (size_t)s.batch * s.n_kv_heads;
   const bkv::AttendPlan p = bkv::plan_attend(s);
   const size_t splits = pairs * p.n_wsplit * s.group;
   WsLayout L;
-  L.arrive = 0;
-  L.part_acc = align256(pairs * (sizeof(uint64_t) + sizeof(uint32_t)));
+  L.part_acc = 0;
   L.part_ml = L.part_acc + align256(splits * s.rank_v * sizeof(float));
   L.z = L.part_ml + align256(splits * 2 * sizeof(float));
   size_t rows = (size_t)s.batch;
   if (max_prefill_tokens > 0 && (size_t)max_prefill_tokens > rows) rows = max_prefill_tokens;
-  L.sel_phys = L.z + align256(rows * s.n_q_heads * s.rank_v * sizeof(float));
-  L.route_keys = L.sel_phys + align256(pairs * s.top_k * sizeof(int32_t));
-  L.route_pages = L.route_keys + align256(pairs * s.top_k * sizeof(uint32_t));
-  L.total = L.route_pages + align256(pairs * s.top_k * sizeof(int32_t));
+  L.total = L.z + align256(rows * s.n_q_heads * s.rank_v * sizeof(float));
   return L;
 }
 
@@ -165,9 +161,16 @@ inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 // Attention over the selection.  Several splits leave their partials in the
 // workspace; with `merge` they are combined into z_out right away, otherwise
 // the caller consumes them (the fused merge + projection).
+// Selection done by the attention kernel's prologue (the decode step).
+struct PrologueSelect {
+  const float* scores = nullptr;
+  int32_t *sel = nullptr, *n_sel = nullptr;
+  int sink_pages = 0, local_pages = 0;
+};
+
 int do_attend(const bkv::Shape& s, const basiskv_cache* cache, const int32_t* seq_lens, const void* q,
               const int32_t* sel, const int32_t* n_sel, void* ws, size_t ws_bytes, float* z_out,
-              void* stream, const int32_t* sel_phys, bool merge) {
+              void* stream, const int32_t* sel_phys, bool merge, const PrologueSelect& ps = PrologueSelect()) {
   const WsLayout L = ws_layout(s, 0);
   if (ws_bytes < L.z)
     return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, attention needs %zu", ws_bytes, L.z);
@@ -181,6 +184,11 @@ int do_attend(const bkv::Shape& s, const basiskv_cache* cache, const int32_t* se
   a.sel = sel;
   a.n_sel = n_sel;
   a.sel_phys = sel_phys;
+  a.scores = ps.scores;
+  a.sel_out = ps.sel;
+  a.n_sel_out = ps.n_sel;
+  a.sink_pages = ps.sink_pages;
+  a.local_pages = ps.local_pages;
   char* w = static_cast<char*>(ws);
   a.part_acc = reinterpret_cast<float*>(w + L.part_acc);
   a.part_ml = reinterpret_cast<float*>(w + L.part_ml);
@@ -222,12 +230,13 @@ int do_project(const bkv::Shape& s, const basiskv_factors* f, const float* z, in
 // Decode attention, the merge of its splits, then the output projection.
 int attend_project(const bkv::Shape& s, const basiskv_factors* f, const basiskv_cache* cache,
                    const int32_t* seq_lens, const void* q, const int32_t* sel, const int32_t* n_sel,
-                   const int32_t* sel_phys, void* ws, size_t ws_bytes, float* z_out, float* out, void* stream) {
+                   const int32_t* sel_phys, void* ws, size_t ws_bytes, float* z_out, float* out, void* stream,
+                   const PrologueSelect& psel = PrologueSelect()) {
   const WsLayout L = ws_layout(s, 0);
   float* z = z_out ? z_out : reinterpret_cast<float*>(static_cast<char*>(ws) + L.z);
   const bool fused = bkv::plan_attend(s).n_wsplit > 1 && bkv::merge_project_supported(s);
   // fused: the splits' partials stay in the workspace for the merge-projection
-  const int rc = do_attend(s, cache, seq_lens, q, sel, n_sel, ws, ws_bytes, z, stream, sel_phys, !fused);
+  const int rc = do_attend(s, cache, seq_lens, q, sel, n_sel, ws, ws_bytes, z, stream, sel_phys, !fused, psel);
   if (rc) return rc;
   if (!fused) return do_project(s, f, z, s.batch, out, stream);
   char* w = static_cast<char*>(ws);
@@ -268,13 +277,14 @@ int do_write(const bkv::Shape& s, const basiskv_factors* f, const basiskv_cache*
   return e == hipSuccess ? BASISKV_OK : hip_fail(e, "writer launch");
 }
 
+// Page scores (with the append fused when pos is given), then, when sel is
+// given, the top-k selection.
 int do_route(const bkv::Shape& s, const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
              const int32_t* pos, const void* k_new, const void* v_new, const int32_t* seq_lens, const void* q,
-             int32_t* sel, int32_t* n_sel, float* scores, void* stream, int32_t* sel_phys, void* ws) {
-  if (!bkv::route_fits(s, pos != nullptr))
-    return fail(BASISKV_E_UNSUPPORTED, "route: page table of %d pages with these factor sizes exceeds the LDS",
-                s.max_pages);
-  bkv::RouteArgs a;
+             int32_t* sel, int32_t* n_sel, float* scores, int32_t* sel_phys, void* stream) {
+  if (!bkv::score_fits(s, pos != nullptr))
+    return fail(BASISKV_E_UNSUPPORTED, "route: the appending workgroup's factors and page image exceed the LDS");
+  bkv::ScoreArgs a;
   a.s = s;
   a.B = f->B;
   a.P = f->P;
@@ -290,67 +300,62 @@ int do_route(const bkv::Shape& s, const basiskv_dims* dims, const basiskv_factor
   a.pos = pos;
   a.k_new = k_new;
   a.v_new = v_new;
-  a.sel = sel;
-  a.n_sel = n_sel;
-  a.sel_phys = sel_phys;
   a.scores = scores;
-  a.meet = nullptr;
-  a.arrive = nullptr;
-  a.part_keys = nullptr;
-  a.part_pages = nullptr;
-  a.sink_pages = dims->sink_pages;
-  a.local_pages = dims->local_pages;
   a.group_mean = dims->group_mean;
-  if (ws) {
-    const WsLayout L = ws_layout(s, 0);
-    char* w = static_cast<char*>(ws);
-    a.meet = reinterpret_cast<unsigned long long*>(w + L.arrive);
-    a.arrive = reinterpret_cast<uint32_t*>(w + L.arrive + (size_t)s.batch * s.n_kv_heads * sizeof(uint64_t));
-    a.part_keys = reinterpret_cast<uint32_t*>(w + L.route_keys);
-    a.part_pages = reinterpret_cast<int32_t*>(w + L.route_pages);
-  }
-  const hipError_t e = bkv::launch_route(a, as_stream(stream));
-  return e == hipSuccess ? BASISKV_OK : hip_fail(e, "route launch");
-}
-
-// An optional workspace for the router: large enough for a decode step.
-int route_workspace(const bkv::Shape& s, void* ws, size_t ws_bytes) {
-  if (!ws) return BASISKV_OK;
-  const WsLayout L = ws_layout(s, 0);
-  if (ws_bytes < L.total)
-    return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, the router needs %zu", ws_bytes, L.total);
-  return BASISKV_OK;
+  bkv::score_plan(s, pos != nullptr, &a.cluster, &a.per);
+  hipError_t e = bkv::launch_score(a, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "score launch");
+  if (!sel) return BASISKV_OK;
+  bkv::SelectArgs sa;
+  sa.s = s;
+  sa.scores = scores;
+  sa.page_table = cache->page_table;
+  sa.seq_lens = seq_lens;
+  sa.sel = sel;
+  sa.n_sel = n_sel;
+  sa.sel_phys = sel_phys;
+  sa.sink_pages = dims->sink_pages;
+  sa.local_pages = dims->local_pages;
+  e = bkv::launch_select(sa, as_stream(stream));
+  return e == hipSuccess ? BASISKV_OK : hip_fail(e, "selection launch");
 }
 
 int check_step_args(const bkv::Shape& s, const basiskv_factors* f, const basiskv_cache* cache, const int32_t* pos,
                     const void* k_new, const void* v_new, const int32_t* seq_lens, const void* q, int32_t* sel,
                     int32_t* n_sel, float* scores, float* out, const char* who) {
-  (void)s;
   if (!f || !f->B || !f->P || !f->R_enc || !f->R_dec || !f->W_ofT)
     return fail(BASISKV_E_NULL, "%s: every factor is required", who);
   int rc = check_cache(cache, true, true, true);
   if (rc) return rc;
   if (!pos || !k_new || !v_new || !seq_lens || !q || !sel || !n_sel || !scores || !out)
     return fail(BASISKV_E_NULL, "%s: a required pointer is NULL", who);
+  if (bkv::attend_lds_bytes(s, true) > 160 * 1024)
+    return fail(BASISKV_E_UNSUPPORTED, "%s: max_pages_per_seq %d needs more LDS than a CU has for the "
+                "attention's selection", who, s.max_pages);
   return BASISKV_OK;
 }
 
-// The decode layer step on a checked workspace of ws_bytes >= ws_layout(s, 0).total.
+// The decode layer step on a checked workspace of ws_bytes >= ws_layout(s, 0).total:
+// append + scores, then attention with the selection in its prologue, then
+// the split merge fused with the projection.
 int decode_step(const bkv::Shape& s, const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
                 const int32_t* pos, const void* k_new, const void* v_new, const int32_t* seq_lens, const void* q,
                 int32_t* sel, int32_t* n_sel, float* scores, void* ws, size_t ws_bytes, float* z_out, float* out,
                 void* stream) {
-  const WsLayout L = ws_layout(s, 0);
-  int32_t* sel_phys = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.sel_phys);
   bkv::ValidateArgs va = validate_args(s, cache);
   va.seq_lens = seq_lens;
   va.pos = pos;
   int rc = debug_check(va, stream, "decode_step");
   if (rc) return rc;
-  if ((rc = do_route(s, dims, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, stream, sel_phys,
-                     ws)))
+  if ((rc = do_route(s, dims, f, cache, pos, k_new, v_new, seq_lens, q, nullptr, nullptr, scores, nullptr, stream)))
     return rc;
-  return attend_project(s, f, cache, seq_lens, q, sel, n_sel, sel_phys, ws, ws_bytes, z_out, out, stream);
+  PrologueSelect psel;
+  psel.scores = scores;
+  psel.sel = sel;
+  psel.n_sel = n_sel;
+  psel.sink_pages = dims->sink_pages;
+  psel.local_pages = dims->local_pages;
+  return attend_project(s, f, cache, seq_lens, q, nullptr, nullptr, nullptr, ws, ws_bytes, z_out, out, stream, psel);
 }
 
 // ---- scratch of the no-allocation decode step: one array per device, for
@@ -450,40 +455,40 @@ int basiskv_append(const basiskv_dims* dims, const basiskv_factors* f, const bas
 
 int basiskv_route(const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
                   const int32_t* seq_lens, const void* q, int32_t* sel, int32_t* n_sel, float* scores,
-                  int32_t* sel_phys, void* ws, size_t ws_bytes, void* stream) {
+                  int32_t* sel_phys, void* stream) {
   bkv::Shape s;
   int rc = check_dims(dims, &s);
   if (rc) return rc;
   if (!f || !f->P || !f->R_dec) return fail(BASISKV_E_NULL, "route: factors P and R_dec required");
   if ((rc = check_cache(cache, false, false, false))) return rc;
-  if (!seq_lens || !q || !sel || !n_sel || !scores)
-    return fail(BASISKV_E_NULL, "route: seq_lens, q, sel, n_sel and scores are required");
-  if ((rc = route_workspace(s, ws, ws_bytes))) return rc;
+  if (!seq_lens || !q || !scores) return fail(BASISKV_E_NULL, "route: seq_lens, q and scores are required");
+  if (!sel != !n_sel || (!sel && sel_phys))
+    return fail(BASISKV_E_NULL, "route: sel and n_sel are both given or both NULL (then sel_phys is NULL)");
   bkv::ValidateArgs va = validate_args(s, cache);
   va.seq_lens = seq_lens;
   if ((rc = debug_check(va, stream, "route"))) return rc;
-  return do_route(s, dims, f, cache, nullptr, nullptr, nullptr, seq_lens, q, sel, n_sel, scores, stream, sel_phys,
-                  ws);
+  return do_route(s, dims, f, cache, nullptr, nullptr, nullptr, seq_lens, q, sel, n_sel, scores, sel_phys, stream);
 }
 
 int basiskv_append_route(const basiskv_dims* dims, const basiskv_factors* f, const basiskv_cache* cache,
                          const int32_t* pos, const void* k_new, const void* v_new, const int32_t* seq_lens,
                          const void* q, int32_t* sel, int32_t* n_sel, float* scores, int32_t* sel_phys,
-                         void* ws, size_t ws_bytes, void* stream) {
+                         void* stream) {
   bkv::Shape s;
   int rc = check_dims(dims, &s);
   if (rc) return rc;
   if (!f || !f->B || !f->P || !f->R_enc || !f->R_dec)
     return fail(BASISKV_E_NULL, "append_route: factors B, P, R_enc and R_dec required");
   if ((rc = check_cache(cache, true, true, true))) return rc;
-  if (!pos || !k_new || !v_new || !seq_lens || !q || !sel || !n_sel || !scores)
-    return fail(BASISKV_E_NULL, "append_route: pos, k_new, v_new, seq_lens, q, sel, n_sel, scores required");
-  if ((rc = route_workspace(s, ws, ws_bytes))) return rc;
+  if (!pos || !k_new || !v_new || !seq_lens || !q || !scores)
+    return fail(BASISKV_E_NULL, "append_route: pos, k_new, v_new, seq_lens, q and scores are required");
+  if (!sel != !n_sel || (!sel && sel_phys))
+    return fail(BASISKV_E_NULL, "append_route: sel and n_sel are both given or both NULL (then sel_phys is NULL)");
   bkv::ValidateArgs va = validate_args(s, cache);
   va.seq_lens = seq_lens;
   va.pos = pos;
   if ((rc = debug_check(va, stream, "append_route"))) return rc;
-  return do_route(s, dims, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, stream, sel_phys, ws);
+  return do_route(s, dims, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, sel_phys, stream);
 }
 
 size_t basiskv_workspace_bytes(const basiskv_dims* dims, int32_t max_prefill_tokens) {
@@ -595,13 +600,10 @@ int basiskv_decode_step_noalloc(const basiskv_dims* dims, const basiskv_factors*
     return fail(BASISKV_E_WORKSPACE, "decode_step_noalloc: these dims need %zu bytes of scratch, the library "
                 "holds %zu per device (use basiskv_decode_step with a workspace)", L.total,
                 (size_t)BASISKV_NOALLOC_SCRATCH_BYTES);
+  // nothing in the array needs to start at any value: every byte a call
+  // reads it has written before, in the same call
   void* ws = nullptr;
   if ((rc = scratch_address(&ws))) return rc;
-  // the router's counters must start at zero; the array keeps whatever the
-  // last call on this device left, so they are cleared here (a fill kernel)
-  const hipError_t e = bkv::launch_zero_u32(static_cast<unsigned*>(ws), L.part_acc / sizeof(unsigned),
-                                            as_stream(stream));
-  if (e != hipSuccess) return hip_fail(e, "decode_step_noalloc: clearing the counters");
   return decode_step(s, dims, f, cache, pos, k_new, v_new, seq_lens, q, sel, n_sel, scores, ws, L.total, z_out,
                      out, stream);
 }

@@ -160,6 +160,28 @@ __device__ __forceinline__ uint32_t float_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Intra-wave LDS hand-off: the wave's LDS writes are complete and visible to
+// its other lanes.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Workgroup barrier that orders LDS only: the wave's LDS accesses complete
+// before it, while its global loads stay in flight across it (a plain
+// __syncthreads also waits for every outstanding global load).  LDS filled
+// by direct global -> LDS copies may be read after it only when every wave
+// has waited for its copies (vmcnt) before arriving.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Wait until every global load (and direct global -> LDS copy) this wave
+// issued has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
 // Map a linear workgroup id so that consecutive "logical" ids owned by one
 // unit land on the same XCD: the hardware deals workgroups round-robin over
 // the 8 XCDs, so logical id L is placed at a physical id with the same

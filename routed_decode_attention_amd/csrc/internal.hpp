@@ -32,31 +32,35 @@ struct WriteArgs {
   int seq, start, n_tok;
 };
 
-struct RouteArgs {
+// Page scores (and the fused decode-step append): score_kernel.hpp.
+struct ScoreArgs {
   Shape s;
   const float *B, *P, *R_enc, *R_dec;
   void *K, *Z, *S;            // written only by the fused append
   float* summ;
   const int32_t *page_table, *seq_lens;
   const void* q;
-  const int32_t* pos;         // fused append of one token per row at pos[b]; nullptr: route only
+  const int32_t* pos;         // fused append of one token per row at pos[b]; nullptr: scores only
   const void *k_new, *v_new;
-  int32_t *sel, *n_sel;
-  int32_t* sel_phys;          // optional [batch][n_kv_heads][top_k]: physical ids of sel
-  float* scores;
-  unsigned long long* meet;   // [batch][n_kv_heads] zeroed words where the appending and selecting workgroups meet
-  uint32_t* arrive;           // [batch][n_kv_heads] zeroed arrival counters of the scorers; nullptr: one
-                              //   workgroup per pair
-  uint32_t* part_keys;        // [batch][n_kv_heads][top_k] a cluster's selection without the appended page
-  int32_t* part_pages;        //   (keys and pages), handed to whichever finishes the selection
-  int sink_pages, local_pages;  // pages always kept at either end of a sequence (0, 0: plain top-k)
-  int group_mean;               // a page's score over the group's query heads: 0 max, 1 mean
+  float* scores;              // [batch][n_kv_heads][max_pages]
+  int group_mean;             // a page's score over the group's query heads: 0 max, 1 mean
+  int cluster;                // workgroups per (sequence, KV head): [appender] + scorers
+  int per;                    // pages per scoring workgroup (<= 256)
 };
 
-// Workgroups per (sequence, KV head) of the router: one for the append (when
-// fused) plus enough to give each scoring one at most 512 pages; 1 without
-// arrival counters or for at most 128 pages.
-int route_cluster(const Shape& s, bool append, bool counters);
+// Workgroups per (sequence, KV head) and pages per scoring workgroup.
+void score_plan(const Shape& s, bool append, int* cluster, int* per);
+bool score_fits(const Shape& s, bool append);  // the appending workgroup's LDS fits one CU
+
+// Top-k selection over the scores: select.hip (and the attention prologue).
+struct SelectArgs {
+  Shape s;
+  const float* scores;
+  const int32_t *page_table, *seq_lens;
+  int32_t *sel, *n_sel;
+  int32_t* sel_phys;          // optional: page_table entries of sel
+  int sink_pages, local_pages;  // pages always kept at either end of a sequence (0, 0: plain top-k)
+};
 
 struct AttendArgs {
   Shape s;
@@ -65,6 +69,11 @@ struct AttendArgs {
   const void* q;
   const int32_t *sel, *n_sel;
   const int32_t* sel_phys;  // physical ids of sel (nullptr: looked up in page_table)
+  // selection in the prologue (scores != nullptr): every workgroup selects
+  // its pair's pages from the scores; split 0 writes sel / n_sel (outputs)
+  const float* scores;
+  int32_t *sel_out, *n_sel_out;
+  int sink_pages, local_pages;
   float* part_acc;          // [pairs][n_wsplit][group][rank_v]  split partial sums
   float* part_ml;           // [pairs][n_wsplit][group][2]       split (max, denominator)
   float* z_out;             // [batch][n_q_heads][rank_v], written directly when n_wsplit == 1
@@ -120,20 +129,18 @@ struct AttendPlan {
   int pages_per_wave, n_wsplit, waves;
 };
 AttendPlan plan_attend(const Shape& s);
+size_t attend_lds_bytes(const Shape& s, bool select);  // dynamic LDS of the attention kernel
 
 bool attend_mfma_supported(const Shape& s);
-bool route_fits(const Shape& s, bool append);  // the router's LDS fits one CU
 bool project_mfma_supported(int kdim, int n, int dtype);
 bool prefill_mfma_supported(const Shape& s);
 
 hipError_t launch_fold(const Shape& s, const float* B, const void* W_O, void* W_ofT, hipStream_t st);
 hipError_t launch_write(const WriteArgs& a, hipStream_t st);
-hipError_t launch_route(const RouteArgs& a, hipStream_t st);
-// the router's kernels by storage dtype and fusion with the append
-hipError_t launch_route_f32(const RouteArgs& a, hipStream_t st);
-hipError_t launch_route_f32_append(const RouteArgs& a, hipStream_t st);
-hipError_t launch_route_bf16(const RouteArgs& a, hipStream_t st);
-hipError_t launch_route_bf16_append(const RouteArgs& a, hipStream_t st);
+hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
+hipError_t launch_score_f32(const ScoreArgs& a, hipStream_t st);   // by storage dtype
+hipError_t launch_score_bf16(const ScoreArgs& a, hipStream_t st);
+hipError_t launch_select(const SelectArgs& a, hipStream_t st);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
 bool merge_project_supported(const Shape& s);

@@ -5,10 +5,10 @@
 // the router reads per-page sums of the stored z~ and s~).
 //
 // Everything here is executed by one whole wave (64 lanes) per token.  A
-// matrix-vector product spreads its outputs over lanes in groups of four
-// (one 16-byte LDS read per row) and its rows over lane slices; each slice
-// accumulates its rows in order and the slices are combined by an xor tree,
-// so the summation order is fixed by the shapes alone.
+// matrix-vector product puts its outputs on lanes and its rows on lane
+// slices; each slice accumulates its rows in order and the slices are
+// combined by an xor tree, so the summation order is fixed by the shapes
+// alone.
 #pragma once
 
 #include "common.hpp"
@@ -25,22 +25,6 @@ __device__ __forceinline__ void dma16(const void* src, void* dst) {
   __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)dst, 16, 0, 0);
 }
 
-// Intra-wave LDS hand-off: the wave's LDS writes are complete and visible to
-// its other lanes.
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
-
-// Workgroup barrier that orders LDS only: the wave's LDS accesses complete
-// before it, while its global loads stay in flight across it (a plain
-// __syncthreads also waits for every outstanding global load).  Not for
-// handing off LDS written by direct global -> LDS copies.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // LDS layout of the factor P (and R_dec): row x holds D floats whose 16-byte
 // granules are rotated by x, so lanes reading the same column of different
@@ -139,111 +123,109 @@ __device__ __forceinline__ void xor_tree(f32x4& a, int lane) {
 __device__ __forceinline__ float lds_elem(const float* p, int i) { return p[i]; }
 __device__ __forceinline__ float lds_elem(const uint16_t* p, int i) { return bf16_to_f32(p[i]); }
 
-// acc[k] += x[i] * M[i][k] for i < ROWS in order (M rows nc floats apart).
-template <int ROWS, typename X>
-__device__ __forceinline__ void rows_fma(const X* x, const float* M, int nc, f32x4& acc) {
-  if constexpr (ROWS > 16) {  // at most 16 rows of operands in flight
-    rows_fma<16>(x, M, nc, acc);
-    rows_fma<ROWS - 16>(x + 16, M + (size_t)16 * nc, nc, acc);
-    return;
-  }
-  float xv[ROWS];
-  f32x4 mv[ROWS];
-#pragma unroll
-  for (int i = 0; i < ROWS; ++i) {
-    xv[i] = lds_elem(x, i);
-    mv[i] = *reinterpret_cast<const f32x4*>(M + (size_t)i * nc);
-  }
-#pragma unroll
-  for (int i = 0; i < ROWS; ++i)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) acc[k] = fmaf(xv[i], mv[i][k], acc[k]);
+// Four consecutive LDS elements (storage dtype or fp32) as fp32; p 8-byte
+// (bf16) or 16-byte (fp32) aligned.
+__device__ __forceinline__ f32x4 lds_f4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 lds_f4(const uint16_t* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+               __uint_as_float(w.y & 0xffff0000u)};
 }
 
-// A token's three products are split over CW "virtual waves" of 64 lanes,
-// each taking a fixed 1/CW of the contraction; their partials are combined
-// in virtual-wave order starting from 0.  The router runs the CW virtual
-// waves as its CW real waves at once (partials through LDS); the chunk
-// writer runs them in turn on one wave.  The same additions happen in the
-// same order, so both produce the same bits.
-constexpr int CW = 8;
+// A token's three products are each split into TP fixed parts of their
+// contraction, combined in part order (part 0, then + part 1, + part 2,
+// + part 3).  The decode-step append computes the parts on TP waves at once;
+// the chunk writer computes them in turn on one wave.  The same additions
+// happen in the same order, so both store the same bits.
+constexpr int TP = 4;
 
-// Partial of virtual wave w for out[c] = sum_i x[i] M[i][c] (nc % 4 == 0,
-// nc <= 64; x [D], M row-major [D][nc], both in LDS): rows
-// [w D/CW, (w+1) D/CW).  Lane layout: output group g = lane % GP (GP = nc/4
-// rounded up to a power of two), slice s = lane / GP of RS consecutive rows
-// (S slices; lanes of later slices contribute 0), slices combined by the xor
-// tree.  Returns whether this lane holds outputs 4g..4g+3 in acc.
+// Part p of out[c] = sum_i x[i] M[i][c], c < nc (x [D], M row-major [D][nc],
+// in LDS; nc a multiple of 4): rows [p D/TP, (p+1) D/TP) on one wave.  Lane
+// = g + GP s: outputs 4g..4g+3 (GP the power of two >= nc/4) over the s-th of
+// S runs of consecutive rows (accumulated in row order), the runs added by
+// the xor tree over the lane bits >= log2(GP); lanes of runs >= S add zeros.
+// Lanes g < nc/4 of run 0 return the part's outputs 4g..4g+3.
 template <int D, int GP, typename X>
-__device__ __forceinline__ bool part_matvec_gp(const X* x, const float* M, int nc, int w, int lane, f32x4& acc,
-                                               int& g) {
-  constexpr int RW = D / CW, S = (64 / GP) < RW ? 64 / GP : RW, RS = RW / S;
-  const int G4 = nc >> 2;
-  g = lane & (GP - 1);
-  const int s = lane / GP;
-  const int r0 = w * RW + (s < S ? s : 0) * RS;
-  acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  // lanes past the last output group read group 0 and are discarded
-  rows_fma<RS>(x + r0, M + (size_t)r0 * nc + 4 * (g < G4 ? g : 0), nc, acc);
-  if (s >= S) acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  xor_tree<GP>(acc, lane);
-  return s == 0 && g < G4;
-}
-
-template <int D, typename X>
-__device__ __forceinline__ bool part_matvec(const X* x, const float* M, int nc, int w, int lane, f32x4& acc,
-                                            int& g) {
-  const int G4 = nc >> 2;
-  switch (G4 <= 1 ? 1 : 1 << (32 - __builtin_clz(G4 - 1))) {
-    case 1: return part_matvec_gp<D, 1>(x, M, nc, w, lane, acc, g);
-    case 2: return part_matvec_gp<D, 2>(x, M, nc, w, lane, acc, g);
-    case 4: return part_matvec_gp<D, 4>(x, M, nc, w, lane, acc, g);
-    case 8: return part_matvec_gp<D, 8>(x, M, nc, w, lane, acc, g);
-    default: return part_matvec_gp<D, 16>(x, M, nc, w, lane, acc, g);
-  }
-}
-
-// acc[q] += zt[r] * P[r][4 gi + q] over ROWS rows from r0, P rotated.
-template <int D, int ROWS>
-__device__ __forceinline__ void remainder_rows(const float* zt, const float* P, int r0, int gi, f32x4& acc) {
-  float zv[ROWS];
-  f32x4 pv[ROWS];
-#pragma unroll
-  for (int i = 0; i < ROWS; ++i) {
-    zv[i] = zt[r0 + i];
-    pv[i] = *reinterpret_cast<const f32x4*>(P + (r0 + i) * D + rot_granule(r0 + i, gi, D) * 4);
-  }
-#pragma unroll
-  for (int i = 0; i < ROWS; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc[q] = fmaf(zv[i], pv[i][q], acc[q]);
-}
-
-// Partial of virtual wave w for kh[i] = sum_r zt[r] P[r][i], i < D (P in the
-// rotated layout, R a multiple of 16): latent rows [w R/CW, (w+1) R/CW).
-// Lane layout: column group gi = lane % (D/4), slice lane / (D/4) of RS rows
-// (S slices: the largest power of two <= 256/D dividing R/CW; lanes of later
-// slices contribute 0), slices combined by the xor tree.  Lanes of slice 0
-// hold kh[4gi .. 4gi+3].
-template <int D>
-__device__ __forceinline__ f32x4 part_remainder(const float* zt, const float* P, int R, int w, int lane) {
-  constexpr int GD = D / 4, SL = 64 / GD;
-  const int RW = R / CW;
-  int S = SL;
-  while (RW % S) S >>= 1;
-  const int RS = RW / S;
-  const int gi = lane % GD, sr = lane / GD;
-  const int r0 = w * RW + (sr < S ? sr : 0) * RS;
+__device__ __forceinline__ f32x4 part_dot(const X* x, const float* M, int nc, int p, int lane) {
+  constexpr int ROWS = D / TP;
+  constexpr int S = (64 / GP) < (ROWS / 4) ? (64 / GP) : (ROWS / 4);
+  constexpr int TS = ROWS / S;
+  static_assert(TS % 4 == 0, "rows per run in fours");
+  const int g = lane & (GP - 1), s = lane / GP;
+  const int gg = 4 * g < nc ? g : 0;  // lanes past the outputs repeat group 0, unused
+  const int r0 = p * ROWS + (s < S ? s : 0) * TS;
+  const X* xs = x + r0;
+  const float* Ms = M + (size_t)r0 * nc + 4 * gg;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  switch (RS) {
-    case 1: remainder_rows<D, 1>(zt, P, r0, gi, acc); break;
-    case 2: remainder_rows<D, 2>(zt, P, r0, gi, acc); break;
-    case 3: remainder_rows<D, 3>(zt, P, r0, gi, acc); break;
-    default: remainder_rows<D, 4>(zt, P, r0, gi, acc); break;
+#pragma unroll
+  for (int i0 = 0; i0 < TS; i0 += 4) {
+    const f32x4 x4 = lds_f4(xs + i0);
+    f32x4 m[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m[e] = *reinterpret_cast<const f32x4*>(Ms + (size_t)(i0 + e) * nc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = fmaf(x4[e], m[e][k], acc[k]);
   }
-  if (sr >= S) acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  xor_tree<GD>(acc, lane);
+  if (s >= S) acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (GP < 64) xor_tree<GP>(acc, lane);
   return acc;
+}
+
+// part_dot for nc <= 64; `own`: this lane holds outputs 4 lane .. 4 lane + 3.
+template <int D, typename X>
+__device__ __forceinline__ f32x4 part_dot_any(const X* x, const float* M, int nc, int p, int lane, bool& own) {
+  f32x4 r;
+  int gp;
+  if (nc <= 8) {
+    gp = 2;
+    r = part_dot<D, 2>(x, M, nc, p, lane);
+  } else if (nc <= 16) {
+    gp = 4;
+    r = part_dot<D, 4>(x, M, nc, p, lane);
+  } else if (nc <= 32) {
+    gp = 8;
+    r = part_dot<D, 8>(x, M, nc, p, lane);
+  } else {
+    gp = 16;
+    r = part_dot<D, 16>(x, M, nc, p, lane);
+  }
+  own = lane < gp && 4 * lane < nc;
+  return r;
+}
+
+// Part p of k^[i] = sum_r z~[r] P[r][i], i < D (rows [p R/TP, (p+1) R/TP)):
+// lane gi < D/4 takes outputs 4gi..4gi+3 over the part's rows in order (P
+// rotated: granule gi of row r at rot_granule(r, gi)); other lanes return 0.
+template <int D>
+__device__ __forceinline__ f32x4 part_keyest(const float* zt, const float* P, int R, int p, int lane) {
+  const int RP = R / TP, gi = lane & (D / 4 - 1);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int r0 = p * RP; r0 < (p + 1) * RP; r0 += 4) {
+    const f32x4 z4 = *reinterpret_cast<const f32x4*>(zt + r0);
+    f32x4 pv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pv[e] = *reinterpret_cast<const f32x4*>(P + (r0 + e) * D + rot_granule(r0 + e, gi, D) * 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = fmaf(z4[e], pv[e][k], acc[k]);
+  }
+  return lane < D / 4 ? acc : f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// x0 + x1 + x2 + x3 in part order, four at a time from part buffers
+// [TP][stride] at column c.
+__device__ __forceinline__ f32x4 parts_sum4(const float* parts, int stride, int c) {
+  f32x4 v = *reinterpret_cast<const f32x4*>(parts + c);
+#pragma unroll
+  for (int q = 1; q < TP; ++q) {
+    const f32x4 w = *reinterpret_cast<const f32x4*>(parts + q * stride + c);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] += w[k];
+  }
+  return v;
 }
 
 // LDS operands of one token's write.
@@ -253,47 +235,76 @@ struct TokenLds {
   const float *B, *P, *Re;   // B [D][R], P rotated [R][D], R_enc [D][RK]
   float* e;                  // [D] scratch: the Key remainder
   float* st;                 // [R + RK] out: stored latent, then residual (fp32 values)
+  float *zp, *kp, *sp;       // part buffers [TP][64], [TP][128], [TP][64]
 };
 
-// One token's stored values on one wave (the chunk writer), LDS only: the
-// rounded latent z~ = round(v.B) and residual s~ = round((k - z~.P).R_enc)
-// as fp32 into L.st, the CW virtual waves of each product taken in turn.
+// Steps of one token's stored values, each taking part p of its product
+// (LDS only; all buffers 16-byte aligned):
+//   latent:    zp[p] = part p of v.B;              z~ = round(sum of the parts)
+//   remainder: kp[p] = part p of z~.P;             e = k - sum of the parts
+//   residual:  sp[p] = part p of e.R_enc;          s~ = round(sum of the parts)
+template <typename T, int D>
+__device__ __forceinline__ void token_latent_part(const TokenLds<T>& L, int R, int p, int lane) {
+  bool own;
+  const f32x4 z = part_dot_any<D>(L.v, L.B, R, p, lane, own);
+  if (own) *reinterpret_cast<f32x4*>(L.zp + p * 64 + 4 * lane) = z;
+}
+// z~ rows [r0, r0 + n) from the latent parts (n <= 64, r0 + n <= R), lanes < n
+template <typename T>
+__device__ __forceinline__ void token_latent_finish(const TokenLds<T>& L, int r0, int n, int lane) {
+  if (lane < n) {
+    float v = L.zp[r0 + lane];
+#pragma unroll
+    for (int q = 1; q < TP; ++q) v += L.zp[q * 64 + r0 + lane];
+    L.st[r0 + lane] = round_only(v, static_cast<const T*>(nullptr));
+  }
+}
+template <typename T, int D>
+__device__ __forceinline__ void token_keyest_part(const TokenLds<T>& L, int R, int p, int lane) {
+  const f32x4 kh = part_keyest<D>(L.st, L.P, R, p, lane);
+  if (lane < D / 4) *reinterpret_cast<f32x4*>(L.kp + p * 128 + 4 * lane) = kh;
+}
+// e[i] for i in [i0, i0 + 4 n4) from the key-estimate parts, lanes < n4
+template <typename T>
+__device__ __forceinline__ void token_remainder_finish(const TokenLds<T>& L, int i0, int n4, int lane) {
+  if (lane < n4) {
+    const int c = i0 + 4 * lane;
+    const f32x4 kh = parts_sum4(L.kp, 128, c);
+    const f32x4 k4 = lds_f4(L.k + c);
+    *reinterpret_cast<f32x4*>(L.e + c) = f32x4{k4[0] - kh[0], k4[1] - kh[1], k4[2] - kh[2], k4[3] - kh[3]};
+  }
+}
+template <typename T, int D>
+__device__ __forceinline__ void token_residual_part(const TokenLds<T>& L, int RK, int p, int lane) {
+  bool own;
+  const f32x4 s = part_dot_any<D>(static_cast<const float*>(L.e), L.Re, RK, p, lane, own);
+  if (own) *reinterpret_cast<f32x4*>(L.sp + p * 64 + 4 * lane) = s;
+}
+template <typename T>
+__device__ __forceinline__ void token_residual_finish(const TokenLds<T>& L, int R, int RK, int lane) {
+  if (lane < RK) {
+    float v = L.sp[lane];
+#pragma unroll
+    for (int q = 1; q < TP; ++q) v += L.sp[q * 64 + lane];
+    L.st[R + lane] = round_only(v, static_cast<const T*>(nullptr));
+  }
+}
+
+// One token's stored values on one wave (the chunk writer): the parts in
+// turn, then their sums, for each product; values into L.st.
 template <typename T, int D>
 __device__ __forceinline__ void wave_token_values(const TokenLds<T>& L, int R, int RK, int lane) {
-  f32x4 acc, sum = {0.f, 0.f, 0.f, 0.f};
-  int g = 0;
-  bool own = false;
-  for (int w = 0; w < CW; ++w) {
-    own = part_matvec<D>(L.v, L.B, R, w, lane, acc, g);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) sum[q] += acc[q];
-  }
-  if (own) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) L.st[4 * g + q] = round_only(sum[q], static_cast<const T*>(nullptr));
-  }
+  for (int p = 0; p < TP; ++p) token_latent_part<T, D>(L, R, p, lane);
   wave_sync();
-  f32x4 kh = {0.f, 0.f, 0.f, 0.f};
-  for (int w = 0; w < CW; ++w) {
-    const f32x4 p = part_remainder<D>(L.st, L.P, R, w, lane);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) kh[q] += p[q];
-  }
-  if (lane < D / 4) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) L.e[4 * lane + q] = lds_elem(L.k, 4 * lane + q) - kh[q];
-  }
+  token_latent_finish(L, 0, R, lane);
   wave_sync();
-  sum = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int w = 0; w < CW; ++w) {
-    own = part_matvec<D>(L.e, L.Re, RK, w, lane, acc, g);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) sum[q] += acc[q];
-  }
-  if (own) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) L.st[R + 4 * g + q] = round_only(sum[q], static_cast<const T*>(nullptr));
-  }
+  for (int p = 0; p < TP; ++p) token_keyest_part<T, D>(L, R, p, lane);
+  wave_sync();
+  token_remainder_finish(L, 0, D / 4, lane);
+  wave_sync();
+  for (int p = 0; p < TP; ++p) token_residual_part<T, D>(L, RK, p, lane);
+  wave_sync();
+  token_residual_finish(L, R, RK, lane);
   wave_sync();
 }
 

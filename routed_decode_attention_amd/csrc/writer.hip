@@ -13,9 +13,10 @@
 //   z~ = round(v.B);  e = k - z~.P;  s~ = round(e.R_enc);  store k, z~, s~.
 // The page's earlier slots are copied into an LDS image that receives the
 // new values; then its sums over slots [0, last written] are set from
-// scratch.  The fused decode-step append runs the same wave functions, so
-// append and chunk writes are bit-identical, and rewriting a position is
-// idempotent.
+// scratch.  Each of a token's products is taken in four fixed parts of its
+// contraction, added in part order; the fused decode-step append computes
+// the parts on four waves at once and adds them in the same order, so append
+// and chunk writes are bit-identical, and rewriting a position is idempotent.
 #include "common.hpp"
 #include "internal.hpp"
 #include "token_math.hpp"
@@ -26,7 +27,8 @@ namespace {
 
 constexpr int THREADS = 256;
 constexpr int NWAVES = THREADS / 64;
-constexpr int TOKEN_SCRATCH = 3 * 128 + 128;  // per wave: v, k, Key remainder [D], stored values [R + RK]
+// per wave: v, k, Key remainder [D], stored values [R + RK], part buffers
+constexpr int TOKEN_SCRATCH = 3 * 128 + 128 + TP * (64 + 128 + 64);
 
 // LDS bytes: B, rotated P, R_enc (fp32), the page image (storage dtype), and
 // each wave's token scratch.
@@ -89,7 +91,8 @@ __global__ __launch_bounds__(THREADS) void write_kernel(WriteArgs a) {
 
   T* mv = reinterpret_cast<T*>(my);  // the token's v and k, storage dtype
   T* mk = mv + D;
-  const TokenLds<T> L{mv, mk, sB, sP, sRe, my + 2 * D, my + 3 * D};
+  float* parts = my + 3 * D + 128;
+  const TokenLds<T> L{mv, mk, sB, sP, sRe, my + 2 * D, my + 3 * D, parts, parts + TP * 64, parts + TP * 192};
   for (int t = t0 + wave; t < t1; t += NWAVES) {
     const int slot = t - page * ps;
     const size_t src = ((size_t)(row0 + t - t0) * H + g) * D;

@@ -92,10 +92,15 @@ def _decode_full(gc, name, sample):
     cache.Z[dst] = gc.dev(sc.cache.Z[src], w.dtype)
     cache.S[dst] = gc.dev(sc.cache.S[src], w.dtype)
     cache.summ[dst] = gc.dev(sc.cache.summ[src], 0)
-    rda.basiskv_route(d, f, cache, seq_lens, q, sel, n_sel, scores, ws=ws)  # workgroup clusters
+    rda.basiskv_route(d, f, cache, seq_lens, q, sel, n_sel, scores)
     torch.cuda.synchronize()
     g_sel, g_nsel, g_scores = gc.host(sel), gc.host(n_sel), gc.host(scores)
-    rda.basiskv_route(d, f, cache, seq_lens, q, sel, n_sel, scores)  # one workgroup per pair: same bits
+    import os
+    os.environ["BASISKV_SCORE_PAGES_PER_WG"] = "256"  # another scoring plan: same bits
+    try:
+        rda.basiskv_route(d, f, cache, seq_lens, q, sel, n_sel, scores)
+    finally:
+        del os.environ["BASISKV_SCORE_PAGES_PER_WG"]
     torch.cuda.synchronize()
     assert np.array_equal(gc.host(sel), g_sel) and np.array_equal(gc.host(n_sel), g_nsel)
     for i, b in enumerate(sample):

@@ -135,9 +135,8 @@ def test_appends_equal_one_chunk_write(name):
 @pytest.mark.parametrize("pages_per_wg", [None, 3])
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_route_matches_oracle(name, pages_per_wg, monkeypatch):
-    """One workgroup per (sequence, KV head), and clusters of workgroups
-    sharing the scoring (a few pages each, ragged last range) that meet
-    through the workspace's arrival counters: same bits either way."""
+    """The default scoring plan, and one of a few pages per scoring
+    workgroup (ragged last range): same bits either way."""
     sc = scenario(name)
     sel, n_sel, scores = oracle.route(sc.d, sc.fac, sc.cache, sc.lengths, sc.q)
     g = gc.upload(sc, cache=True)
@@ -145,15 +144,14 @@ def test_route_matches_oracle(name, pages_per_wg, monkeypatch):
     if pages_per_wg is None:
         gs, gn, gscores = single
     else:
-        monkeypatch.setenv("BASISKV_ROUTE_PAGES_PER_WG", str(pages_per_wg))
-        gs, gn, gscores = gc.route(g, ws=g.ws)
-        gs2, gn2, gscores2 = gc.route(g, ws=g.ws)  # the counters were left at zero
+        monkeypatch.setenv("BASISKV_SCORE_PAGES_PER_WG", str(pages_per_wg))
+        gs, gn, gscores = gc.route(g)
+        gs2, gn2, gscores2 = gc.route(g)
         assert np.array_equal(gs, gs2) and np.array_equal(gn, gn2)
         assert np.array_equal(gs, single[0]) and np.array_equal(gn, single[1])
         for b, n in enumerate(sc.lengths):
             npg = -(-int(n) // sc.w.page_size)
             assert np.array_equal(gscores[b, :, :npg], single[2][b, :, :npg])
-        assert not gc.host(g.ws)[:12 * g.d.batch * g.d.n_kv_heads].any()  # counters back at zero
     assert np.array_equal(gn, n_sel)
     for b, n in enumerate(sc.lengths):
         npg = -(-int(n) // sc.w.page_size)
@@ -207,10 +205,9 @@ def test_attend_standalone_and_split_partials(name):
     rda.basiskv_attend(d, g.cache, g.seq_lens, g.q, sel_t, nsel_t, ws, None)
     torch.cuda.synchronize()
     ns, pairs, G, R = rda.attend_splits(d), d.batch * d.n_kv_heads, w.group, w.rank_v
-    acc_at = (12 * pairs + 255) // 256 * 256 // 4  # after the router's arrival counters
-    raw = gc.host(ws).view(np.float32)
-    acc = raw[acc_at:acc_at + pairs * ns * G * R].reshape(pairs, ns, G, R).astype(np.float64)
-    ml_at = acc_at + (pairs * ns * G * R * 4 + 255) // 256 * 256 // 4
+    raw = gc.host(ws).view(np.float32)  # partials at the start of the workspace
+    acc = raw[:pairs * ns * G * R].reshape(pairs, ns, G, R).astype(np.float64)
+    ml_at = (pairs * ns * G * R * 4 + 255) // 256 * 256 // 4
     ml = raw[ml_at:ml_at + pairs * ns * G * 2].reshape(pairs, ns, G, 2).astype(np.float64)
     m, l = ml[..., 0], ml[..., 1]
     M = m.max(axis=1, keepdims=True)
@@ -221,16 +218,14 @@ def test_attend_standalone_and_split_partials(name):
     zp = zp.reshape(d.batch, d.n_kv_heads * G, R)
     np.testing.assert_allclose(zp, z_ref, rtol=rtol, atol=atol)
 
-    # merged into z: everything but the counters NaN beforehand, so a
-    # partial read before it was stored shows
+    # merged into z: the whole workspace NaN beforehand, so a partial read
+    # before it was stored shows
     ws.fill_(0xFF)
-    ws[:acc_at * 4].zero_()
     for _ in range(2):
         z2 = torch.full((d.batch, d.n_q_heads, d.rank_v), float("nan"), device="cuda")
         rda.basiskv_attend(d, g.cache, g.seq_lens, g.q, sel_t, nsel_t, ws, z2)
         torch.cuda.synchronize()
         np.testing.assert_allclose(gc.host(z2).astype(np.float64), z_ref, rtol=rtol, atol=atol)
-        assert not gc.host(ws)[:acc_at * 4].any()  # counters back at zero
 
 
 @pytest.mark.parametrize("name", ["g4_d128_p64", "ragged_permuted", "g8_2kv_r48_p32"])
@@ -248,6 +243,14 @@ def test_route_physical_ids(name):
     s_, p_ = gc.host(sel), gc.host(phys)
     want = np.where(s_ >= 0, np.take_along_axis(sc.page_table[:, None, :], np.maximum(s_, 0), axis=2), -1)
     assert np.array_equal(p_, want)
+    # the scores-only form: the same score bits, nothing else written
+    only = torch.full_like(scores, float("nan"))
+    rda.basiskv_route(g.d, g.f, g.cache, g.seq_lens, g.q, None, None, only)
+    torch.cuda.synchronize()
+    a, b = gc.host(scores), gc.host(only)
+    for r, n in enumerate(sc.lengths):
+        npg = -(-int(n) // sc.w.page_size)
+        assert a[r, :, :npg].tobytes() == b[r, :, :npg].tobytes()
 
 
 @pytest.mark.parametrize("name", ["g4_d128_p64", "g8_2kv_r48_p32", "ragged_permuted"])
@@ -400,7 +403,6 @@ def test_decode_step_edge_rows():
         k = int(n_sel[b, 0])
         cases.check_selection_valid(scores[b, 0, :npg], gs[b, 0, :k], k, 1e-5)
     cases.check_outputs_on_selection(sc, gs, gnn, gc.host(z), gc.host(out))
-    assert not gc.host(g.ws)[:12 * B].any()  # the router's counters are back at zero
 
 
 @pytest.mark.parametrize("name,chunks", [("g4_d128_p64", [0, 128, 300]), ("g8_2kv_r48_p32", [0, 77, 513]),
@@ -506,18 +508,17 @@ def test_prefill_interleaved_with_decode_steps():
     compare_written(sc, gc.cache_host(g), ora)
 
 
-@pytest.mark.parametrize("pages_per_wg", [None, 5, 8192])
+@pytest.mark.parametrize("pages_per_wg", [None, 5, 256])
 @pytest.mark.parametrize("name", ["g4_d128_p64", "g8_2kv_r48_p32", "ragged_permuted", "tiny_f32", "g4_forced",
                                   "g8_mean_forced"])
 def test_fused_append_route_equals_separate_calls(name, pages_per_wg, monkeypatch):
-    """The decode step (append and route fused; with pages_per_wg set, a
-    cluster of the appending workgroup and scorers of that many pages each,
-    their partial selection completed with the appended page) against
-    append, route in one workgroup per (sequence, KV head), decode:
-    bit-identical."""
+    """The decode step (the append fused with the scores; the selection in
+    the attention kernel's prologue; with pages_per_wg set, scoring
+    workgroups of that many pages) against separate append, route and
+    decode calls: bit-identical."""
     import routed_decode_attention_amd as rda
     if pages_per_wg is not None:
-        monkeypatch.setenv("BASISKV_ROUTE_PAGES_PER_WG", str(pages_per_wg))
+        monkeypatch.setenv("BASISKV_SCORE_PAGES_PER_WG", str(pages_per_wg))
     sc = scenario(name)
     outs = []
     for fused in (False, True):

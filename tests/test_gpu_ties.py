@@ -4,10 +4,11 @@ The cases (tests/tie_constructions.py) make pages share their score bits on
 both sides, so only the tie rule decides what is kept: larger score first,
 then the smaller logical page (weekinpapers "BasisKV: Value Latents for
 Communication and Key Routing", Abstract: the router identifies which Key
-pages are read).  Both selection paths are covered (at most 512 pages and
-2 <= top_k <= 64; top_k above 64 or more than 512 pages), with one workgroup
-per (sequence, KV head) and with clusters of workgroups that share the
-scoring, and the decode-step append whose new page ties a kept page.
+pages are read).  Shapes with at most 512 pages and 2 <= top_k <= 64, with
+top_k above 64 and with more than 512 pages are covered; the selection runs
+in the selection kernel (route, append + route) and in the attention
+kernel's prologue (the decode step), under two scoring plans, and with the
+decode-step append whose new page ties a kept page.
 
 Scores of exactly zero cannot carry a sign here: every GPU score is an fma
 chain started from +0, so -0 never reaches the selection; the oracle's
@@ -34,7 +35,7 @@ def _gpu():
     oracle.build(force=False)
 
 
-@pytest.mark.parametrize("pages_per_wg", [None, 64])
+@pytest.mark.parametrize("pages_per_wg", [None, 7])
 @pytest.mark.parametrize("name", [s[0] for s in tk.SUMMARY_SHAPES])
 def test_route_ties_bit_equal(name, pages_per_wg, monkeypatch):
     sc, k, tied = tk.summary_case(name)
@@ -43,8 +44,8 @@ def test_route_ties_bit_equal(name, pages_per_wg, monkeypatch):
     if pages_per_wg is None:
         gs, gn, gsc = gc.route(g)
     else:
-        monkeypatch.setenv("BASISKV_ROUTE_PAGES_PER_WG", str(pages_per_wg))
-        gs, gn, gsc = gc.route(g, ws=g.ws)
+        monkeypatch.setenv("BASISKV_SCORE_PAGES_PER_WG", str(pages_per_wg))
+        gs, gn, gsc = gc.route(g)
     print(f"[ties] {name} pages_per_wg={pages_per_wg}", flush=True)
     assert np.array_equal(gn, n_sel)
     assert np.array_equal(gs, sel), [(b, gs[b, 0, :k].tolist(), sel[b, 0, :k].tolist()) for b in range(sc.batch)
@@ -61,7 +62,7 @@ def _append_inputs(sc):
     return kn, vn, pos
 
 
-@pytest.mark.parametrize("mode", ["fused_single", "fused_cluster", "decode_step"])
+@pytest.mark.parametrize("mode", ["fused_single", "fused_cluster", "decode_step"])  # fused_*: append_route
 @pytest.mark.parametrize("name", [s[0] for s in tk.APPEND_SHAPES])
 def test_appended_page_ties_bit_equal(name, mode, monkeypatch):
     """The decode-step append fills the last page with a copy of the page at
@@ -82,8 +83,8 @@ def test_appended_page_ties_bit_equal(name, mode, monkeypatch):
     if mode == "fused_single":
         rda.basiskv_append_route(d, g.f, g.cache, pos, kn, vn, g.seq_lens, g.q, gsel, gn, gscores)
     elif mode == "fused_cluster":
-        monkeypatch.setenv("BASISKV_ROUTE_PAGES_PER_WG", "48")
-        rda.basiskv_append_route(d, g.f, g.cache, pos, kn, vn, g.seq_lens, g.q, gsel, gn, gscores, ws=g.ws)
+        monkeypatch.setenv("BASISKV_SCORE_PAGES_PER_WG", "13")
+        rda.basiskv_append_route(d, g.f, g.cache, pos, kn, vn, g.seq_lens, g.q, gsel, gn, gscores)
     else:
         out = torch.zeros((1, d.d_model), device="cuda")
         z = torch.zeros((1, d.n_q_heads, d.rank_v), device="cuda")
