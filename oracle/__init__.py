@@ -46,7 +46,7 @@ class _Dims(C.Structure):
         "batch", "n_q_heads", "n_kv_heads", "head_dim", "rank_v", "rank_k",
         "page_size", "d_model", "top_k", "max_pages", "num_pages", "dtype")] + [
         ("scale", C.c_double), ("sink_pages", C.c_int32), ("local_pages", C.c_int32),
-        ("group_mean", C.c_int32)]
+        ("group_mean", C.c_int32), ("head_select", C.c_int32)]
 
 
 class _Cache(C.Structure):
@@ -107,6 +107,7 @@ class Dims:
     sink_pages: int = 0
     local_pages: int = 0
     group_mean: int = 0
+    head_select: int = 0
 
     @classmethod
     def of(cls, w: Workload, **kw) -> "Dims":
@@ -115,7 +116,7 @@ class Dims:
                     page_size=w.page_size, d_model=w.d_model, top_k=w.top_k,
                     max_pages=w.max_pages_per_seq, num_pages=0, dtype=w.dtype,
                     scale=w.softmax_scale, sink_pages=w.sink_pages, local_pages=w.local_pages,
-                    group_mean=w.group_mean)
+                    group_mean=w.group_mean, head_select=w.head_select)
         base.update(kw)
         return cls(**base)
 
@@ -123,11 +124,16 @@ class Dims:
         return _Dims(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim,
                      self.rank_v, self.rank_k, self.page_size, self.d_model,
                      self.top_k, self.max_pages, self.num_pages, self.dtype, self.scale,
-                     self.sink_pages, self.local_pages, self.group_mean)
+                     self.sink_pages, self.local_pages, self.group_mean, self.head_select)
 
     @property
     def np_dtype(self):
         return np.float32 if self.dtype == F32 else np.uint16
+
+    @property
+    def units(self) -> int:
+        """Selection units per sequence: KV heads, or query heads with head_select."""
+        return self.n_q_heads if self.head_select else self.n_kv_heads
 
 
 class Cache:
@@ -189,10 +195,12 @@ def write(d: Dims, fac, cache: Cache, seq: int, start: int, k: np.ndarray, v: np
 
 
 def route(d: Dims, fac, cache: Cache, seq_lens: np.ndarray, q: np.ndarray):
-    """Returns sel [B][H_kv][top_k], n_sel [B][H_kv], scores [B][H_kv][max_pages]."""
-    sel = np.full((d.batch, d.n_kv_heads, d.top_k), -1, np.int32)
-    n_sel = np.zeros((d.batch, d.n_kv_heads), np.int32)
-    scores = np.zeros((d.batch, d.n_kv_heads, d.max_pages), np.float32)
+    """Returns sel [B][U][top_k], n_sel [B][U], scores [B][U][max_pages] with
+    U = d.units selection units per sequence."""
+    U = d.units
+    sel = np.full((d.batch, U, d.top_k), -1, np.int32)
+    n_sel = np.zeros((d.batch, U), np.int32)
+    scores = np.zeros((d.batch, U, d.max_pages), np.float32)
     sl = np.ascontiguousarray(seq_lens, np.int32)
     q = np.ascontiguousarray(q, d.np_dtype)
     P = np.ascontiguousarray(fac.P, np.float32)

@@ -198,17 +198,21 @@ void ora_route(const ora_dims *d, const float *P, const float *R_dec, const ora_
                float *scores) {
   const int D = d->head_dim, R = d->rank_v, RK = d->rank_k, ps = d->page_size;
   const int H = d->n_kv_heads, G = d->n_q_heads / H;
+  /* selection units per sequence, and the query heads scored in a unit */
+  const int U = d->head_select ? d->n_q_heads : H, GU = d->head_select ? 1 : G;
 #pragma omp parallel for schedule(dynamic)
-  for (long pair = 0; pair < (long)d->batch * H; ++pair) {
-    int b = (int)(pair / H), g = (int)(pair % H);
+  for (long unit = 0; unit < (long)d->batch * U; ++unit) {
+    int b = (int)(unit / U), u = (int)(unit % U);
+    int g = d->head_select ? u / G : u;      /* the unit's KV head */
+    int h0 = d->head_select ? u : g * G;     /* its first query head */
     int n = seq_lens[b];
     int npg = (n + ps - 1) / ps;
     int keff = d->top_k < npg ? d->top_k : npg;
-    double *qz = malloc(sizeof(double) * (size_t)G * (R + RK));
+    double *qz = malloc(sizeof(double) * (size_t)GU * (R + RK));
     ranked *rk = malloc(sizeof(ranked) * (size_t)(npg > 0 ? npg : 1));
     /* the query seen through the latent predictor and through the residual decoder */
-    for (int hh = 0; hh < G; ++hh) {
-      int h = g * G + hh;
+    for (int hh = 0; hh < GU; ++hh) {
+      int h = h0 + hh;
       for (int j = 0; j < R; ++j) {
         double acc = 0.0;
         for (int i = 0; i < D; ++i)
@@ -222,12 +226,12 @@ void ora_route(const ora_dims *d, const float *P, const float *R_dec, const ora_
         qz[(size_t)hh * (R + RK) + R + j] = acc;
       }
     }
-    float *srow = scores ? scores + pair * d->max_pages : NULL;
+    float *srow = scores ? scores + unit * d->max_pages : NULL;
     for (int j = 0; j < npg; ++j) {
       int phys = phys_of(d, c, b, j);
       int cnt = n - j * ps < ps ? n - j * ps : ps;
       double best = -INFINITY, sum = 0.0;
-      for (int hh = 0; hh < G; ++hh) {
+      for (int hh = 0; hh < GU; ++hh) {
         double dot = 0.0;
         for (int x = 0; x < R + RK; ++x)
           dot += qz[(size_t)hh * (R + RK) + x] * (double)c->summ[summ_idx(d, phys, g, x)];
@@ -235,7 +239,7 @@ void ora_route(const ora_dims *d, const float *P, const float *R_dec, const ora_
         if (sc > best) best = sc;
         sum += sc;
       }
-      if (d->group_mean) best = sum / G; /* the group's mean instead of its max */
+      if (d->group_mean) best = sum / GU; /* the group's mean instead of its max */
       rk[j].score = (float)best;
       if (rk[j].score == 0.0f) rk[j].score = 0.0f; /* one zero */
       rk[j].page = j;
@@ -245,11 +249,11 @@ void ora_route(const ora_dims *d, const float *P, const float *R_dec, const ora_
     if (srow)
       for (int j = npg; j < d->max_pages; ++j) srow[j] = -INFINITY;
     qsort(rk, (size_t)npg, sizeof(ranked), by_score_then_page);
-    int32_t *out = sel + pair * d->top_k;
+    int32_t *out = sel + unit * d->top_k;
     for (int i = 0; i < keff; ++i) out[i] = rk[i].page;
     qsort(out, (size_t)keff, sizeof(int32_t), ascending_int);
     for (int i = keff; i < d->top_k; ++i) out[i] = -1;
-    n_sel[pair] = keff;
+    n_sel[unit] = keff;
     free(qz);
     free(rk);
   }
@@ -305,20 +309,23 @@ void ora_decode(const ora_dims *d, const void *W_ofT, const ora_cache *c,
                 const int32_t *n_sel, double *z_out, double *out) {
   const int R = d->rank_v, ps = d->page_size;
   const int H = d->n_kv_heads, G = d->n_q_heads / H;
+  const int U = d->head_select ? d->n_q_heads : H, GU = d->head_select ? 1 : G;
 #pragma omp parallel for schedule(dynamic)
-  for (long pair = 0; pair < (long)d->batch * H; ++pair) {
-    int b = (int)(pair / H), g = (int)(pair % H);
+  for (long unit = 0; unit < (long)d->batch * U; ++unit) {
+    int b = (int)(unit / U), u = (int)(unit % U);
+    int g = d->head_select ? u / G : u;
+    int h0 = d->head_select ? u : g * G;
     int n = seq_lens[b];
-    int ns = n > 0 ? n_sel[pair] : 0;
+    int ns = n > 0 ? n_sel[unit] : 0;
     int *phys = malloc(sizeof(int) * (size_t)(ns > 0 ? 2 * ns : 1));
     int *cnt = phys + ns;
     for (int i = 0; i < ns; ++i) {
-      int j = sel[pair * d->top_k + i];
+      int j = sel[unit * d->top_k + i];
       phys[i] = phys_of(d, c, b, j);
       cnt[i] = n - j * ps < ps ? n - j * ps : ps;
     }
-    for (int hh = 0; hh < G; ++hh) {
-      int h = g * G + hh;
+    for (int hh = 0; hh < GU; ++hh) {
+      int h = h0 + hh;
       attend_pages(d, c, g, q, (size_t)b * d->n_q_heads + h, phys, cnt, ns,
                    z_out + ((size_t)b * d->n_q_heads + h) * R);
     }

@@ -16,7 +16,8 @@
  *             sums of its stored latents and residuals.
  *   route   - per query head, page score = scale * q . mean_t(z~_t.P + s~_t.R_dec)
  *             evaluated from the page sums; the group's score is the max over
- *             its query heads; the top-k pages are kept.
+ *             its query heads (or their mean); the top-k pages are kept, per
+ *             KV head (or, with head_select, per query head).
  *   decode  - exact q.k on the selected pages only, softmax over their valid
  *             tokens, weighted sum of the stored latents, then the projection
  *             through W_of = B^T.W_O (the value basis folded into the output
@@ -49,6 +50,7 @@ typedef struct {
   double scale;           /* softmax scale, e.g. 1/sqrt(d_h) */
   int32_t sink_pages, local_pages;  /* routing: pages always kept at either end */
   int32_t group_mean;               /* routing: group score = mean over its query heads (else max) */
+  int32_t head_select;              /* routing: 1 = every query head selects its own pages */
 } ora_dims;
 
 typedef struct {
@@ -70,14 +72,19 @@ void ora_write(const ora_dims *d, const float *B, const float *P, const float *R
                const ora_cache *c, int32_t seq, int32_t start, int32_t n,
                const void *k, const void *v);
 
-/* Router: sel [batch][H_kv][top_k] ascending logical ids, -1 padded;
- * n_sel [batch][H_kv]; scores [batch][H_kv][max_pages] fp32 group scores
- * (-inf beyond the sequence's pages). */
+/* Router.  A selection unit is a (sequence, KV head) pair scored over the
+ * KV head's query heads, or with head_select a (sequence, query head) pair
+ * scored by that head alone; U = H_kv (or H_q) units per sequence.
+ * sel [batch][U][top_k] ascending logical ids, -1 padded; n_sel [batch][U];
+ * scores [batch][U][max_pages] fp32 unit scores (-inf beyond the sequence's
+ * pages). */
 void ora_route(const ora_dims *d, const float *P, const float *R_dec, const ora_cache *c,
                const int32_t *seq_lens, const void *q, int32_t *sel, int32_t *n_sel,
                float *scores);
 
-/* Decode over a given selection: z_out [batch][H_q][r], out [batch][d_model]. */
+/* Decode over a given selection (per unit, as the router lists it): every
+ * query head of a unit attends over the unit's pages.  z_out [batch][H_q][r],
+ * out [batch][d_model]. */
 void ora_decode(const ora_dims *d, const void *W_ofT, const ora_cache *c,
                 const int32_t *seq_lens, const void *q, const int32_t *sel,
                 const int32_t *n_sel, double *z_out, double *out);

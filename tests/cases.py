@@ -128,7 +128,7 @@ def check_outputs_on_selection(sc, sel, n_sel, z, out):
     ps = sc.w.page_size
     for b, n in enumerate(sc.lengths):
         npg = -(-int(n) // ps)
-        for h in range(sc.w.n_kv_heads):
+        for h in range(sc.w.units):
             k = int(n_sel[b, h])
             assert 0 <= k <= sc.w.top_k and all(0 <= j < npg for j in sel[b, h, :k])
     z_ref, out_ref = oracle.decode(sc.d, sc.W_ofT, sc.cache, sc.lengths, sc.q, sel, n_sel)

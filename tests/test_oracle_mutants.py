@@ -37,6 +37,12 @@ MUTANTS = {
         ("acc += (double)B[((size_t)g * D + i) * R + j] *", "acc += (double)(i == j) *"),
     "summary over one slot too many":
         ("int valid = end - page * ps;", "int valid = end - page * ps + 1;"),
+    "per-head routing scores the group's first head":
+        ("int h0 = d->head_select ? u : g * G;     /* its first query head */",
+         "int h0 = g * G;     /* its first query head */"),
+    "per-head decode attends with the group's first head":
+        ("int h0 = d->head_select ? u : g * G;\n    int n = seq_lens[b];\n    int ns",
+         "int h0 = g * G;\n    int n = seq_lens[b];\n    int ns"),
 }
 
 

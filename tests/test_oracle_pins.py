@@ -306,6 +306,87 @@ def test_group_mean_brute_force(seed):
         assert sel[0, 0, :keff].tolist() == cases.brute_topk(scores[0, 0, :npg].astype(np.float64), keff)
 
 
+# ---- head_select: every query head selects its own pages (routing variant) -----
+
+@pytest.mark.parametrize("seed", range(8))
+def test_head_select_brute_force(seed):
+    """Each query head's scores are its own page values and its selection the
+    brute-force top-k of them (ties to the smaller page, forced pages first)."""
+    rng = np.random.default_rng(300 + seed)
+    ps, G = 4, 2 + seed % 3
+    n = int(rng.integers(1, 60))
+    npg = -(-n // ps)
+    vals = rng.integers(-3, 4, size=(G, npg)).astype(np.float64)
+    d, fac, cache, q = _hand_cache(npg, ps, G, vals)
+    for j in range(npg):
+        cnt = min(ps, n - j * ps)
+        for h in range(G):
+            cache.summ[j, 0, h] = vals[h, j] * cnt
+    d.head_select = 1
+    d.sink_pages, d.local_pages = seed % 2, (seed // 2) % 2
+    for top_k in (1, 3, 16):
+        d.top_k = top_k
+        sel, n_sel, scores = oracle.route(d, fac, cache, np.array([n], np.int32), q)
+        assert sel.shape == (1, G, top_k) and n_sel.shape == (1, G)
+        keff = min(top_k, npg)
+        for h in range(G):
+            np.testing.assert_array_equal(scores[0, h, :npg], vals[h].astype(np.float32))
+            forced = [j for j in range(npg) if j < d.sink_pages or j >= npg - d.local_pages]
+            rest = [j for j in sorted(range(npg), key=lambda j: (-vals[h, j], j)) if j not in forced]
+            assert n_sel[0, h] == keff
+            assert sel[0, h, :keff].tolist() == sorted((forced + rest)[:keff])
+            assert (sel[0, h, keff:] == -1).all()
+
+
+def test_head_select_decode_brute_force():
+    """Per-head selection, then each query head's latent from a numpy softmax
+    over the tokens of its own pages and the projection of all heads."""
+    w = small("hs", 131, dtype=F32, top_k=3, head_select=1)
+    sc = make_scenario(w, lengths=[37, 22])
+    sel, n_sel, _ = oracle.route(sc.d, sc.fac, sc.cache, sc.lengths, sc.q)
+    assert sel.shape == (2, w.n_q_heads, w.top_k)
+    z, out = oracle.decode(sc.d, sc.W_ofT, sc.cache, sc.lengths, sc.q, sel, n_sel)
+    G, ps = w.group, w.page_size
+    differs = False
+    for b in range(2):
+        n = int(sc.lengths[b])
+        for h in range(w.n_q_heads):
+            g = h // G
+            pages = sel[b, h, :n_sel[b, h]].tolist()
+            differs |= pages != sel[b, g * G, :n_sel[b, g * G]].tolist()
+            toks = [t for j in pages for t in range(j * ps, min(n, (j + 1) * ps))]
+            K = to_f64(sc.K[b][toks, g], w.dtype)
+            zt = np.stack([to_f64(sc.cache.Z[sc.page_table[b, t // ps], g, :, t % ps], w.dtype) for t in toks])
+            p = cases.softmax(K @ to_f64(sc.q[b, h], w.dtype) * w.softmax_scale)
+            np.testing.assert_allclose(z[b, h], p @ zt, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(out[b], z[b].reshape(-1) @ to_f64(sc.W_ofT, w.dtype).T, rtol=1e-12, atol=1e-12)
+    assert differs, "the case should give some heads of a group different pages"
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_head_select_scores_max_to_the_group_score(dtype):
+    """The per-head scores' max over a group is the group score, bit for bit
+    (fp32 rounding is monotone); with one query head per KV head both
+    routings select the same pages and decode the same output."""
+    w = small("hm", 132, dtype=dtype, top_k=4)
+    sc = make_scenario(w, lengths=[37, 22])
+    _, _, grp = oracle.route(sc.d, sc.fac, sc.cache, sc.lengths, sc.q)
+    sc.d.head_select = 1
+    _, _, per = oracle.route(sc.d, sc.fac, sc.cache, sc.lengths, sc.q)
+    G = w.group
+    for g in range(w.n_kv_heads):
+        assert np.array_equal(per[:, g * G:(g + 1) * G].max(axis=1), grp[:, g])
+    w1 = small("h1", 133, dtype=dtype, n_q_heads=2, n_kv_heads=2, top_k=4)
+    sc1 = make_scenario(w1, lengths=[37, 22])
+    res = []
+    for hs in (0, 1):
+        sc1.d.head_select = hs
+        sel, n_sel, scores = oracle.route(sc1.d, sc1.fac, sc1.cache, sc1.lengths, sc1.q)
+        res.append((sel, n_sel, scores) + oracle.decode(sc1.d, sc1.W_ofT, sc1.cache, sc1.lengths, sc1.q, sel, n_sel))
+    for a, b in zip(*res):
+        assert np.array_equal(a, b)
+
+
 def test_topk_all_equal_takes_first_pages():
     d, fac, cache, q = _hand_cache(10, 4, 1, np.zeros((1, 10)))
     cache.summ[:, 0, 0] = 8.0      # every score 2.0

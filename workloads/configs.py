@@ -63,10 +63,16 @@ class Workload:
     sink_pages: int = 0         # routing: first pages always kept (0: plain top-k)
     local_pages: int = 0        # routing: last pages always kept
     group_mean: int = 0         # routing: group score = mean over its query heads (0: max)
+    head_select: int = 0        # routing: every query head selects its own pages (0: per KV head)
 
     @property
     def group(self) -> int:
         return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def units(self) -> int:
+        """Selection units per sequence: KV heads, or query heads with head_select."""
+        return self.n_q_heads if self.head_select else self.n_kv_heads
 
     @property
     def max_ctx(self) -> int:
