@@ -43,6 +43,8 @@ DESC = {
     "llama70b_128k": "Llama-3-70B TP=8 share long-context decode",
     "ragged_mix": "ragged paged serving mix decode (lengths U[1024, 65536], scattered pages)",
     "prefill_8k": "causal prefill of one 8192-token prompt in chunks of 2048",
+    "llama8b_32k_head_select": "Llama-3-8B TP=8 share decode with one page selection per query head "
+                               "(top-k 64 per head) instead of per KV head",
 }
 LAYERS = {"llama8b_32k": 32, "llama70b_128k": 8, "ragged_mix": 10}
 
@@ -116,7 +118,7 @@ class Decode:
         from workloads import synth
         self.w, self.L = w, L
         t0 = time.time()
-        B, H = w.batch, w.n_kv_heads
+        B, H = w.batch, w.units  # selection units per row
         self.fac = fac = synth.make_factors(w, seed)
         self.lengths = lengths = synth.make_lengths(w, seed)
         pt, total = synth.make_page_table(w, lengths, seed)
@@ -313,7 +315,7 @@ def sampled_parity(st, rows):
     assert np.array_equal(nsel, o_nsel)
     for i in range(len(rows)):
         npg = -(-int(sc.lengths[i]) // w.page_size)
-        for g in range(w.n_kv_heads):
+        for g in range(w.units):
             k = int(o_nsel[i, g])
             cases.check_selection_valid(o_scores[i, g, :npg], sel[i, g, :k], k, 1e-5)
     _, out_ref = oracle.decode(sc.d, sc.W_ofT, sc.cache, sc.lengths, sc.q, sel, nsel)
@@ -535,13 +537,15 @@ def main():
     # ---- extra workloads, each after its own parity check -------------------
     extra = {}
     if not args.no_extra and args.workload == "llama8b_32k" and args.top_k is None:
-        for name, rows in (("llama70b_128k", [0, 31]), ("ragged_mix", None)):
-            we = configs.get(name)
+        for name, rows in (("llama70b_128k", [0, 31]), ("ragged_mix", None), ("llama8b_32k_head_select", [0, 15])):
+            we = configs.get("llama8b_32k").with_(name=name, head_select=1) if name.endswith("head_select") \
+                else configs.get(name)
             if rows is None:
                 from workloads import synth
                 ln = synth.make_lengths(we, args.seed)
                 rows = sorted({int(np.argmin(ln)), int(np.argmax(ln)), 17})
-            ste, rec = run_decode(we, LAYERS[name], 4 * LAYERS[name], 2 * LAYERS[name], 10,
+            Le = LAYERS.get(name, LAYERS["llama8b_32k"])
+            ste, rec = run_decode(we, Le, 4 * Le, 2 * Le, 10,
                                   min(args.kernel_launches, 64), args.seed, parity_rows=rows)
             rec["workload"] = f"{name}: {DESC[name]}"
             extra[name] = rec

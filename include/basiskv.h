@@ -59,6 +59,14 @@
  *   j < sink_pages and j >= n_pg - local_pages rank above every score (among
  *   themselves the smaller j first), so they are kept whenever they fit in
  *   top_k; scores are reported unchanged.
+ * Selection units: by default a unit is a (sequence b, KV head g) pair and
+ * its score is score(j) above; with head_select = 1 every query head h is a
+ * unit of its own, scored by score_h(j) alone (group_mean has no effect),
+ * and attends over its own pages of KV head h / group (the pages leave the
+ * GQA granularity of routing open: kongchang article, Value-latent Key
+ * routing).  U = n_kv_heads (or n_q_heads) units per sequence; the router's
+ * scores, sel, n_sel and sel_phys below are [batch][U][...], and "pair"
+ * below means a unit.
  * ---------------------------------------------------------------------------
  */
 #ifndef BASISKV_H
@@ -71,7 +79,7 @@
 extern "C" {
 #endif
 
-#define BASISKV_VERSION 3
+#define BASISKV_VERSION 4
 
 enum {
   BASISKV_OK = 0,
@@ -111,7 +119,7 @@ typedef struct {
   int32_t rank_k;             /* r_k: residual width, multiple of 4, <= 64            */
   int32_t page_size;          /* tokens per page: 16, 32 or 64                        */
   int32_t d_model;            /* output width of this GPU's projection slice          */
-  int32_t top_k;              /* pages selected per (sequence, KV head)              */
+  int32_t top_k;              /* pages selected per selection unit (see above)       */
   int32_t max_pages_per_seq;  /* columns of page_table, <= 8192                       */
   int32_t num_phys_pages;     /* pages in each pool                                   */
   int32_t dtype;              /* BASISKV_F32 or BASISKV_BF16                          */
@@ -120,6 +128,8 @@ typedef struct {
   int32_t local_pages;        /* routing: the last local_pages pages are always kept  */
   int32_t group_mean;         /* routing: 0 = a page's score is the max over the KV
                                  head's query heads, 1 = their mean                  */
+  int32_t head_select;        /* routing: 0 = one selection per (sequence, KV head);
+                                 1 = one per (sequence, query head), see above       */
 } basiskv_dims;
 
 /* Factors.  Host struct of device pointers; read only. */
@@ -184,18 +194,18 @@ int basiskv_append(const basiskv_dims *dims, const basiskv_factors *f,
  * routing, a Key residual stores the rest; kongchang article, coarse routing
  * then exact scoring).  Reads P, R_dec, summ, page_table, seq_lens and
  * q [batch][n_q_heads][head_dim]; writes
- *   scores [batch][n_kv_heads][max_pages_per_seq] fp32 (required): score(j)
+ *   scores [batch][U][max_pages_per_seq] fp32 (required): the unit's score(j)
  *          for j < n_pg; entries j >= n_pg are left unspecified;
- *   sel    [batch][n_kv_heads][top_k] int32 ascending logical pages, -1 padded;
- *   n_sel  [batch][n_kv_heads] int32 = min(top_k, n_pg);
- *   sel_phys (nullable) [batch][n_kv_heads][top_k] int32: page_table entries of
+ *   sel    [batch][U][top_k] int32 ascending logical pages, -1 padded;
+ *   n_sel  [batch][U] int32 = min(top_k, n_pg);
+ *   sel_phys (nullable) [batch][U][top_k] int32: page_table entries of
  *          sel (-1 padded), which basiskv_attend/decode may take to skip the
  *          page-table lookup.
  * sel and n_sel are both given or both NULL; NULL asks for the scores alone
  * (sel_phys must then be NULL too).
  * Two launches: the scores (a cluster of workgroups per (sequence, KV head),
  * each scoring a few dozen pages), then the selection (a workgroup per
- * (sequence, KV head)), which the scores-only form leaves out.  Needs no
+ * unit), which the scores-only form leaves out.  Needs no
  * workspace.
  */
 int basiskv_route(const basiskv_dims *dims, const basiskv_factors *f,
@@ -231,27 +241,29 @@ int basiskv_workspace_init(const basiskv_dims *dims, void *ws, size_t ws_bytes, 
 /*
  * Routed exact attention over the selected pages (Abstract: original Keys
  * retrieved only for the selected pages to compute exact QK scores).  For
- * query head h of KV head g and sequence b:
+ * query head h of KV head g and sequence b, u its unit (g, or h with
+ * head_select):
  *   s_t = scale * q_h . k_t   for every token t < seq_lens[b] of every page
- *                             listed in sel[b][g][0 .. n_sel[b][g])
+ *                             listed in sel[b][u][0 .. n_sel[b][u])
  *   z_out[b][h] = sum_t softmax(s)_t * z~_t          (fp32 [batch][n_q_heads][rank_v])
  * A sequence with no selected page gets z_out = 0.  sel_phys (nullable): the
  * physical ids of sel as basiskv_route writes them; NULL looks them up.
- * The selection of each (sequence, KV head) is processed in splits whose
+ * The selection of each unit is processed in splits whose
  * partial results are combined afterwards (flash-decoding style).  z_out may
  * be NULL: the combination is then left to the caller and the partials stay
- * at the start of ws, fp32 [batch*n_kv_heads][n_split][group][rank_v] partial
+ * at the start of ws, fp32 [batch*U][n_split][Gu][rank_v] partial
  * sums sum_t 2^(s_t*log2(e) - m) z~_t, followed (at the next 256-byte
- * boundary) by [batch*n_kv_heads][n_split][group][2] pairs (m, sum_t
+ * boundary) by [batch*U][n_split][Gu][2] pairs (m, sum_t
  * 2^(s_t*log2(e) - m)) with m the split's max of s_t*log2(e) (-inf for an
- * empty split); n_split = basiskv_attend_splits(dims).
+ * empty split); Gu = group (1 with head_select), n_split =
+ * basiskv_attend_splits(dims).
  */
 int basiskv_attend(const basiskv_dims *dims, const basiskv_cache *cache,
                    const int32_t *seq_lens, const void *q, const int32_t *sel,
                    const int32_t *n_sel, const int32_t *sel_phys, void *ws, size_t ws_bytes,
                    float *z_out, void *stream);
 
-/* Number of splits per (sequence, KV head) that basiskv_attend plans for
+/* Number of splits per selection unit that basiskv_attend plans for
  * these dims (>= 1), or a negative error code.  Host function. */
 int basiskv_attend_splits(const basiskv_dims *dims);
 

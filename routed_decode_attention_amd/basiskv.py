@@ -39,7 +39,7 @@ class basiskv_dims(C.Structure):
         "batch", "n_q_heads", "n_kv_heads", "head_dim", "rank_v", "rank_k", "page_size",
         "d_model", "top_k", "max_pages_per_seq", "num_phys_pages", "dtype")] + [
         ("softmax_scale", C.c_float), ("sink_pages", C.c_int32), ("local_pages", C.c_int32),
-        ("group_mean", C.c_int32)]
+        ("group_mean", C.c_int32), ("head_select", C.c_int32)]
 
 
 class basiskv_factors(C.Structure):
@@ -139,12 +139,14 @@ class Dims:
     sink_pages: int = 0
     local_pages: int = 0
     group_mean: int = 0
+    head_select: int = 0
 
     def c(self) -> basiskv_dims:
         return basiskv_dims(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim,
                             self.rank_v, self.rank_k, self.page_size, self.d_model, self.top_k,
                             self.max_pages_per_seq, self.num_phys_pages, self.dtype,
-                            self.softmax_scale, self.sink_pages, self.local_pages, self.group_mean)
+                            self.softmax_scale, self.sink_pages, self.local_pages, self.group_mean,
+                            self.head_select)
 
     @property
     def torch_dtype(self):
@@ -153,6 +155,11 @@ class Dims:
     @property
     def group(self) -> int:
         return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def units(self) -> int:
+        """Selection units per sequence: KV heads, or query heads with head_select."""
+        return self.n_q_heads if self.head_select else self.n_kv_heads
 
 
 @dataclass
@@ -257,7 +264,7 @@ def basiskv_workspace_init(d: Dims, ws: torch.Tensor, stream=None) -> None:
 def basiskv_route(d: Dims, f: Factors, cache: Cache, seq_lens: torch.Tensor, q: torch.Tensor,
                   sel: torch.Tensor, n_sel: torch.Tensor, scores: torch.Tensor, sel_phys=None,
                   stream=None) -> None:
-    pairs = d.batch * d.n_kv_heads
+    pairs = d.batch * d.units
     fc, cc = f.c(d), cache.c(d)
     _check(_lib.basiskv_route(
         C.byref(d.c()), C.byref(fc), C.byref(cc),
@@ -272,7 +279,7 @@ def basiskv_append_route(d: Dims, f: Factors, cache: Cache, pos: torch.Tensor, k
                          v_new: torch.Tensor, seq_lens: torch.Tensor, q: torch.Tensor,
                          sel: torch.Tensor, n_sel: torch.Tensor, scores: torch.Tensor,
                          sel_phys=None, stream=None) -> None:
-    pairs = d.batch * d.n_kv_heads
+    pairs = d.batch * d.units
     need = d.batch * d.n_kv_heads * d.head_dim
     fc, cc = f.c(d), cache.c(d)
     _check(_lib.basiskv_append_route(
@@ -287,7 +294,7 @@ def basiskv_append_route(d: Dims, f: Factors, cache: Cache, pos: torch.Tensor, k
 
 def basiskv_decode_step(d: Dims, f: Factors, cache: Cache, pos, k_new, v_new, seq_lens, q, sel, n_sel,
                         scores, ws, out, z_out=None, stream=None) -> None:
-    pairs = d.batch * d.n_kv_heads
+    pairs = d.batch * d.units
     need = d.batch * d.n_kv_heads * d.head_dim
     fc, cc = f.c(d), cache.c(d)
     _check(_lib.basiskv_decode_step(
@@ -305,7 +312,7 @@ def basiskv_decode_step(d: Dims, f: Factors, cache: Cache, pos, k_new, v_new, se
 def basiskv_decode_step_noalloc(d: Dims, f: Factors, cache: Cache, pos, k_new, v_new, seq_lens, q, sel, n_sel,
                                 scores, out, z_out=None, stream=None) -> None:
     """basiskv_decode_step on the library's own per-device scratch (no workspace)."""
-    pairs = d.batch * d.n_kv_heads
+    pairs = d.batch * d.units
     need = d.batch * d.n_kv_heads * d.head_dim
     fc, cc = f.c(d), cache.c(d)
     _check(_lib.basiskv_decode_step_noalloc(
@@ -328,7 +335,7 @@ def attend_splits(d: Dims) -> int:
 def basiskv_attend(d: Dims, cache: Cache, seq_lens, q, sel, n_sel, ws, z_out, sel_phys=None,
                    stream=None) -> None:
     """z_out None: the split partials stay in ws (see the header)."""
-    pairs = d.batch * d.n_kv_heads
+    pairs = d.batch * d.units
     cc = cache.c(d)
     _check(_lib.basiskv_attend(
         C.byref(d.c()), C.byref(cc), _ptr(seq_lens, "seq_lens", torch.int32, d.batch),
@@ -350,7 +357,7 @@ def basiskv_project(d: Dims, f: Factors, z: torch.Tensor, rows: int, out: torch.
 
 def basiskv_decode(d: Dims, f: Factors, cache: Cache, seq_lens, q, sel, n_sel, ws, out,
                    z_out=None, sel_phys=None, stream=None) -> None:
-    pairs = d.batch * d.n_kv_heads
+    pairs = d.batch * d.units
     fc, cc = f.c(d), cache.c(d)
     _check(_lib.basiskv_decode(
         C.byref(d.c()), C.byref(fc), C.byref(cc), _ptr(seq_lens, "seq_lens", torch.int32, d.batch),

@@ -271,6 +271,7 @@ __global__ __launch_bounds__(64 * ATTEND_WAVES_MAX) void attend_mfma_kernel(Atte
   const int pair = wg / a.n_wsplit, split = wg % a.n_wsplit;
   const int H = a.s.n_kv_heads, G = a.s.group;
   const int b = pair / H, g = pair % H;
+  const int CH = a.s.cache_heads, cg = g / a.s.unit_div;  // the pair's head in the cache pools
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, qd = lane >> 4;
 
@@ -318,11 +319,11 @@ __global__ __launch_bounds__(64 * ATTEND_WAVES_MAX) void attend_mfma_kernel(Atte
   const uint16_t* Zp = static_cast<const uint16_t*>(a.Z);
   auto kpage = [&](int u) {
     const int phys = __builtin_amdgcn_readlane(my_phys, u);
-    return Kp + ((size_t)phys * H + g) * PS * D;
+    return Kp + ((size_t)phys * CH + cg) * PS * D;
   };
   auto zpage = [&](int u) {
     const int phys = __builtin_amdgcn_readlane(my_phys, u);
-    return Zp + ((size_t)phys * H + g) * R * PS;
+    return Zp + ((size_t)phys * CH + cg) * R * PS;
   };
 
   OnlineSoftmax<D, PS, R> os;
@@ -410,8 +411,8 @@ __global__ __launch_bounds__(64 * ATTEND_WAVES_MAX) void attend_valu_kernel(Atte
     const int j = SEL ? L.mine_j[i - base] : a.sel[(size_t)pair * a.s.top_k + i];
     const int phys = SEL ? L.mine_p[i - base] : a.page_table[(size_t)b * a.s.max_pages + j];
     const int cnt = min(PS, seq_len - j * PS);
-    const size_t kbase = ((size_t)phys * H + g) * PS * D;
-    const size_t zbase = ((size_t)phys * H + g) * R * PS;
+    const size_t kbase = ((size_t)phys * a.s.cache_heads + g / a.s.unit_div) * PS * D;
+    const size_t zbase = ((size_t)phys * a.s.cache_heads + g / a.s.unit_div) * R * PS;
     for (int h = 0; h < G; ++h) {
       float s = NEG_INF;
       if (lane < cnt) {

@@ -48,7 +48,7 @@ bkv::ValidateArgs validate_args(const bkv::Shape& s, const basiskv_cache* c) {
   v.page_size = s.page_size;
   v.num_phys = s.num_pages;
   v.top_k = s.top_k;
-  v.n_kv_heads = s.n_kv_heads;
+  v.n_kv_heads = bkv::unit_shape(s).n_kv_heads;  // selection units per row
   v.page_table = c->page_table;
   return v;
 }
@@ -97,6 +97,7 @@ int check_dims(const basiskv_dims* d, bkv::Shape* s) {
   if (d->sink_pages < 0 || d->local_pages < 0)
     return fail(BASISKV_E_DIMS, "sink_pages %d and local_pages %d must be >= 0", d->sink_pages, d->local_pages);
   if (d->group_mean != 0 && d->group_mean != 1) return fail(BASISKV_E_DIMS, "group_mean %d (0 or 1)", d->group_mean);
+  if (d->head_select != 0 && d->head_select != 1) return fail(BASISKV_E_DIMS, "head_select %d (0 or 1)", d->head_select);
   const int group = d->n_q_heads / d->n_kv_heads;
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(BASISKV_E_UNSUPPORTED, "head_dim %d (supported: 64, 128)", d->head_dim);
@@ -125,6 +126,9 @@ int check_dims(const basiskv_dims* d, bkv::Shape* s) {
   s->num_pages = d->num_phys_pages;
   s->dtype = d->dtype;
   s->scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf((float)d->head_dim);
+  s->cache_heads = d->n_kv_heads;
+  s->unit_div = 1;
+  s->head_select = d->head_select;
   return BASISKV_OK;
 }
 
@@ -135,7 +139,8 @@ struct WsLayout {
 // Workspace: the attention splits' partials (latent sums, then max /
 // denominator pairs), then latent rows (decode batch or prefill chunk).
 // Nothing in it carries over between calls.
-WsLayout ws_layout(const bkv::Shape& s, int max_prefill_tokens) {
+WsLayout ws_layout(const bkv::Shape& s0, int max_prefill_tokens) {
+  const bkv::Shape s = bkv::unit_shape(s0);
   const size_t pairs = (size_t)s.batch * s.n_kv_heads;
   const bkv::AttendPlan p = bkv::plan_attend(s);
   const size_t splits = pairs * p.n_wsplit * s.group;
@@ -168,9 +173,10 @@ struct PrologueSelect {
   int sink_pages = 0, local_pages = 0;
 };
 
-int do_attend(const bkv::Shape& s, const basiskv_cache* cache, const int32_t* seq_lens, const void* q,
+int do_attend(const bkv::Shape& s0, const basiskv_cache* cache, const int32_t* seq_lens, const void* q,
               const int32_t* sel, const int32_t* n_sel, void* ws, size_t ws_bytes, float* z_out,
               void* stream, const int32_t* sel_phys, bool merge, const PrologueSelect& ps = PrologueSelect()) {
+  const bkv::Shape s = bkv::unit_shape(s0);  // pairs are selection units
   const WsLayout L = ws_layout(s, 0);
   if (ws_bytes < L.z)
     return fail(BASISKV_E_WORKSPACE, "workspace of %zu bytes, attention needs %zu", ws_bytes, L.z);
@@ -228,10 +234,11 @@ int do_project(const bkv::Shape& s, const basiskv_factors* f, const float* z, in
 }
 
 // Decode attention, the merge of its splits, then the output projection.
-int attend_project(const bkv::Shape& s, const basiskv_factors* f, const basiskv_cache* cache,
+int attend_project(const bkv::Shape& s0, const basiskv_factors* f, const basiskv_cache* cache,
                    const int32_t* seq_lens, const void* q, const int32_t* sel, const int32_t* n_sel,
                    const int32_t* sel_phys, void* ws, size_t ws_bytes, float* z_out, float* out, void* stream,
                    const PrologueSelect& psel = PrologueSelect()) {
+  const bkv::Shape s = bkv::unit_shape(s0);
   const WsLayout L = ws_layout(s, 0);
   float* z = z_out ? z_out : reinterpret_cast<float*>(static_cast<char*>(ws) + L.z);
   const bool fused = bkv::plan_attend(s).n_wsplit > 1 && bkv::merge_project_supported(s);
@@ -307,7 +314,7 @@ int do_route(const bkv::Shape& s, const basiskv_dims* dims, const basiskv_factor
   if (e != hipSuccess) return hip_fail(e, "score launch");
   if (!sel) return BASISKV_OK;
   bkv::SelectArgs sa;
-  sa.s = s;
+  sa.s = bkv::unit_shape(s);
   sa.scores = scores;
   sa.page_table = cache->page_table;
   sa.seq_lens = seq_lens;
@@ -329,7 +336,7 @@ int check_step_args(const bkv::Shape& s, const basiskv_factors* f, const basiskv
   if (rc) return rc;
   if (!pos || !k_new || !v_new || !seq_lens || !q || !sel || !n_sel || !scores || !out)
     return fail(BASISKV_E_NULL, "%s: a required pointer is NULL", who);
-  if (bkv::attend_lds_bytes(s, true) > 160 * 1024)
+  if (bkv::attend_lds_bytes(bkv::unit_shape(s), true) > 160 * 1024)
     return fail(BASISKV_E_UNSUPPORTED, "%s: max_pages_per_seq %d needs more LDS than a CU has for the "
                 "attention's selection", who, s.max_pages);
   return BASISKV_OK;
@@ -533,7 +540,7 @@ int basiskv_attend_splits(const basiskv_dims* dims) {
   bkv::Shape s;
   const int rc = check_dims(dims, &s);
   if (rc) return rc;
-  return bkv::plan_attend(s).n_wsplit;
+  return bkv::plan_attend(bkv::unit_shape(s)).n_wsplit;
 }
 
 int basiskv_project(const basiskv_dims* dims, const basiskv_factors* f, const float* z, int32_t rows,

@@ -17,7 +17,25 @@ struct Shape {
   int batch, n_q_heads, n_kv_heads, group, head_dim, rank_v, rank_k, page_size;
   int d_model, top_k, max_pages, num_pages, dtype;
   float scale;
+  // The cache pools hold cache_heads KV heads; head g of this shape reads
+  // cache head g / unit_div.  As the caller gives it (head_select 0 or 1):
+  // cache_heads = n_kv_heads, unit_div = 1.
+  int cache_heads, unit_div;
+  int head_select;  // every query head selects its own pages (see unit_shape)
 };
+
+// The shape the selection and the attention see.  With head_select every
+// query head is a selection unit of its own: n_kv_heads becomes n_q_heads,
+// group 1, and unit g reads cache head g / group.  Otherwise s itself.
+inline Shape unit_shape(const Shape& s) {
+  if (!s.head_select) return s;
+  Shape u = s;
+  u.n_kv_heads = s.n_q_heads;
+  u.group = 1;
+  u.unit_div = s.group;
+  u.head_select = 0;
+  return u;
+}
 
 struct WriteArgs {
   Shape s;
@@ -42,7 +60,7 @@ struct ScoreArgs {
   const void* q;
   const int32_t* pos;         // fused append of one token per row at pos[b]; nullptr: scores only
   const void *k_new, *v_new;
-  float* scores;              // [batch][n_kv_heads][max_pages]
+  float* scores;              // [batch][units][max_pages], units: n_kv_heads (or n_q_heads with s.head_select)
   int group_mean;             // a page's score over the group's query heads: 0 max, 1 mean
   int cluster;                // workgroups per (sequence, KV head): [appender] + scorers
   int per;                    // pages per scoring workgroup (<= 256)

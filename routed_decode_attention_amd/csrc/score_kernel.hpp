@@ -9,7 +9,7 @@
 // score of page j for query head h is scale * q_h . mean_t k~_t, which by
 // linearity is scale * ((P.q_h) . sumz_j + (R_dec.q_h) . sums_j) / cnt_j.
 // A page's group score is the max over the KV head's query heads (their mean
-// with group_mean).  Decode appends the new token before attending
+// with group_mean); with per-query-head selection every head keeps its own.  Decode appends the new token before attending
 // (machinelearning.ru "KV-кэширование", "Фаза Decode"), so the appended page
 // is scored from its sums after the write.
 //
@@ -53,30 +53,41 @@ __device__ __forceinline__ f32x4 lds4(const uint16_t* p) {
                __uint_as_float(w.y & 0xffff0000u)};
 }
 
-// best[i] = max (MEAN: mean) over the group's heads h of qc[h] . sums(page i),
-// each dot split over the four lanes of a quad (NG 16-byte channel granules
-// per lane: granule part + 4u) and summed by the quad.
-template <int NG, int PPL, bool MEAN>
+// How a unit's page score combines the group's query heads: the max, the
+// mean, or every head its own score (per-query-head selection).
+enum { AGG_MAX = 0, AGG_MEAN = 1, AGG_HEAD = 2 };
+
+// d[i] = qh . sums(page i), each dot split over the four lanes of a quad (NG
+// 16-byte channel granules per lane: granule part + 4u) and summed by the quad.
+template <int NG, int PPL>
+__device__ __forceinline__ void head_dots(const f32x4 (&sv)[PPL][NG], const float* qh, int part, float (&d)[PPL]) {
+  f32x4 qg[NG];
+#pragma unroll
+  for (int u = 0; u < NG; ++u) qg[u] = *reinterpret_cast<const f32x4*>(&qh[4 * (part + 4 * u)]);
+#pragma unroll
+  for (int i = 0; i < PPL; ++i) {
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < NG; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = fmaf(qg[u][e], sv[i][u][e], acc);
+    d[i] = quad_sum(acc);
+  }
+}
+
+// best[i] = max (AGG_MEAN: mean) over the group's heads h of qc[h] . sums(page i).
+template <int NG, int PPL, int AGG>
 __device__ __forceinline__ void score_group(const f32x4 (&sv)[PPL][NG], const float (*qc)[SC_XMAX], int G, int part,
                                             float (&best)[PPL]) {
 #pragma unroll
-  for (int i = 0; i < PPL; ++i) best[i] = MEAN ? 0.f : -__builtin_huge_valf();
+  for (int i = 0; i < PPL; ++i) best[i] = AGG == AGG_MEAN ? 0.f : -__builtin_huge_valf();
   for (int h = 0; h < G; ++h) {
-    f32x4 qg[NG];
+    float d[PPL];
+    head_dots<NG, PPL>(sv, qc[h], part, d);
 #pragma unroll
-    for (int u = 0; u < NG; ++u) qg[u] = *reinterpret_cast<const f32x4*>(&qc[h][4 * (part + 4 * u)]);
-#pragma unroll
-    for (int i = 0; i < PPL; ++i) {
-      float acc = 0.f;
-#pragma unroll
-      for (int u = 0; u < NG; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc = fmaf(qg[u][e], sv[i][u][e], acc);
-      if constexpr (MEAN) best[i] += quad_sum(acc);
-      else best[i] = fmaxf(best[i], quad_sum(acc));
-    }
+    for (int i = 0; i < PPL; ++i) best[i] = AGG == AGG_MEAN ? best[i] + d[i] : fmaxf(best[i], d[i]);
   }
-  if constexpr (MEAN)
+  if constexpr (AGG == AGG_MEAN)
 #pragma unroll
     for (int i = 0; i < PPL; ++i) best[i] /= (float)G;
 }
@@ -144,9 +155,9 @@ __device__ __forceinline__ void project_query(const float* sP, const float* sRd,
 }
 
 // NG: 16-byte channel granules per scoring lane, ceil((r + r_k) / 16); 0 for
-// wide page sums (r + r_k > 64), scored by a plain per-thread path; MEAN: the
-// group score is the mean over the query heads.
-template <typename T, bool APPEND, int D, int NG, bool MEAN>
+// wide page sums (r + r_k > 64), scored by a plain per-thread path; AGG: how
+// the query heads' scores combine (AGG_HEAD: scores [b][query head][page]).
+template <typename T, bool APPEND, int D, int NG, int AGG>
 __global__ __launch_bounds__(SC_T) void score_kernel(ScoreArgs a) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   __shared__ __attribute__((aligned(16))) float s_qc[MAX_GROUP][SC_XMAX];
@@ -176,7 +187,8 @@ __global__ __launch_bounds__(SC_T) void score_kernel(ScoreArgs a) {
   float* sP = reinterpret_cast<float*>(base + lay.P);    // [R][D] rotated
   float* sRd = reinterpret_cast<float*>(base + lay.Rd);  // [RK][D] rotated
   T* sq = reinterpret_cast<T*>(base + lay.q);            // [G][D]
-  float* out = a.scores + (size_t)pair * maxp;
+  // scores of the unit(s): [pair][page], or with AGG_HEAD [pair][head][page]
+  float* out = a.scores + (size_t)pair * (AGG == AGG_HEAD ? G : 1) * maxp;
 
   // pages [lo, hi) of a scoring workgroup (the appender scores only its page)
   const int sidx = APPEND ? c - 1 : c;
@@ -266,7 +278,8 @@ __global__ __launch_bounds__(SC_T) void score_kernel(ScoreArgs a) {
       wave_token_store<T, D>(Lt, R, RK, ps, slot, Kp + (size_t)slot * D, Zp, Sp, lane);
       for (int x = lane; x < RR; x += 64) a.summ[((size_t)aphys * H + g) * RR + x] = s_newsum[x];
       if (apage < npg) {
-        float best = MEAN ? 0.f : -__builtin_huge_valf();
+        const float cnt = (float)min(ps, n - apage * ps);
+        float best = AGG == AGG_MEAN ? 0.f : -__builtin_huge_valf();
         if constexpr (NG > 0) {
           const int part = lane & 3;
           f32x4 sv[1][NG];
@@ -275,18 +288,27 @@ __global__ __launch_bounds__(SC_T) void score_kernel(ScoreArgs a) {
             const int gr = part + 4 * u;
             sv[0][u] = 4 * gr < RR ? *reinterpret_cast<const f32x4*>(s_newsum + 4 * gr) : f32x4{0.f, 0.f, 0.f, 0.f};
           }
-          float bst[1];
-          score_group<NG, 1, MEAN>(sv, s_qc, G, part, bst);
-          best = bst[0];
+          if constexpr (AGG == AGG_HEAD) {
+            for (int h = 0; h < G; ++h) {
+              float d[1];
+              head_dots<NG, 1>(sv, s_qc[h], part, d);
+              if (lane == 0) out[(size_t)h * maxp + apage] = d[0] / cnt;
+            }
+          } else {
+            float bst[1];
+            score_group<NG, 1, AGG>(sv, s_qc, G, part, bst);
+            best = bst[0];
+          }
         } else if (lane == 0) {
           for (int h = 0; h < G; ++h) {
             float d = 0.f;
             for (int x = 0; x < RR; ++x) d = fmaf(s_qc[h][x], s_newsum[x], d);
-            best = MEAN ? best + d : fmaxf(best, d);
+            if constexpr (AGG == AGG_HEAD) out[(size_t)h * maxp + apage] = d / cnt;
+            best = AGG == AGG_MEAN ? best + d : fmaxf(best, d);
           }
-          if constexpr (MEAN) best /= (float)G;
+          if constexpr (AGG == AGG_MEAN) best /= (float)G;
         }
-        if (lane == 0) out[apage] = best / (float)min(ps, n - apage * ps);
+        if (AGG != AGG_HEAD && lane == 0) out[apage] = best / cnt;
       }
     }
     return;
@@ -320,12 +342,24 @@ __global__ __launch_bounds__(SC_T) void score_kernel(ScoreArgs a) {
 #pragma unroll
       for (int u = 0; u < NG; ++u)
         if (4 * (part + 4 * u) >= RR) sv[i][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float best[SC_PPL];
-    score_group<NG, SC_PPL, MEAN>(sv, s_qc, G, part, best);
+    if constexpr (AGG == AGG_HEAD) {
+      for (int h = 0; h < G; ++h) {
+        float d[SC_PPL];
+        head_dots<NG, SC_PPL>(sv, s_qc[h], part, d);
 #pragma unroll
-    for (int i = 0; i < SC_PPL; ++i) {
-      const int j = lo + quad + 64 * i;
-      if (part == 0 && j < hi && j != apage) out[j] = best[i] / (float)min(ps, n - j * ps);
+        for (int i = 0; i < SC_PPL; ++i) {
+          const int j = lo + quad + 64 * i;
+          if (part == 0 && j < hi && j != apage) out[(size_t)h * maxp + j] = d[i] / (float)min(ps, n - j * ps);
+        }
+      }
+    } else {
+      float best[SC_PPL];
+      score_group<NG, SC_PPL, AGG>(sv, s_qc, G, part, best);
+#pragma unroll
+      for (int i = 0; i < SC_PPL; ++i) {
+        const int j = lo + quad + 64 * i;
+        if (part == 0 && j < hi && j != apage) out[j] = best[i] / (float)min(ps, n - j * ps);
+      }
     }
   } else {
     // wide sums (r + r_k > 64): a thread per page, 64 channels at a time
@@ -357,40 +391,48 @@ __global__ __launch_bounds__(SC_T) void score_kernel(ScoreArgs a) {
               if (x0 + x < RR) d[h] = fmaf(s_qc[h][x0 + x], v[x], d[h]);
           }
       }
-      float best = MEAN ? 0.f : -__builtin_huge_valf();
+      const float cnt = (float)min(ps, n - j * ps);
+      if constexpr (AGG == AGG_HEAD) {
 #pragma unroll
-      for (int h = 0; h < MAX_GROUP; ++h)
-        if (h < G) best = MEAN ? best + d[h] : fmaxf(best, d[h]);
-      if constexpr (MEAN) best /= (float)G;
-      out[j] = best / (float)min(ps, n - j * ps);
+        for (int h = 0; h < MAX_GROUP; ++h)
+          if (h < G) out[(size_t)h * maxp + j] = d[h] / cnt;
+      } else {
+        float best = AGG == AGG_MEAN ? 0.f : -__builtin_huge_valf();
+#pragma unroll
+        for (int h = 0; h < MAX_GROUP; ++h)
+          if (h < G) best = AGG == AGG_MEAN ? best + d[h] : fmaxf(best, d[h]);
+        if constexpr (AGG == AGG_MEAN) best /= (float)G;
+        out[j] = best / cnt;
+      }
     }
   }
 }
 
-template <typename T, bool APPEND, int D, int NG, bool MEAN>
+template <typename T, bool APPEND, int D, int NG, int AGG>
 hipError_t launch_sc(const ScoreArgs& a, hipStream_t st) {
   const size_t lds = score_lds(a.s.head_dim, a.s.rank_v, a.s.rank_k, a.s.group, a.s.page_size,
                                (int)sizeof(T), APPEND).total;
-  const hipError_t e = allow_lds((const void*)score_kernel<T, APPEND, D, NG, MEAN>, lds);
+  const hipError_t e = allow_lds((const void*)score_kernel<T, APPEND, D, NG, AGG>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((score_kernel<T, APPEND, D, NG, MEAN>), dim3(a.s.batch * a.s.n_kv_heads * a.cluster),
+  hipLaunchKernelGGL((score_kernel<T, APPEND, D, NG, AGG>), dim3(a.s.batch * a.s.n_kv_heads * a.cluster),
                      dim3(SC_T), lds, st, a);
   return hipGetLastError();
 }
 
-template <typename T, bool APPEND, int D, bool MEAN>
+template <typename T, bool APPEND, int D, int AGG>
 hipError_t launch_sc_n(const ScoreArgs& a, hipStream_t st) {
   const int rr = a.s.rank_v + a.s.rank_k;
   const int ng = (rr + 15) / 16;
-  if (rr > SC_VMAX) return launch_sc<T, APPEND, D, 0, MEAN>(a, st);  // wide page sums
-  if (ng <= 2) return launch_sc<T, APPEND, D, 2, MEAN>(a, st);
-  if (ng == 3) return launch_sc<T, APPEND, D, 3, MEAN>(a, st);
-  return launch_sc<T, APPEND, D, 4, MEAN>(a, st);
+  if (rr > SC_VMAX) return launch_sc<T, APPEND, D, 0, AGG>(a, st);  // wide page sums
+  if (ng <= 2) return launch_sc<T, APPEND, D, 2, AGG>(a, st);
+  if (ng == 3) return launch_sc<T, APPEND, D, 3, AGG>(a, st);
+  return launch_sc<T, APPEND, D, 4, AGG>(a, st);
 }
 
 template <typename T, bool APPEND, int D>
 hipError_t launch_sc_g(const ScoreArgs& a, hipStream_t st) {
-  return a.group_mean ? launch_sc_n<T, APPEND, D, true>(a, st) : launch_sc_n<T, APPEND, D, false>(a, st);
+  if (a.s.head_select) return launch_sc_n<T, APPEND, D, AGG_HEAD>(a, st);
+  return a.group_mean ? launch_sc_n<T, APPEND, D, AGG_MEAN>(a, st) : launch_sc_n<T, APPEND, D, AGG_MAX>(a, st);
 }
 
 template <typename T>

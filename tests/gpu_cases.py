@@ -36,7 +36,7 @@ def dims_of(w: Workload, batch: int, num_pages: int, **kw) -> rda.Dims:
                 rank_v=w.rank_v, rank_k=w.rank_k, page_size=w.page_size, d_model=w.d_model,
                 top_k=w.top_k, max_pages_per_seq=w.max_pages_per_seq, num_phys_pages=num_pages,
                 dtype=w.dtype, softmax_scale=0.0, sink_pages=w.sink_pages, local_pages=w.local_pages,
-                group_mean=w.group_mean)
+                group_mean=w.group_mean, head_select=w.head_select)
     base.update(kw)
     return rda.Dims(**base)
 
@@ -98,11 +98,10 @@ def append_last(g: Dev, sc) -> None:
 
 
 def route(g: Dev, q: Optional[torch.Tensor] = None):
-    pairs = g.d.batch * g.d.n_kv_heads
-    sel = torch.full((g.d.batch, g.d.n_kv_heads, g.d.top_k), -7, dtype=torch.int32, device="cuda")
-    n_sel = torch.full((g.d.batch, g.d.n_kv_heads), -7, dtype=torch.int32, device="cuda")
-    scores = torch.zeros((g.d.batch, g.d.n_kv_heads, g.d.max_pages_per_seq), dtype=torch.float32,
-                         device="cuda")
+    U = g.d.units
+    sel = torch.full((g.d.batch, U, g.d.top_k), -7, dtype=torch.int32, device="cuda")
+    n_sel = torch.full((g.d.batch, U), -7, dtype=torch.int32, device="cuda")
+    scores = torch.zeros((g.d.batch, U, g.d.max_pages_per_seq), dtype=torch.float32, device="cuda")
     rda.basiskv_route(g.d, g.f, g.cache, g.seq_lens, g.q if q is None else q, sel, n_sel, scores)
     torch.cuda.synchronize()
     return host(sel), host(n_sel), host(scores)

@@ -88,6 +88,7 @@ def _decode(lib, d, ws_bytes):
     (dict(sink_pages=-1), -2),
     (dict(local_pages=-3), -2),
     (dict(group_mean=2), -2),
+    (dict(head_select=-1), -2),
     (dict(head_dim=96, rank_v=32), -3),
     (dict(page_size=48), -3),
     (dict(rank_v=24), -3),

@@ -291,6 +291,83 @@ def test_decode_step_end_to_end(name):
     cases.check_outputs_on_selection(sc, gs, gn, z, out)
 
 
+# per-query-head selection: the headline geometry, a wide group with forced
+# pages, fp32 pages (the plain kernels), and a ragged permuted mix
+HEAD_SELECT = ["g4_d128_p64", "g8_mean_forced", "f32_p16_g2", "ragged_permuted"]
+
+
+def _head_select_scenario(name):
+    w, lengths = CASES[name]
+    return cases.make_scenario(w.with_(head_select=1), lengths=lengths)
+
+
+def _check_unit_selections(sc, scores, n_sel, gs, gn, gscores):
+    """Every unit's GPU selection a valid top-k of the oracle's scores (forced
+    pages first), its count equal, its scores within the fp32 bound."""
+    w = sc.w
+    assert np.array_equal(gn, n_sel)
+    for b, n in enumerate(sc.lengths):
+        npg = -(-int(n) // w.page_size)
+        for u in range(w.units):
+            k = int(n_sel[b, u])
+            np.testing.assert_allclose(gscores[b, u, :npg], scores[b, u, :npg], rtol=1e-5,
+                                       atol=1e-5 * max(1.0, float(np.abs(scores[b, u, :npg]).max(initial=0))))
+            ranked = scores[b, u, :npg].astype(np.float64).copy()
+            ranked[[j for j in range(npg) if j < w.sink_pages or j >= npg - w.local_pages]] = np.inf
+            cases.check_selection_valid(ranked, gs[b, u, :k], k, 1e-5)
+            assert (gs[b, u, k:] == -1).all()
+
+
+@pytest.mark.parametrize("name", HEAD_SELECT)
+def test_head_select_route_and_decode(name):
+    """Router and decode with one selection per query head against the
+    oracle: every head's selection, then every row's output re-run by the
+    oracle on the GPU's selections."""
+    sc = _head_select_scenario(name)
+    sel, n_sel, scores = oracle.route(sc.d, sc.fac, sc.cache, sc.lengths, sc.q)
+    assert sel.shape[1] == sc.w.n_q_heads
+    g = gc.upload(sc, cache=True, W_ofT=sc.W_ofT)
+    gs, gn, gscores = gc.route(g)
+    _check_unit_selections(sc, scores, n_sel, gs, gn, gscores)
+    z, out = gc.decode(g, gs, gn)
+    cases.check_outputs_on_selection(sc, gs, gn, z, out)
+
+
+@pytest.mark.parametrize("name", HEAD_SELECT)
+def test_head_select_decode_step(name):
+    """The decode step (append fused into the scoring launch, selection in
+    the attention prologue, merge fused into the projection) with one
+    selection per query head, against the oracle's step."""
+    import routed_decode_attention_amd as rda
+    sc = _head_select_scenario(name)
+    sel, n_sel, scores = oracle.route(sc.d, sc.fac, sc.cache, sc.lengths, sc.q)
+    g = gc.upload(sc, W_ofT=sc.W_ofT)
+    gc.write_all(g, sc, upto_last=True, chunk=1000)
+    B, U, w = sc.batch, sc.w.units, sc.w
+    kn = gc.dev(np.stack([sc.K[b][int(sc.lengths[b]) - 1] for b in range(B)]), w.dtype)
+    vn = gc.dev(np.stack([sc.V[b][int(sc.lengths[b]) - 1] for b in range(B)]), w.dtype)
+    pos = torch.from_numpy(np.asarray(sc.lengths, np.int32) - 1).cuda()
+    gsel = torch.full((B, U, w.top_k), -7, dtype=torch.int32, device="cuda")
+    gnn = torch.full((B, U), -7, dtype=torch.int32, device="cuda")
+    gsc = torch.zeros((B, U, w.max_pages_per_seq), device="cuda")
+    z = torch.zeros((B, w.n_q_heads, w.rank_v), device="cuda")
+    out = torch.zeros((B, w.d_model), device="cuda")
+    rda.basiskv_decode_step(g.d, g.f, g.cache, pos, kn, vn, g.seq_lens, g.q, gsel, gnn, gsc, g.ws, out, z_out=z)
+    torch.cuda.synchronize()
+    gs, gn = gc.host(gsel), gc.host(gnn)
+    # the GPU scored its own written cache (within the writer bound of the
+    # oracle's): the oracle routes that same cache
+    got = gc.cache_host(g)
+    compare_written(sc, got, sc.cache)
+    oc = oracle.Cache(sc.d, sc.page_table)
+    for k in ("K", "Z", "S", "summ"):
+        getattr(oc, k)[...] = got[k]
+    _, n_sel2, scores2 = oracle.route(sc.d, sc.fac, oc, sc.lengths, sc.q)
+    assert np.array_equal(n_sel2, n_sel)
+    _check_unit_selections(sc, scores2, n_sel2, gs, gn, gc.host(gsc))
+    cases.check_outputs_on_selection(sc, gs, gn, gc.host(z), gc.host(out))
+
+
 def _permuted(sc, seed):
     pt2 = synth.permute_pool(sc.page_table, sc.num_pages, seed)
     c2 = oracle.Cache(sc.d, pt2)

@@ -67,31 +67,35 @@ def decode_step_bytes(w: Workload, lengths: Sequence[int],
                       n_selected: Optional[np.ndarray] = None) -> StepBytes:
     """Algorithmic bytes of one decode layer step (append, route, attend, project).
 
-    ``selections`` [B][H_kv][top_k] (optional) gives exact valid-token counts
+    ``selections`` [B][U][top_k] (U selection units per row, w.units) gives exact valid-token counts
     for partially filled selected pages; without it every selected page is
     counted full (capped by the sequence length).
     """
     eb, ps, D, R, RK = w.elem_bytes, w.page_size, w.head_dim, w.rank_v, w.rank_k
     G = w.group
+    GU = 1 if w.head_select else G   # query heads per selection unit
     s = dict(summaries=0, keys=0, latents=0, page_table=0, queries=0, append=0)
     meta = 0
     for b, n in enumerate(lengths):
         n = int(n)
         npg = -(-n // ps)
         for g in range(w.n_kv_heads):
-            k_eff = min(w.top_k, npg)
-            sel = None if selections is None else selections[b, g]
-            if n_selected is not None:
-                k_eff = int(n_selected[b, g])
-            tok = _valid_selected_tokens(n, ps, k_eff, sel)
             s["summaries"] += npg * (R + RK) * 4
-            s["keys"] += tok * D * eb
-            s["latents"] += tok * R * eb
             s["page_table"] += npg * 4
             s["queries"] += G * D * eb
             # new token: k and v in; K, latent and residual out; page sums read+written
             s["append"] += 2 * D * eb + (D + R + RK) * eb + 2 * (R + RK) * 4
-            meta += 2 * k_eff * 4 + G * R * 4   # selection ids, their page-table entries, z-hat out
+        # each selection unit (a KV head, or a query head with head_select)
+        # reads the Keys and latents of its own pages
+        for u in range(w.units):
+            k_eff = min(w.top_k, npg)
+            sel = None if selections is None else selections[b, u]
+            if n_selected is not None:
+                k_eff = int(n_selected[b, u])
+            tok = _valid_selected_tokens(n, ps, k_eff, sel)
+            s["keys"] += tok * D * eb
+            s["latents"] += tok * R * eb
+            meta += 2 * k_eff * 4 + GU * R * 4   # selection ids, their page-table entries, z-hat out
     w_of = w.n_q_heads * R * w.d_model * eb
     out = len(lengths) * w.d_model * 4
     factors = w.n_kv_heads * (2 * D * R + 2 * D * RK) * 4
