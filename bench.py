@@ -100,6 +100,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the oracle's timed CPU work")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-extra", action="store_true", help="skip the extra workloads")
+    p.add_argument("--extras", default="llama70b_128k,ragged_mix,llama8b_32k_head_select,prefill_8k",
+                   help="comma-separated extra workloads to run after the headline one")
+    p.add_argument("--no-headline", action="store_true",
+                   help="run only the extra workloads (for profiling one of them); prints no JSON line")
     p.add_argument("--kernel-launches", type=int, default=256, help="launches per kernel for per-kernel timing")
     p.add_argument("--top-k", type=int, default=None, help="pages selected per (sequence, KV head) instead of "
                    "the workload's (a top-k sweep; same data)")
@@ -473,6 +477,39 @@ def cpu_baseline(st, seconds, seed):
     return cpu, full, res
 
 
+def run_extras(args, names):
+    """The extra workloads named (each after its own parity check)."""
+    import torch
+    from workloads import configs
+    extra = {}
+    for name, rows in (("llama70b_128k", [0, 31]), ("ragged_mix", None), ("llama8b_32k_head_select", [0, 15])):
+        if name not in names:
+            continue
+        we = configs.get("llama8b_32k").with_(name=name, head_select=1) if name.endswith("head_select") \
+            else configs.get(name)
+        if rows is None:
+            from workloads import synth
+            ln = synth.make_lengths(we, args.seed)
+            rows = sorted({int(np.argmin(ln)), int(np.argmax(ln)), 17})
+        Le = LAYERS.get(name, LAYERS["llama8b_32k"])
+        ste, rec = run_decode(we, Le, 4 * Le, 2 * Le, 10, min(args.kernel_launches, 64), args.seed, parity_rows=rows)
+        rec["workload"] = f"{name}: {DESC[name]}"
+        extra[name] = rec
+        log(f"{name}: {rec['us_per_step']:.2f} us/step, {rec['tokens_per_s'] / 1e6:.3f} M tokens/s, "
+            f"{100 * rec['frac_of_8TBs']:.1f}% of 8 TB/s; kernels (us): " +
+            ", ".join(f"{k} {v['avg_launch_us']:.2f}" for k, v in rec["kernels"].items()))
+        del ste
+        torch.cuda.empty_cache()
+    if "prefill_8k" in names:
+        pre = run_prefill(args.seed)
+        pre["workload"] = f"prefill_8k: {DESC['prefill_8k']}"
+        extra["prefill_8k"] = pre
+        log(f"prefill_8k: {pre['us_per_prompt']:.0f} us per prompt, {pre['TFLOP_per_s']} TFLOP/s "
+            f"({100 * pre['frac_of_bf16_mfma_peak']:.1f}% of the bf16 matrix-core peak); attention "
+            f"{pre['attention']['TFLOP_per_s']} TFLOP/s")
+    return extra
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -494,6 +531,9 @@ def main():
     L = args.layers or LAYERS.get(w.name, 8)
     B = w.batch
 
+    if args.no_headline:
+        run_extras(args, set(args.extras.split(",")))
+        return
     st, head = run_decode(w, L, args.steps, args.warmup, args.repeats, args.kernel_launches, args.seed,
                           parity_rows=None)
     log(f"{w.name}: {head['steps']} steps, {head['us_per_step']:.2f} us/step, "
@@ -537,29 +577,7 @@ def main():
     # ---- extra workloads, each after its own parity check -------------------
     extra = {}
     if not args.no_extra and args.workload == "llama8b_32k" and args.top_k is None:
-        for name, rows in (("llama70b_128k", [0, 31]), ("ragged_mix", None), ("llama8b_32k_head_select", [0, 15])):
-            we = configs.get("llama8b_32k").with_(name=name, head_select=1) if name.endswith("head_select") \
-                else configs.get(name)
-            if rows is None:
-                from workloads import synth
-                ln = synth.make_lengths(we, args.seed)
-                rows = sorted({int(np.argmin(ln)), int(np.argmax(ln)), 17})
-            Le = LAYERS.get(name, LAYERS["llama8b_32k"])
-            ste, rec = run_decode(we, Le, 4 * Le, 2 * Le, 10,
-                                  min(args.kernel_launches, 64), args.seed, parity_rows=rows)
-            rec["workload"] = f"{name}: {DESC[name]}"
-            extra[name] = rec
-            log(f"{name}: {rec['us_per_step']:.2f} us/step, {rec['tokens_per_s'] / 1e6:.3f} M tokens/s, "
-                f"{100 * rec['frac_of_8TBs']:.1f}% of 8 TB/s; kernels (us): " +
-                ", ".join(f"{k} {v['avg_launch_us']:.2f}" for k, v in rec["kernels"].items()))
-            del ste
-            torch.cuda.empty_cache()
-        pre = run_prefill(args.seed)
-        pre["workload"] = f"prefill_8k: {DESC['prefill_8k']}"
-        extra["prefill_8k"] = pre
-        log(f"prefill_8k: {pre['us_per_prompt']:.0f} us per prompt, {pre['TFLOP_per_s']} TFLOP/s "
-            f"({100 * pre['frac_of_bf16_mfma_peak']:.1f}% of the bf16 matrix-core peak); attention "
-            f"{pre['attention']['TFLOP_per_s']} TFLOP/s")
+        extra = run_extras(args, set(args.extras.split(",")))
 
     res = {
         "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,

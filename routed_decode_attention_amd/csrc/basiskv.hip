@@ -241,7 +241,11 @@ int attend_project(const bkv::Shape& s0, const basiskv_factors* f, const basiskv
   const bkv::Shape s = bkv::unit_shape(s0);
   const WsLayout L = ws_layout(s, 0);
   float* z = z_out ? z_out : reinterpret_cast<float*>(static_cast<char*>(ws) + L.z);
-  const bool fused = bkv::plan_attend(s).n_wsplit > 1 && bkv::merge_project_supported(s);
+  // the fused merge-projection re-merges a row's splits in every column
+  // group and re-reads the weights in every row group: it wins at one MFMA
+  // row tile (16 rows), the separate merge and projection beyond (measured:
+  // 70B 128K share 62.8 against 75.7 us per step, ragged mix 48.0 against 54.9)
+  const bool fused = bkv::plan_attend(s).n_wsplit > 1 && s.batch <= 16 && bkv::merge_project_supported(s);
   // fused: the splits' partials stay in the workspace for the merge-projection
   const int rc = do_attend(s, cache, seq_lens, q, sel, n_sel, ws, ws_bytes, z, stream, sel_phys, !fused, psel);
   if (rc) return rc;
