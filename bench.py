@@ -65,14 +65,14 @@ def source_hash() -> str:
 
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` on `workload` from the committed
-    rocprofv3 counter summary profiles/<kernel>_<workload>_counters.md
-    (FETCH_SIZE x the copy-calibrated scale + WRITE_SIZE), or None when there
-    is none or the sources have changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.md")
+    rocprofv3 counter summary profiles/<workload>_counters.md (FETCH_SIZE x
+    the copy-calibrated scale + WRITE_SIZE), or None when there is none or the
+    sources have changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_counters.md")
     try:
         text = open(path).read()
         want = re.search(r"sources sha256: ([0-9a-f]{64})", text).group(1)
-        traffic = int(re.search(r"traffic bytes per launch: (\d+)", text).group(1))
+        traffic = int(re.search(r"traffic bytes per launch \[" + re.escape(kernel) + r"\]: (\d+)", text).group(1))
     except (OSError, AttributeError):
         return None
     return traffic if source_hash() == want else None
