@@ -11,35 +11,77 @@
 // keys as rows (two tiles, row m <-> key 32c + 8*(m/4) + 4a + m%4) and the 16
 // query rows as columns; each lane then holds 8 consecutive keys of one
 // query row, which is the k-slice it supplies to O^T[r][row] += Z^T[r][key] .
-// P^T[key][row] with the channel-major latent page as the A operand.  The
-// next page's fragments are loaded while the current one is multiplied.
+// P^T[key][row] with the channel-major latent page as the A operand.
+//
+// The four waves of a workgroup (64 rows: consecutive queries) walk the same
+// pages: each page's Keys and latents are copied once per workgroup straight
+// into LDS (gfx950's direct global -> LDS loads, 16-byte granules rotated by
+// row so that the fragment reads spread over the banks), double-buffered: a
+// wave reads page p's fragments into registers, then the copy of page p + 1
+// is issued and runs while page p is multiplied.
 #include "common.hpp"
 #include "internal.hpp"
+#include "token_math.hpp"
 
 namespace bkv {
 
 namespace {
 
 constexpr float NEG_INF = -__builtin_huge_valf();
+// 16-row tiles per wave.  Two tiles share each fragment read but halve the
+// workgroups: a 2048-query chunk of the 8K prompt then runs 128 workgroups
+// on 256 CUs and measured 1208 against 1003 us per prompt.
+constexpr int PREFILL_RT = 1;
+
+// One page staged in LDS: the Keys [PS][D], then the latents [R][PS], each
+// row's 16-byte granules rotated by the row index (granule j of row x holds
+// the row's granule (j - x) mod granules-per-row).
+template <int D, int PS, int R>
+struct PageLds {
+  static constexpr int KG = D / 8, ZG = PS / 8;    // granules per Key row / latent row
+  static constexpr int NK = PS * KG, NZ = R * ZG;  // granules of each part
+  static constexpr int BYTES = 16 * (NK + NZ);
+  // copy one page (its Key block kp, latent block zp) into buf; every wave
+  // of the workgroup takes its share of 64-granule blocks
+  static __device__ __forceinline__ void stage(char* buf, const uint16_t* kp, const uint16_t* zp, int wave,
+                                               int lane) {
+    const char* K = reinterpret_cast<const char*>(kp);
+    const char* Z = reinterpret_cast<const char*>(zp);
+    const int first = dma_stage(
+        buf, NK, [&](int G) { const int x = G / KG, j = G % KG; return K + 16 * (x * KG + ((j - x) & (KG - 1))); },
+        0, 4, wave, lane);
+    dma_stage(
+        buf + 16 * NK, NZ, [&](int G) { const int x = G / ZG, j = G % ZG; return Z + 16 * (x * ZG + ((j - x) & (ZG - 1))); },
+        first, 4, wave, lane);
+  }
+};
 
 template <int D, int PS, int R>
 struct PageFrags {
   static constexpr int KS = D / 32, NC = PS / 32, MT = R / 16;
   bf16x8 k[NC][2][KS];
   bf16x8 z[NC][MT];
-  __device__ __forceinline__ void load(const uint16_t* kp, const uint16_t* zp, int n, int qd) {
+  // this lane's fragments of a page staged by PageLds
+  __device__ __forceinline__ void load(const char* buf, int n, int qd) {
+    using L = PageLds<D, PS, R>;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         const int tok = 32 * c + 8 * (n >> 2) + 4 * t2 + (n & 3);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) k[c][t2][s] = load_bf16x8(kp + tok * D + 8 * qd + 32 * s);
+        for (int s = 0; s < KS; ++s) {
+          const int gr = qd + 4 * s;
+          k[c][t2][s] = *reinterpret_cast<const bf16x8*>(buf + 16 * (tok * L::KG + ((gr + tok) & (L::KG - 1))));
+        }
       }
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int t = 0; t < MT; ++t) z[c][t] = load_bf16x8(zp + (16 * t + n) * PS + 32 * c + 8 * qd);
+      for (int t = 0; t < MT; ++t) {
+        const int row = 16 * t + n, gr = 4 * c + qd;
+        z[c][t] = *reinterpret_cast<const bf16x8*>(buf + 16 * (L::NK + row * L::ZG + ((gr + row) & (L::ZG - 1))));
+      }
   }
 };
 
@@ -54,77 +96,81 @@ __device__ __forceinline__ bf16x8 keep_first(bf16x8 v, int valid) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
-template <int D, int PS, int R>
+// RT row tiles of 16 per wave (a workgroup: 64 RT rows), every tile
+// multiplied with the same page fragments, which are read from LDS once.
+template <int D, int PS, int R, int RT>
 __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
   using F = PageFrags<D, PS, R>;
+  using L = PageLds<D, PS, R>;
   constexpr int KS = F::KS, NC = F::NC, MT = F::MT;
+  constexpr int WROWS = 16 * RT, BROWS = 4 * WROWS;  // rows per wave, per workgroup
+  extern __shared__ __attribute__((aligned(16))) char s_pages[];  // two staged pages
   const int G = a.s.group, H = a.s.n_kv_heads;
   const int g = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, qd = lane >> 4;
   const int rows = a.n_tok * G;
   const int wgi = gridDim.x - 1 - blockIdx.x;  // longest (latest) queries first
-  const int r0 = wgi * 64 + wave * 16;
-  if (r0 >= rows) return;
-  const int rr = r0 + n;
-  const int qi = rr / G, hh = rr % G;
-  const bool row_ok = rr < rows;
-  const int qpos = a.start + qi;  // this lane's query position
-  const int last_row = min(r0 + 15, rows - 1);
-  const int maxpos = a.start + last_row / G;
-  const int minpos = a.start + r0 / G;
+  const int w0 = wgi * BROWS + wave * WROWS;    // this wave's first row
+  // a wave past the chunk's rows still copies and meets the barriers
+  const bool wave_ok = w0 < rows;
   const int end = a.start + a.n_tok;  // tokens written in the cache
+  // pages the workgroup walks (its last row's) and the pages this wave needs
+  const int n_pages = (a.start + min(wgi * BROWS + BROWS - 1, rows - 1) / G) / PS + 1;
+  const int my_pages = wave_ok ? (a.start + min(w0 + WROWS - 1, rows - 1) / G) / PS + 1 : 0;
 
-  bf16x8 qb[KS];
-  {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                         ((size_t)(row_ok ? qi : 0) * a.s.n_q_heads + g * G + hh) * D;
+  // tile i: rows w0 + 16 i + (0..15); this lane's row w0 + 16 i + n
+  int qpos[RT], minpos[RT], maxpos[RT];
+  bool row_ok[RT];
+  bf16x8 qb[RT][KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qb[s] = row_ok ? load_bf16x8(qp + 8 * qd + 32 * s) : zero_bf16x8();
+  for (int i = 0; i < RT; ++i) {
+    const int r0 = w0 + 16 * i, rr = r0 + n;
+    const int qi = rr / G, hh = rr % G;
+    row_ok[i] = rr < rows;
+    qpos[i] = a.start + qi;
+    minpos[i] = a.start + r0 / G;
+    maxpos[i] = r0 < rows ? a.start + min(r0 + 15, rows - 1) / G : -1;  // -1: the tile has no row
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                         ((size_t)(row_ok[i] ? qi : 0) * a.s.n_q_heads + g * G + (row_ok[i] ? hh : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qb[i][s] = row_ok[i] ? load_bf16x8(qp + 8 * qd + 32 * s) : zero_bf16x8();
   }
 
   const uint16_t* Kp = static_cast<const uint16_t*>(a.K);
   const uint16_t* Zp = static_cast<const uint16_t*>(a.Z);
   const int32_t* pt = a.page_table + (size_t)a.seq * a.s.max_pages;
-  const int n_pages = maxpos / PS + 1;
 
-  float m_run = NEG_INF, l_run = 0.f;
-  f32x4 acc[MT];
+  float m_run[RT], l_run[RT];
+  f32x4 acc[RT][MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  F cur, nxt;
-  {
-    const int phys = pt[0];
-    cur.load(Kp + ((size_t)phys * H + g) * PS * D, Zp + ((size_t)phys * H + g) * R * PS, n, qd);
+  for (int i = 0; i < RT; ++i) {
+    m_run[i] = NEG_INF;
+    l_run[i] = 0.f;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+
+  auto stage = [&](int pg, int phys) {
+    L::stage(s_pages + (pg & 1) * L::BYTES, Kp + ((size_t)phys * H + g) * PS * D, Zp + ((size_t)phys * H + g) * R * PS,
+             wave, lane);
+  };
+  stage(0, pt[0]);
+  int phys_next = n_pages > 1 ? pt[1] : 0;
   for (int pg = 0; pg < n_pages; ++pg) {
+    wait_vmem();    // this wave's copies of page pg are in
+    lds_barrier();  // every wave's are, and page pg - 1's buffer is no longer read
+    F cur;
+    if (pg < my_pages) cur.load(s_pages + (pg & 1) * L::BYTES, n, qd);
+    // the fragment reads are issued before the next copy into the other buffer
+    __builtin_amdgcn_sched_barrier(0);
     if (pg + 1 < n_pages) {
-      const int phys = pt[pg + 1];
-      nxt.load(Kp + ((size_t)phys * H + g) * PS * D, Zp + ((size_t)phys * H + g) * R * PS, n, qd);
+      stage(pg + 1, phys_next);
+      if (pg + 2 < n_pages) phys_next = pt[pg + 2];
     }
+    if (pg >= my_pages) continue;  // (wave-uniform)
     const int kbase = pg * PS;
     const int written = min(PS, end - kbase);  // slots holding data
-
-    float sv[NC][8];
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k[c][t2][s], qb[s], s4, 0, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sv[c][4 * t2 + e] = s4[e] * a.scale_log2;
-      }
-    if (kbase + PS - 1 > minpos) {  // the diagonal: per-row causal limit
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (!row_ok || kbase + 32 * c + 8 * qd + e > qpos) sv[c][e] = NEG_INF;
-    }
     if (written < PS) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -133,44 +179,70 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
         for (int t = 0; t < MT; ++t) cur.z[c][t] = keep_first(cur.z[c][t], valid);
       }
     }
-    float mx = NEG_INF;
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+    for (int i = 0; i < RT; ++i) {
+      if (kbase > maxpos[i]) continue;  // (wave-uniform) every key of the page is after the tile's queries
+      float sv[NC][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sv[c][e]);
-    mx = pair_max<32>(pair_max<16>(mx));
-    const float m_new = fmaxf(m_run, mx);
-    // rows with nothing valid yet keep a zero state (their p below is 0)
-    const float alpha = m_new == NEG_INF ? 1.f : exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
+      for (int c = 0; c < NC; ++c)
 #pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] *= alpha;
+        for (int t2 = 0; t2 < 2; ++t2) {
+          f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      float p[8];
+          for (int s = 0; s < KS; ++s)
+            s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k[c][t2][s], qb[i][s], s4, 0, 0, 0);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = m_new == NEG_INF ? 0.f : exp2f(sv[c][e] - m_new);
-      // the weights enter the product rounded to bf16; the denominator sums
-      // the same rounded values
-      const bf16x8 pb = pack_bf16x8(p);
+          for (int e = 0; e < 4; ++e) sv[c][4 * t2 + e] = s4[e] * a.scale_log2;
+        }
+      if (kbase + PS - 1 > minpos[i]) {  // the diagonal: per-row causal limit
 #pragma unroll
-      for (int e = 0; e < 8; ++e) l_run += bf16x8_elem(pb, e);
+        for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int t = 0; t < MT; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.z[c][t], pb, acc[t], 0, 0, 0);
+          for (int e = 0; e < 8; ++e)
+            if (!row_ok[i] || kbase + 32 * c + 8 * qd + e > qpos[i]) sv[c][e] = NEG_INF;
+      }
+      float mx = NEG_INF;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sv[c][e]);
+      mx = pair_max<32>(pair_max<16>(mx));
+      const float m_new = fmaxf(m_run[i], mx);
+      // rows with nothing valid yet keep a zero state (their p below is 0)
+      const float alpha = m_new == NEG_INF ? 1.f : exp2f(m_run[i] - m_new);
+      m_run[i] = m_new;
+      l_run[i] *= alpha;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[i][t] *= alpha;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = m_new == NEG_INF ? 0.f : exp2f(sv[c][e] - m_new);
+        // the weights enter the product rounded to bf16; the denominator sums
+        // the same rounded values
+        const bf16x8 pb = pack_bf16x8(p);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) l_run[i] += bf16x8_elem(pb, e);
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+          acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.z[c][t], pb, acc[i][t], 0, 0, 0);
+      }
     }
-    if (pg + 1 < n_pages) cur = nxt;
   }
 
-  l_run = pair_sum<32>(pair_sum<16>(l_run));
-  if (row_ok) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    float* zo = a.z_out + ((size_t)qi * a.s.n_q_heads + g * G + hh) * R;
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+  for (int i = 0; i < RT; ++i) {
+    const float l = pair_sum<32>(pair_sum<16>(l_run[i]));
+    if (wave_ok && row_ok[i]) {
+      const int rr = w0 + 16 * i + n, qi = rr / G, hh = rr % G;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      float* zo = a.z_out + ((size_t)qi * a.s.n_q_heads + g * G + hh) * R;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) zo[16 * t + 4 * qd + e] = acc[t][e] * inv;
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) zo[16 * t + 4 * qd + e] = acc[i][t][e] * inv;
+    }
   }
 }
 
@@ -249,11 +321,16 @@ hipError_t launch_prefill_attend(const PrefillArgs& a, hipStream_t st) {
   if (a.n_tok <= 0) return hipSuccess;
   if (prefill_mfma_supported(a.s)) {
     const int rows = a.n_tok * a.s.group;
-    const dim3 grid((rows + 63) / 64, a.s.n_kv_heads), block(256);
+    const dim3 grid((rows + 64 * PREFILL_RT - 1) / (64 * PREFILL_RT), a.s.n_kv_heads), block(256);
     const int key = a.s.head_dim * 10000 + a.s.page_size * 100 + a.s.rank_v;
     switch (key) {
-#define BKV_CASE(D, PS, R) \
-  case D * 10000 + PS * 100 + R: hipLaunchKernelGGL((prefill_mfma_kernel<D, PS, R>), grid, block, 0, st, a); break;
+#define BKV_CASE(D, PS, R)                                                                              \
+  case D * 10000 + PS * 100 + R: {                                                                       \
+    const size_t lds = 2 * (size_t)PageLds<D, PS, R>::BYTES;                                             \
+    const hipError_t e = allow_lds((const void*)prefill_mfma_kernel<D, PS, R, PREFILL_RT>, lds);         \
+    if (e != hipSuccess) return e;                                                                       \
+    hipLaunchKernelGGL((prefill_mfma_kernel<D, PS, R, PREFILL_RT>), grid, block, lds, st, a);            \
+  } break;
       BKV_CASE(128, 64, 16) BKV_CASE(128, 64, 32) BKV_CASE(128, 64, 48) BKV_CASE(128, 64, 64)
       BKV_CASE(128, 32, 16) BKV_CASE(128, 32, 32) BKV_CASE(128, 32, 48) BKV_CASE(128, 32, 64)
       BKV_CASE(64, 64, 16) BKV_CASE(64, 64, 32) BKV_CASE(64, 64, 48) BKV_CASE(64, 64, 64)
