@@ -92,21 +92,39 @@ __device__ inline SelLds sel_lds(float* dyn, int waves, int G, int R, int maxp, 
 // (sel, n_sel) for the caller.  Returns the selection count.
 __device__ int select_prologue(const AttendArgs& a, int pair, int split, const SelLds& L) {
   const int b = pair / a.s.n_kv_heads, ps = a.s.page_size, maxp = a.s.max_pages, top_k = a.s.top_k;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const float* sc = a.scores + (size_t)pair * maxp;
+  const int32_t* pt = a.page_table + (size_t)b * maxp;
+  // the first SEL_PRE strides of scores and page-table entries are requested
+  // before the sequence length is known (clamped and unconditional, so that
+  // they are in flight together with it; entries past the sequence are
+  // read but not used)
+  constexpr int SEL_PRE = 2;
+  float s_pre[SEL_PRE];
+  int32_t p_pre[SEL_PRE];
+#pragma unroll
+  for (int i = 0; i < SEL_PRE; ++i) {
+    const int j = min(tid + i * nt, maxp - 1);
+    s_pre[i] = sc[j];
+    p_pre[i] = pt[j];
+  }
   const int n = a.seq_lens[b];
   const int npg = n > 0 ? min((n + ps - 1) / ps, maxp) : 0;
   const int ks = min(top_k, npg);
-  const float* sc = a.scores + (size_t)pair * maxp;
-  const int32_t* pt = a.page_table + (size_t)b * maxp;
   uint32_t kmax = 0u, kmin = 0xffffffffu;  // the range of the keys of pages that are not forced
-  for (int j = threadIdx.x; j < npg; j += blockDim.x) {
-    const uint32_t k = select_key(sc[j], j < a.sink_pages || j >= npg - a.local_pages);
+  auto take = [&](int j, float score, int32_t phys) {
+    const uint32_t k = select_key(score, j < a.sink_pages || j >= npg - a.local_pages);
     L.pg.keys[j] = k;
-    L.pt[j] = pt[j];
+    L.pt[j] = phys;
     if (k != 0xFFFFFFFFu) {
       kmax = max(kmax, k);
       kmin = min(kmin, k);
     }
-  }
+  };
+#pragma unroll
+  for (int i = 0; i < SEL_PRE; ++i)
+    if (tid + i * nt < npg) take(tid + i * nt, s_pre[i], p_pre[i]);
+  for (int j = tid + SEL_PRE * nt; j < npg; j += nt) take(j, sc[j], pt[j]);
   int32_t* sel = a.sel_out + (size_t)pair * top_k;
   if (split == 0) {
     for (int p = ks + threadIdx.x; p < top_k; p += blockDim.x) sel[p] = -1;
@@ -118,14 +136,16 @@ __device__ int select_prologue(const AttendArgs& a, int pair, int split, const S
   lds_barrier();
   const TopK t = topk_find(L.pg, npg, ks, *L.sh);
   const int base = split * a.waves * a.pages_per_wave, cnt = a.waves * a.pages_per_wave;
-  topk_emit(L.pg, npg, t, *L.sh, [&](int p, int j) {
+  auto put = [&](int p, int j) {
     if (p >= ks) return;  // (never: the selection keeps exactly ks pages)
     if (split == 0) sel[p] = j;
     if (p >= base && p < base + cnt) {
       L.mine_j[p - base] = j;
       L.mine_p[p - base] = L.pt[j];
     }
-  });
+  };
+  if (t.mode == 2) topk_emit(L.pg, npg, t, *L.sh, put);
+  else topk_emit_masked(L.pg, npg, t, *L.sh, put);
   lds_barrier();
   return ks;
 }

@@ -45,11 +45,13 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(SelectArgs a) {
   lds_barrier();
   const TopK t = topk_find(pg, npg, ks, sh);
   const int32_t* pt = a.page_table + (size_t)b * maxp;
-  topk_emit(pg, npg, t, sh, [&](int p, int j) {
+  auto put = [&](int p, int j) {
     if (p >= ks) return;  // (never: the cut keeps exactly ks pages)
     sel[p] = j;
     if (selp) selp[p] = pt[j];
-  });
+  };
+  if (t.mode == 2) topk_emit(pg, npg, t, sh, put);
+  else topk_emit_masked(pg, npg, t, sh, put);
 }
 
 }  // namespace

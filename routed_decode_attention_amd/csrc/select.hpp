@@ -22,7 +22,8 @@
 //      MSB-first radix cut over the keys (8-bit digits, per-wave histograms).
 //   3. every thread counts the kept pages of a run of consecutive pages; a
 //      workgroup prefix sum gives each run its first position, and each kept
-//      page is emitted with its position in page order.
+//      page is emitted with its position in page order (for the bins' cut:
+//      per-wave ballot masks and popcount prefixes instead).
 // Every barrier orders LDS only, so global loads issued before the selection
 // stay in flight.
 #pragma once
@@ -325,6 +326,47 @@ __device__ inline void topk_emit(const SelectPages& pg, int nk, const TopK& t, S
     if (g || (e && eq_before < take_eq)) emit(gt_before + min(eq_before, take_eq), j);
     gt_before += g;
     eq_before += e;
+  }
+}
+
+// Emit as topk_emit does, for the bins' cut (modes 0 and 1), through
+// per-wave ballot masks: page j is classified by thread j mod the workgroup
+// size, each wave's kept bits for one stride of pages form a 64-bit word in
+// LDS, and after one barrier a kept page's position is the kept count of the
+// words before its own (a scan over at most 128 words that every wave does
+// for itself) plus the kept lanes below it in its word.
+template <typename Emit>
+__device__ inline void topk_emit_masked(const SelectPages& pg, int nk, const TopK& t, SelectShared& sh, Emit&& emit) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  // the candidate list's area is free once the cut is found: 8 KiB, 1024 words
+  uint64_t* words = reinterpret_cast<uint64_t*>(&sh.area[1][0][0]);
+  const int nwords = (nk + 63) / 64;
+  for (int j0 = 0; j0 < nk; j0 += nt) {
+    const int j = j0 + tid;
+    bool g = false;
+    if (j < nk) {
+      if (t.mode == 0) {
+        g = true;
+      } else {
+        const int b = pg.bin[j];
+        g = b > t.bstar || (b == t.bstar && (t.all_b || pg.pick[j]));
+      }
+    }
+    const uint64_t m = __ballot(g);
+    if (lane == 0 && j0 + 64 * wave < nk) words[(j0 >> 6) + wave] = m;
+  }
+  lds_barrier();
+  const int c0 = lane < nwords ? __popcll(words[lane]) : 0;
+  const int c1 = lane + 64 < nwords ? __popcll(words[lane + 64]) : 0;
+  const int i0 = wave_incl_scan(c0), i1 = wave_incl_scan(c1);
+  const int ex0 = i0 - c0, ex1 = __builtin_amdgcn_readlane(i0, 63) + i1 - c1;  // kept pages before each word
+  for (int j0 = 0; j0 < nk; j0 += nt) {
+    const int w = (j0 >> 6) + wave;  // this wave's word of the stride (wave-uniform)
+    if (j0 + 64 * wave >= nk) break;
+    const uint64_t m = words[w];
+    const int before = w < 64 ? __builtin_amdgcn_readlane(ex0, w) : __builtin_amdgcn_readlane(ex1, w - 64);
+    if ((m >> lane) & 1u) emit(before + __popcll(m & ((1ull << lane) - 1ull)), j0 + tid);
   }
 }
 
