@@ -178,6 +178,16 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// A wave-uniform 32-bit load of data the kernel never writes, through the
+// scalar cache (constant address space): it is counted by lgkmcnt, so waiting
+// for it does not also wait for the wave's vector loads and direct copies,
+// which vmcnt counts in issue order.
+__device__ __forceinline__ int32_t load_uniform(const int32_t* p, int i) {
+  typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+  // (global memory has the same address in the constant address space)
+  return reinterpret_cast<const_i32_ptr>(reinterpret_cast<uintptr_t>(p))[uniform(i)];
+}
+
 // Wait until every global load (and direct global -> LDS copy) this wave
 // issued has completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)

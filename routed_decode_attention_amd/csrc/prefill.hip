@@ -155,8 +155,8 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
     L::stage(s_pages + (pg & 1) * L::BYTES, Kp + ((size_t)phys * H + g) * PS * D, Zp + ((size_t)phys * H + g) * R * PS,
              wave, lane);
   };
-  stage(0, pt[0]);
-  int phys_next = n_pages > 1 ? pt[1] : 0;
+  stage(0, load_uniform(pt, 0));
+  int phys_next = n_pages > 1 ? load_uniform(pt, 1) : 0;
   for (int pg = 0; pg < n_pages; ++pg) {
     wait_vmem();    // this wave's copies of page pg are in
     lds_barrier();  // every wave's are, and page pg - 1's buffer is no longer read
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     if (pg + 1 < n_pages) {
       stage(pg + 1, phys_next);
-      if (pg + 2 < n_pages) phys_next = pt[pg + 2];
+      if (pg + 2 < n_pages) phys_next = load_uniform(pt, pg + 2);  // (scalar: no wait on the copies)
     }
     if (pg >= my_pages) continue;  // (wave-uniform)
     const int kbase = pg * PS;

@@ -172,11 +172,11 @@ __global__ __launch_bounds__(SC_T) void score_kernel(ScoreArgs a) {
   const int b = pair / H, g = pair % H;
   const int R = a.s.rank_v, RK = a.s.rank_k, RR = R + RK, ps = a.s.page_size, maxp = a.s.max_pages;
   const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
-  const int n = a.seq_lens[b];
+  const int n = load_uniform(a.seq_lens, b);
   const int npg = n > 0 ? min((n + ps - 1) / ps, maxp) : 0;
   int pos = -1;
   if (APPEND) {
-    pos = a.pos[b];
+    pos = load_uniform(a.pos, b);
     if (pos < 0 || pos >= maxp * ps) pos = -1;
   }
   const int apage = pos >= 0 ? pos / ps : -1;
@@ -202,43 +202,40 @@ __global__ __launch_bounds__(SC_T) void score_kernel(ScoreArgs a) {
     const char* P = reinterpret_cast<const char*>(a.P + (size_t)g * R * D);
     const char* Rd = reinterpret_cast<const char*>(a.R_dec + (size_t)g * RK * D);
     const char* q = reinterpret_cast<const char*>(static_cast<const T*>(a.q) + ((size_t)b * a.s.n_q_heads + g * G) * D);
-    int first = dma_stage(sP, R * D / 4, [&](int G_) { return P + 16 * rot_source(G_, D); }, 0, SC_NW, wave, lane);
-    first = dma_stage(sRd, RK * D / 4, [&](int G_) { return Rd + 16 * rot_source(G_, D); }, first, SC_NW, wave, lane);
-    first = dma_stage(sq, (int)(G * D * sizeof(T) / 16), [&](int G_) { return q + 16 * G_; }, first, SC_NW, wave,
-                      lane);
-    if (appender) {
-      const char* B = reinterpret_cast<const char*>(a.B + (size_t)g * D * R);
-      const char* Re = reinterpret_cast<const char*>(a.R_enc + (size_t)g * D * RK);
-      const size_t tok = ((size_t)b * H + g) * D;
-      const char* vn = reinterpret_cast<const char*>(static_cast<const T*>(a.v_new) + tok);
-      const char* kn = reinterpret_cast<const char*>(static_cast<const T*>(a.k_new) + tok);
-      const int tc = (int)(D * sizeof(T) / 16);
-      first = dma_stage(base + lay.B, D * R / 4, [&](int G_) { return B + 16 * G_; }, first, SC_NW, wave, lane);
-      first = dma_stage(base + lay.Re, D * RK / 4, [&](int G_) { return Re + 16 * G_; }, first, SC_NW, wave, lane);
-      dma_stage(base + lay.vk, 2 * tc, [&](int G_) { return G_ < tc ? vn + 16 * G_ : kn + 16 * (G_ - tc); },
-                first, SC_NW, wave, lane);
+    // the appender's wave 0 copies nothing: it requests the appended page's
+    // image into its registers instead and so never waits for the copies
+    // (vmcnt counts a wave's loads in issue order)
+    const int cw = appender ? SC_NW - 1 : SC_NW, cwave = appender ? wave - 1 : wave;
+    if (cwave >= 0) {
+      int first = dma_stage(sP, R * D / 4, [&](int G_) { return P + 16 * rot_source(G_, D); }, 0, cw, cwave, lane);
+      first = dma_stage(sRd, RK * D / 4, [&](int G_) { return Rd + 16 * rot_source(G_, D); }, first, cw, cwave, lane);
+      first = dma_stage(sq, (int)(G * D * sizeof(T) / 16), [&](int G_) { return q + 16 * G_; }, first, cw, cwave,
+                        lane);
+      if (appender) {
+        const char* B = reinterpret_cast<const char*>(a.B + (size_t)g * D * R);
+        const char* Re = reinterpret_cast<const char*>(a.R_enc + (size_t)g * D * RK);
+        const size_t tok = ((size_t)b * H + g) * D;
+        const char* vn = reinterpret_cast<const char*>(static_cast<const T*>(a.v_new) + tok);
+        const char* kn = reinterpret_cast<const char*>(static_cast<const T*>(a.k_new) + tok);
+        const int tc = (int)(D * sizeof(T) / 16);
+        first = dma_stage(base + lay.B, D * R / 4, [&](int G_) { return B + 16 * G_; }, first, cw, cwave, lane);
+        first = dma_stage(base + lay.Re, D * RK / 4, [&](int G_) { return Re + 16 * G_; }, first, cw, cwave, lane);
+        dma_stage(base + lay.vk, 2 * tc, [&](int G_) { return G_ < tc ? vn + 16 * G_ : kn + 16 * (G_ - tc); },
+                  first, cw, cwave, lane);
+      }
     }
   }
 
   if (appender) {
     // wave 0 requests the appended page's stored latents and residuals into
-    // registers after its copies, and waits only for the copies before the
-    // token's products; the others wait for all of theirs
-    const int aphys = pt[apage];
+    // registers while waves 1-3's copies land; they wait for their copies
+    const int aphys = load_uniform(pt, apage);
     const int slot = pos - apage * ps;
     T* Zp = static_cast<T*>(a.Z) + ((size_t)aphys * H + g) * R * ps;
     T* Sp = static_cast<T*>(a.S) + ((size_t)aphys * H + g) * ps * RK;
     PageImage pg;
-    if (wave == 0) {
-      // (scheduling fences keep the copies before the image's requests, so
-      // that the count below covers exactly the copies)
-      __builtin_amdgcn_sched_barrier(0);
-      pg.load(Zp, Sp, (int)(R * ps * sizeof(T) / 16), (int)(ps * RK * sizeof(T) / 16), lane);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): all but the image's eight requests
-    } else {
-      wait_vmem();
-    }
+    if (wave == 0) pg.load(Zp, Sp, (int)(R * ps * sizeof(T) / 16), (int)(ps * RK * sizeof(T) / 16), lane);
+    else wait_vmem();
     lds_barrier();
     const T* vn = reinterpret_cast<const T*>(base + lay.vk);
     const T* kn = vn + D;
