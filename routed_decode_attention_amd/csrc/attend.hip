@@ -490,10 +490,15 @@ bool attend_mfma_supported(const Shape& s) {
 }
 
 AttendPlan plan_attend(const Shape& s) {
-  // About 16 waves per CU over 256 CUs once every page unit is counted.
+  // Resident waves: the plain kernel (one page a wave, 132 VGPRs) runs three
+  // waves per SIMD, 3072 over the chip; the pipelined one (about 230 VGPRs)
+  // two, 2048.  One page a wave while the grid fits the plain kernel's slots;
+  // beyond, enough pages a wave for the pipelined kernel's (measured at 4096
+  // page units, the 70B 128K share and the ragged mix: two pages a wave 54.3
+  // and 43.3 us per step against 58.0 and 47.4 with one, 54.2 and 45.1 with
+  // four).
   const long units = (long)s.batch * s.n_kv_heads * s.top_k;
-  int ppw = (int)((units + 4095) / 4096);
-  if (ppw < 1) ppw = 1;
+  int ppw = units <= 3072 ? 1 : (int)((units + 2047) / 2048);
   if (ppw > 8) ppw = 8;
   const char* env = getenv("BASISKV_PAGES_PER_WAVE");
   if (env && atoi(env) > 0) ppw = atoi(env) < 32 ? atoi(env) : 32;

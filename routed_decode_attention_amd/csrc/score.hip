@@ -8,11 +8,21 @@
 
 namespace bkv {
 
+// Workgroups of the scoring launch that are resident at once: four per CU
+// (about 40 KiB of LDS and at most 128 VGPRs each) on 256 CUs.
+constexpr long SC_RESIDENT = 4 * 256;
+
 void score_plan(const Shape& s, bool append, int* cluster, int* per) {
   // Pages per scoring workgroup: few, so that a pair's sums load over many
   // CUs at once (each workgroup is two memory round trips, whatever its
-  // share); at most 256 (four pages per quad).
+  // share), but not so few that the grid needs a second round of residency
+  // (long contexts: 70B 128K share, 2048 pages, 32 pairs -> 67 a workgroup);
+  // at most 256 (four pages per quad).
+  const long pairs = (long)s.batch * s.n_kv_heads;
+  const long room = SC_RESIDENT - pairs * (append ? 1 : 0);  // the appenders take one each
   int p = 64;
+  if (room > 0) p = (int)std::max<long>(64, (pairs * s.max_pages + room - 1) / room);
+  p = std::min(p, 256);
   if (const char* e = getenv("BASISKV_SCORE_PAGES_PER_WG")) p = std::max(1, std::min(256, atoi(e)));
   const int scorers = (s.max_pages + p - 1) / p;
   *per = p;
