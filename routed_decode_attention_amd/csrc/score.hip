@@ -8,18 +8,23 @@
 
 namespace bkv {
 
-// Workgroups of the scoring launch that are resident at once: four per CU
-// (about 40 KiB of LDS and at most 128 VGPRs each) on 256 CUs.
-constexpr long SC_RESIDENT = 4 * 256;
+// The kernel's static LDS (the projected queries, the token's buffers) is
+// under 14 KiB; gfx950 has 160 KiB of LDS per CU and 256 CUs.
+constexpr size_t SC_STATIC_LDS = 14 * 1024, CU_LDS = 160 * 1024;
 
 void score_plan(const Shape& s, bool append, int* cluster, int* per) {
   // Pages per scoring workgroup: few, so that a pair's sums load over many
   // CUs at once (each workgroup is two memory round trips, whatever its
   // share), but not so few that the grid needs a second round of residency
-  // (long contexts: 70B 128K share, 2048 pages, 32 pairs -> 67 a workgroup);
-  // at most 256 (four pages per quad).
+  // (long contexts: 70B 128K share, 2048 pages, 32 pairs); at most 256 (four
+  // pages per quad).  Resident workgroups: at most four per CU (VGPRs), fewer
+  // when LDS decides (every workgroup of a launch reserves the appender's
+  // regions too).
+  const size_t lds = score_lds(s.head_dim, s.rank_v, s.rank_k, s.group, s.page_size, s.dtype == 0 ? 4 : 2,
+                               append).total + SC_STATIC_LDS;
+  const long resident = (long)std::min<size_t>(4, CU_LDS / lds) * 256;
   const long pairs = (long)s.batch * s.n_kv_heads;
-  const long room = SC_RESIDENT - pairs * (append ? 1 : 0);  // the appenders take one each
+  const long room = resident - pairs * (append ? 1 : 0);  // the appenders take one each
   int p = 64;
   if (room > 0) p = (int)std::max<long>(64, (pairs * s.max_pages + room - 1) / room);
   p = std::min(p, 256);
@@ -30,10 +35,9 @@ void score_plan(const Shape& s, bool append, int* cluster, int* per) {
 }
 
 bool score_fits(const Shape& s, bool append) {
-  // the kernel's static arrays take under 14 KiB; gfx950 has 160 KiB per CU
   const size_t lds = score_lds(s.head_dim, s.rank_v, s.rank_k, s.group, s.page_size, s.dtype == 0 ? 4 : 2,
                                append).total;
-  return lds + 14 * 1024 <= 160 * 1024;
+  return lds + SC_STATIC_LDS <= CU_LDS;
 }
 
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {
