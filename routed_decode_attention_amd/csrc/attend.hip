@@ -99,15 +99,17 @@ __device__ int select_prologue(const AttendArgs& a, int pair, int split, const S
   // before the sequence length is known (clamped and unconditional, so that
   // they are in flight together with it; entries past the sequence are
   // read but not used)
-  constexpr int SEL_PRE = 2;
+  constexpr int SEL_PRE = SEL_SB;
+  const int npre = min(SEL_PRE, (maxp + nt - 1) / nt);  // strides the table has (uniform)
   float s_pre[SEL_PRE];
   int32_t p_pre[SEL_PRE];
 #pragma unroll
-  for (int i = 0; i < SEL_PRE; ++i) {
-    const int j = min(tid + i * nt, maxp - 1);
-    s_pre[i] = sc[j];
-    p_pre[i] = pt[j];
-  }
+  for (int i = 0; i < SEL_PRE; ++i)
+    if (i < npre) {
+      const int j = min(tid + i * nt, maxp - 1);
+      s_pre[i] = sc[j];
+      p_pre[i] = pt[j];
+    }
   const int n = a.seq_lens[b];
   const int npg = n > 0 ? min((n + ps - 1) / ps, maxp) : 0;
   const int ks = min(top_k, npg);
@@ -123,7 +125,7 @@ __device__ int select_prologue(const AttendArgs& a, int pair, int split, const S
   };
 #pragma unroll
   for (int i = 0; i < SEL_PRE; ++i)
-    if (tid + i * nt < npg) take(tid + i * nt, s_pre[i], p_pre[i]);
+    if (i < npre && tid + i * nt < npg) take(tid + i * nt, s_pre[i], p_pre[i]);
   for (int j = tid + SEL_PRE * nt; j < npg; j += nt) take(j, sc[j], pt[j]);
   int32_t* sel = a.sel_out + (size_t)pair * top_k;
   if (split == 0) {

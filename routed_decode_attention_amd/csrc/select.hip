@@ -24,12 +24,23 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(SelectArgs a) {
   const int ks = min(top_k, npg);
   const float* sc = a.scores + (size_t)pair * maxp;
   uint32_t kmax = 0u, kmin = 0xffffffffu;  // the range of the keys of pages that are not forced
-  for (int j = threadIdx.x; j < npg; j += SEL_T) {
-    const uint32_t k = select_key(sc[j], j < a.sink_pages || j >= npg - a.local_pages);
-    s_keys[j] = k;
-    if (k != 0xFFFFFFFFu) {
-      kmax = max(kmax, k);
-      kmin = min(kmin, k);
+  for (int s0 = 0; s0 < npg; s0 += SEL_SB * SEL_T) {
+    const int ns = min(SEL_SB, (npg - s0 + SEL_T - 1) / SEL_T), j0 = s0 + threadIdx.x;  // (uniform)
+    float v[SEL_SB];  // the batch's scores requested together (clamped)
+#pragma unroll
+    for (int u = 0; u < SEL_SB; ++u)
+      if (u < ns) v[u] = sc[min(j0 + u * SEL_T, npg - 1)];
+#pragma unroll
+    for (int u = 0; u < SEL_SB; ++u) {
+      const int j = j0 + u * SEL_T;
+      if (u < ns && j < npg) {
+        const uint32_t k = select_key(v[u], j < a.sink_pages || j >= npg - a.local_pages);
+        s_keys[j] = k;
+        if (k != 0xFFFFFFFFu) {
+          kmax = max(kmax, k);
+          kmin = min(kmin, k);
+        }
+      }
     }
   }
   int32_t* sel = a.sel + (size_t)pair * top_k;

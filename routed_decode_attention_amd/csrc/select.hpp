@@ -34,6 +34,7 @@ namespace bkv {
 
 constexpr int SEL_MAXW = 8;    // waves per selecting workgroup (4 or 8)
 constexpr int SEL_CAND = 512;  // boundary-bin pages ranked directly
+constexpr int SEL_SB = 8;      // strides of scores a thread requests together
 
 // LDS the selection needs beside the per-page arrays (16-byte aligned: the
 // histograms are cleared and read 16 bytes at a time).  The radix fallback's
@@ -184,12 +185,13 @@ __device__ inline TopKCut radix_cut(const uint32_t* keys, int nk, int ks, Select
   return TopKCut{prefix, mask, krem};
 }
 
-// Every wave clears its row of the bins' histograms; call before the
-// barrier that precedes topk_find.
+// Every wave clears its row of the bins' histograms (and thread 0 the
+// candidate count); call before the barrier that precedes topk_find.
 __device__ inline void topk_clear(SelectShared& sh) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   *reinterpret_cast<int4*>(&sh.area[0][wave][4 * lane]) = int4{0, 0, 0, 0};
+  if (tid == 0) sh.ncand = 0u;
 }
 
 // Find which of pages [0, nk) the ks best are (0 < ks), whole workgroup.
@@ -255,10 +257,9 @@ __device__ inline TopK topk_find(const SelectPages& pg, int nk, int ks, SelectSh
     return t;
   }
   // 4. the boundary bin's pages, ranked among themselves by (key, page)
+  // (the count was cleared by topk_clear)
   uint32_t* ckey = reinterpret_cast<uint32_t*>(&sh.area[1][0][0]);
   int* cpage = reinterpret_cast<int*>(ckey + SEL_CAND);
-  if (tid == 0) sh.ncand = 0u;
-  lds_barrier();
   for (int j = tid; j < nk; j += nt)
     if (pg.bin[j] == t.bstar) {
       const uint32_t c = atomicAdd(&sh.ncand, 1u);
