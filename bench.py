@@ -72,7 +72,8 @@ def measured_traffic(kernel: str, workload: str):
     try:
         text = open(path).read()
         want = re.search(r"sources sha256: ([0-9a-f]{64})", text).group(1)
-        traffic = int(re.search(r"traffic bytes per launch \[" + re.escape(kernel) + r"\]: (\d+)", text).group(1))
+        traffic = sum(int(re.search(r"traffic bytes per launch \[" + re.escape(k) + r"\]: (\d+)", text).group(1))
+                      for k in kernel.split("+"))  # a step part of two kernels: both launches
     except (OSError, AttributeError):
         return None
     return traffic if source_hash() == want else None
@@ -231,6 +232,13 @@ def time_launches(fn, n):
     return e0.elapsed_time(e1) * 1e3 / n
 
 
+def mp_kernels(w) -> str:
+    """The kernel(s) of the split merge and the projection: fused at one MFMA
+    row tile (16 rows, the library's rule), the merge kernel and the
+    projection kernel beyond."""
+    return "merge_project_kernel" if w.batch <= 16 else "merge_kernel+project_mfma_kernel"
+
+
 def decode_kernels(st, launches):
     """Live per-kernel launch durations of the decode step's three kernels
     (append + scores, attention with its selection prologue, merge +
@@ -265,7 +273,7 @@ def decode_kernels(st, launches):
             ("append_score", "score_kernel", t_score, b_score, "events"),
             ("attend_select", "attend_mfma_kernel", t_step - t_score - t_mp, sb.attend_kernel,
              "events (step minus scoring minus merge-projection)"),
-            ("merge_project", "merge_project_kernel", t_mp, sb.w_of + sb.out,
+            ("merge_project", mp_kernels(w), t_mp, sb.w_of + sb.out,
              "events (decode minus attention)")):
         gbs = by / (us * 1e-6) / 1e9
         recs[name] = {"kernel": kern, "avg_launch_us": round(us, 3), "bytes_per_launch": int(by),
