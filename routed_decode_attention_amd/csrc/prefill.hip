@@ -15,8 +15,8 @@
 //
 // The four waves of a workgroup (64 rows: consecutive queries) walk the same
 // pages: each page's Keys and latents are copied once per workgroup straight
-// into LDS (gfx950's direct global -> LDS loads, 16-byte granules rotated by
-// row so that the fragment reads spread over the banks), double-buffered: a
+// into LDS (gfx950's direct global -> LDS loads, 16-byte granules permuted
+// within each row so that the fragment reads spread over the banks), double-buffered: a
 // wave reads page p's fragments into registers, then the copy of page p + 1
 // is issued and runs while page p is multiplied.
 #include "common.hpp"
@@ -34,13 +34,28 @@ constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr int PREFILL_RT = 1;
 
 // One page staged in LDS: the Keys [PS][D], then the latents [R][PS], each
-// row's 16-byte granules rotated by the row index (granule j of row x holds
-// the row's granule (j - x) mod granules-per-row).
+// row's 16-byte granules permuted within the row by an XOR with a function
+// of the row (its own inverse, so the copy uses the same map).  A 16-byte LDS
+// read serves 16 lanes per pass from a 256-byte bank row; the fragment reads
+// below put 16 different rows in a pass (Key rows 8a + b (+4), a, b < 4;
+// latent rows 16t + n), and the maps send them to 16 different positions.
 template <int D, int PS, int R>
 struct PageLds {
   static constexpr int KG = D / 8, ZG = PS / 8;    // granules per Key row / latent row
   static constexpr int NK = PS * KG, NZ = R * ZG;  // granules of each part
   static constexpr int BYTES = 16 * (NK + NZ);
+  static_assert(KG == 16 || KG == 8, "head_dim 128 or 64");
+  static_assert(ZG == 8 || ZG == 4, "pages of 64 or 32");
+  // position within Key row `tok` of its granule g (and the reverse)
+  static __device__ __forceinline__ int kpos(int tok, int g) {
+    if constexpr (KG == 16) return g ^ ((tok & 3) | (((tok >> 3) & 3) << 2));
+    else return g ^ (((tok >> 1) & 1) | (((tok >> 3) & 3) << 1));  // two rows per bank row
+  }
+  // position within latent row `row` of its granule g (and the reverse)
+  static __device__ __forceinline__ int zpos(int row, int g) {
+    if constexpr (ZG == 8) return g ^ ((row >> 1) & 7);  // two rows per bank row
+    else return g ^ ((row >> 2) & 3);                    // four rows per bank row
+  }
   // copy one page (its Key block kp, latent block zp) into buf; every wave
   // of the workgroup takes its share of 64-granule blocks
   static __device__ __forceinline__ void stage(char* buf, const uint16_t* kp, const uint16_t* zp, int wave,
@@ -48,10 +63,10 @@ struct PageLds {
     const char* K = reinterpret_cast<const char*>(kp);
     const char* Z = reinterpret_cast<const char*>(zp);
     const int first = dma_stage(
-        buf, NK, [&](int G) { const int x = G / KG, j = G % KG; return K + 16 * (x * KG + ((j - x) & (KG - 1))); },
-        0, 4, wave, lane);
+        buf, NK, [&](int G) { const int x = G / KG, j = G % KG; return K + 16 * (x * KG + kpos(x, j)); }, 0, 4,
+        wave, lane);
     dma_stage(
-        buf + 16 * NK, NZ, [&](int G) { const int x = G / ZG, j = G % ZG; return Z + 16 * (x * ZG + ((j - x) & (ZG - 1))); },
+        buf + 16 * NK, NZ, [&](int G) { const int x = G / ZG, j = G % ZG; return Z + 16 * (x * ZG + zpos(x, j)); },
         first, 4, wave, lane);
   }
 };
@@ -70,17 +85,15 @@ struct PageFrags {
       for (int t2 = 0; t2 < 2; ++t2) {
         const int tok = 32 * c + 8 * (n >> 2) + 4 * t2 + (n & 3);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const int gr = qd + 4 * s;
-          k[c][t2][s] = *reinterpret_cast<const bf16x8*>(buf + 16 * (tok * L::KG + ((gr + tok) & (L::KG - 1))));
-        }
+        for (int s = 0; s < KS; ++s)
+          k[c][t2][s] = *reinterpret_cast<const bf16x8*>(buf + 16 * (tok * L::KG + L::kpos(tok, qd + 4 * s)));
       }
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
-        const int row = 16 * t + n, gr = 4 * c + qd;
-        z[c][t] = *reinterpret_cast<const bf16x8*>(buf + 16 * (L::NK + row * L::ZG + ((gr + row) & (L::ZG - 1))));
+        const int row = 16 * t + n;
+        z[c][t] = *reinterpret_cast<const bf16x8*>(buf + 16 * (L::NK + row * L::ZG + L::zpos(row, 4 * c + qd)));
       }
   }
 };
