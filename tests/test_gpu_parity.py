@@ -299,6 +299,38 @@ def test_decode_step_end_to_end(name):
     cases.check_outputs_on_selection(sc, gs, gn, z, out)
 
 
+def test_decode_step_at_the_page_limit():
+    """The decode step (selection in the attention prologue) over 8192 pages
+    of 16 tokens, the most a page-table row may hold: more pages than a
+    workgroup's threads request in one batch, the rest taken by its loop;
+    a second row of 70000 tokens ends in a partial page."""
+    import routed_decode_attention_amd as rda
+    w = small("p8k", 216, batch=2, n_q_heads=4, n_kv_heads=1, head_dim=64, page_size=16, rank_v=16, rank_k=8,
+              top_k=64, d_model=128, dtype=BF16, ctx=131072)
+    assert w.max_pages_per_seq == 8192
+    sc = cases.make_scenario(w, lengths=[131072, 70000])
+    sel, n_sel, scores = oracle.route(sc.d, sc.fac, sc.cache, sc.lengths, sc.q)
+    g = gc.upload(sc, cache=True, W_ofT=sc.W_ofT)
+    pos = torch.full((2,), -1, dtype=torch.int32, device="cuda")  # no append: the cache holds every token
+    kn = torch.zeros((2, 1, 64), dtype=torch.bfloat16, device="cuda")
+    gsel = torch.full((2, 1, 64), -7, dtype=torch.int32, device="cuda")
+    gn = torch.full((2, 1), -7, dtype=torch.int32, device="cuda")
+    gsc = torch.zeros((2, 1, 8192), device="cuda")
+    z = torch.zeros((2, 4, 16), device="cuda")
+    out = torch.zeros((2, 128), device="cuda")
+    print("[page limit] decode step over 8192 pages", flush=True)
+    rda.basiskv_decode_step(g.d, g.f, g.cache, pos, kn, kn, g.seq_lens, g.q, gsel, gn, gsc, g.ws, out, z_out=z)
+    torch.cuda.synchronize()
+    gs, gnn, gscores = gc.host(gsel), gc.host(gn), gc.host(gsc)
+    assert np.array_equal(gnn, n_sel)
+    for b, n in enumerate(sc.lengths):
+        npg = -(-int(n) // 16)
+        np.testing.assert_allclose(gscores[b, 0, :npg], scores[b, 0, :npg], rtol=1e-5,
+                                   atol=1e-5 * max(1.0, float(np.abs(scores[b, 0, :npg]).max())))
+        cases.check_selection_valid(scores[b, 0, :npg].astype(np.float64), gs[b, 0, :64], 64, 1e-5)
+    cases.check_outputs_on_selection(sc, gs, gnn, gc.host(z), gc.host(out))
+
+
 # per-query-head selection: the headline geometry, a wide group with forced
 # pages, fp32 pages (the plain kernels), and a ragged permuted mix
 HEAD_SELECT = ["g4_d128_p64", "g8_mean_forced", "f32_p16_g2", "ragged_permuted"]
