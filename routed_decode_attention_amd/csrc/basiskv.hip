@@ -233,29 +233,35 @@ int do_project(const bkv::Shape& s, const basiskv_factors* f, const float* z, in
   return e == hipSuccess ? BASISKV_OK : hip_fail(e, "projection launch");
 }
 
-// Decode attention, the merge of its splits, then the output projection.
-int attend_project(const bkv::Shape& s0, const basiskv_factors* f, const basiskv_cache* cache,
-                   const int32_t* seq_lens, const void* q, const int32_t* sel, const int32_t* n_sel,
-                   const int32_t* sel_phys, void* ws, size_t ws_bytes, float* z_out, float* out, void* stream,
-                   const PrologueSelect& psel = PrologueSelect()) {
-  const bkv::Shape s = bkv::unit_shape(s0);
-  const WsLayout L = ws_layout(s, 0);
-  float* z = z_out ? z_out : reinterpret_cast<float*>(static_cast<char*>(ws) + L.z);
-  // the fused merge-projection re-merges a row's splits in every column
-  // group and re-reads the weights in every row group: it wins at one MFMA
-  // row tile (16 rows), the separate merge and projection beyond (measured:
-  // 70B 128K share 62.8 against 75.7 us per step, ragged mix 48.0 against 54.9)
-  const bool fused = bkv::plan_attend(s).n_wsplit > 1 && s.batch <= 16 && bkv::merge_project_supported(s);
-  // fused: the splits' partials stay in the workspace for the merge-projection
-  const int rc = do_attend(s, cache, seq_lens, q, sel, n_sel, ws, ws_bytes, z, stream, sel_phys, !fused, psel);
-  if (rc) return rc;
-  if (!fused) return do_project(s, f, z, s.batch, out, stream);
+// After the attention (n_wsplit splits per unit, partials at L in ws, or
+// with one split the latents already in z): the merge of the splits and the
+// output projection.  The fused merge-projection re-merges a row's splits in
+// every column group and re-reads the weights in every row group: it wins at
+// one MFMA row tile (16 rows), the separate merge and projection beyond
+// (measured: 70B 128K share 62.8 against 75.7 us per step, ragged mix 48.0
+// against 54.9).  s: the unit shape.
+int merge_project(const bkv::Shape& s, const basiskv_factors* f, void* ws, const WsLayout& L, int n_wsplit,
+                  float* z, float* z_out, float* out, void* stream) {
   char* w = static_cast<char*>(ws);
+  const bool fused = n_wsplit > 1 && s.batch <= 16 && bkv::merge_project_supported(s);
+  if (!fused) {
+    if (n_wsplit > 1) {
+      bkv::MergeArgs m;
+      m.s = s;
+      m.part_acc = reinterpret_cast<const float*>(w + L.part_acc);
+      m.part_ml = reinterpret_cast<const float*>(w + L.part_ml);
+      m.n_wsplit = n_wsplit;
+      m.z_out = z;
+      const hipError_t e = bkv::launch_merge(m, as_stream(stream));
+      if (e != hipSuccess) return hip_fail(e, "split merge launch");
+    }
+    return do_project(s, f, z, s.batch, out, stream);
+  }
   bkv::MergeProjectArgs m;
   m.s = s;
   m.part_acc = reinterpret_cast<const float*>(w + L.part_acc);
   m.part_ml = reinterpret_cast<const float*>(w + L.part_ml);
-  m.n_wsplit = bkv::plan_attend(s).n_wsplit;
+  m.n_wsplit = n_wsplit;
   m.W = f->W_ofT;
   m.out = out;
   m.z_out = z_out;
@@ -264,6 +270,20 @@ int attend_project(const bkv::Shape& s0, const basiskv_factors* f, const basiskv
   m.n = s.d_model;
   const hipError_t e = bkv::launch_merge_project(m, as_stream(stream));
   return e == hipSuccess ? BASISKV_OK : hip_fail(e, "merge-projection launch");
+}
+
+// Decode attention, the merge of its splits, then the output projection.
+int attend_project(const bkv::Shape& s0, const basiskv_factors* f, const basiskv_cache* cache,
+                   const int32_t* seq_lens, const void* q, const int32_t* sel, const int32_t* n_sel,
+                   const int32_t* sel_phys, void* ws, size_t ws_bytes, float* z_out, float* out, void* stream,
+                   const PrologueSelect& psel = PrologueSelect()) {
+  const bkv::Shape s = bkv::unit_shape(s0);
+  const WsLayout L = ws_layout(s, 0);
+  float* z = z_out ? z_out : reinterpret_cast<float*>(static_cast<char*>(ws) + L.z);
+  // the splits' partials stay in the workspace for merge_project
+  const int rc = do_attend(s, cache, seq_lens, q, sel, n_sel, ws, ws_bytes, z, stream, sel_phys, false, psel);
+  if (rc) return rc;
+  return merge_project(s, f, ws, L, bkv::plan_attend(s).n_wsplit, z, z_out, out, stream);
 }
 
 int do_write(const bkv::Shape& s, const basiskv_factors* f, const basiskv_cache* c, const int32_t* pos,

@@ -112,46 +112,59 @@ __host__ __device__ inline ScoreLds score_lds(int D, int R, int RK, int G, int p
   return L;
 }
 
-// The query seen through P and R_dec, times the softmax scale:
-// qc[h][x] = scale * (P.q_h | R_dec.q_h)[x]; one task per (output row x,
-// quarter c), lane c of a quad taking 16-byte pieces 4u + c of the row, the
-// quad summing the quarters.  Outputs past r + r_k (up to SC_VMAX) are zero.
+// The query seen through P and R_dec, times the softmax scale, on the matrix
+// cores (fp32 products, v_mfma_f32_16x16x4f32): the rows of P and R_dec (r + r_k, in 16-row tiles) times the group's
+// queries (up to 16 heads as the columns).  Waves wave0, wave0 + nwaves, ...
+// take a tile each; lane (n, qd) supplies row 16 t + n and head n over dims
+// 32 qd + s at step s (the contraction's order permuted so that each lane
+// reads 32 consecutive values), two accumulators for the even and odd steps.
+// qc[h][x] = scale * (P.q_h | R_dec.q_h)[x]; outputs past r + r_k (up to
+// SC_VMAX) are zero (the threads of waves >= wave0 write them).
 template <typename T, int D>
-__device__ __forceinline__ void project_query(const float* sP, const float* sRd, const T* sq, float (*qc)[SC_XMAX],
-                                              int R, int RK, int G, float scale, int t0, int stride) {
-  const int RR = R + RK;
-  for (int t = t0; t < ((RR * 4 + 63) & ~63); t += stride) {
-    const int x = min(t >> 2, RR - 1), c = t & 3;  // lanes past the tasks repeat the last row, unused
+__device__ __forceinline__ void project_query(const float* sP, const float* sRd, const T* sq,
+                                                   float (*qc)[SC_XMAX], int R, int RK, int G, float scale, int wave0,
+                                                   int nwaves, int wave, int lane) {
+  static_assert(D == 128 || D == 64, "head_dim");
+  constexpr int KQ = D / 4;  // dims per lane group
+  const int RR = R + RK, n = lane & 15, qd = lane >> 4;
+  // this lane's head: its KQ consecutive query values as fp32
+  float qv[KQ];
+  {
+    const T* qh = sq + min(n, G - 1) * D + KQ * qd;
+#pragma unroll
+    for (int u = 0; u < KQ / 4; ++u) {
+      const f32x4 q4 = lds4(qh + 4 * u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qv[4 * u + e] = n < G ? q4[e] : 0.f;
+    }
+  }
+  for (int t = wave - wave0; 16 * t < RR; t += nwaves) {
+    const int x = min(16 * t + n, RR - 1);
     const int xr = x < R ? x : x - R;
     const float* row = (x < R ? sP : sRd) + xr * D;
-    f32x4 pr[D / 16];
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < D / 16; ++u) pr[u] = lds4(row + rot_granule(xr, 4 * u + c, D) * 4);
-    for (int h0 = 0; h0 < G; h0 += 4) {  // four heads at a time: their loads in flight together
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < KQ / 4; ++u) {
+      // granule KQ/4 qd + u of the row, rotated by the row in LDS
+      const f32x4 p4 = lds4(row + rot_granule(xr, (KQ / 4) * qd + u, D) * 4);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(p4[0], qv[4 * u], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(p4[1], qv[4 * u + 1], acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(p4[2], qv[4 * u + 2], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(p4[3], qv[4 * u + 3], acc1, 0, 0, 0);
+    }
+    // lane (n, qd) holds rows 16 t + 4 qd + i of head n
+    if (n < G) {
 #pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        if (h0 + hh < G) {
-          const T* qh = sq + (h0 + hh) * D;
-#pragma unroll
-          for (int u = 0; u < D / 16; ++u) {
-            const f32x4 q4 = lds4(qh + 16 * u + 4 * c);
-            acc[hh] = fmaf(pr[u][0], q4[0], acc[hh]);
-            acc[hh] = fmaf(pr[u][1], q4[1], acc[hh]);
-            acc[hh] = fmaf(pr[u][2], q4[2], acc[hh]);
-            acc[hh] = fmaf(pr[u][3], q4[3], acc[hh]);
-          }
-        }
-      }
-#pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        const float v = quad_sum(acc[hh]);
-        if (h0 + hh < G && c == 0 && (t >> 2) < RR) qc[h0 + hh][x] = v * scale;
+      for (int i = 0; i < 4; ++i) {
+        const int xo = 16 * t + 4 * qd + i;
+        if (xo < RR) qc[n][xo] = (acc0[i] + acc1[i]) * scale;
       }
     }
   }
-  if (RR < SC_VMAX)
+  if (RR < SC_VMAX) {
+    const int t0 = (wave - wave0) * 64 + lane, stride = nwaves * 64;
     for (int t = t0; t < G * (SC_VMAX - RR); t += stride) qc[t / (SC_VMAX - RR)][RR + t % (SC_VMAX - RR)] = 0.f;
+  }
 }
 
 // NG: 16-byte channel granules per scoring lane, ceil((r + r_k) / 16); 0 for
@@ -233,9 +246,19 @@ __global__ __launch_bounds__(SC_T) void score_kernel(ScoreArgs a) {
     const int slot = pos - apage * ps;
     T* Zp = static_cast<T*>(a.Z) + ((size_t)aphys * H + g) * R * ps;
     T* Sp = static_cast<T*>(a.S) + ((size_t)aphys * H + g) * ps * RK;
+    // (bf16: the operands of the page's sums themselves, in the layout the
+    // sums' products take, so the sums need no LDS copy of the page; fp32:
+    // the raw image, summed through LDS)
+    constexpr bool BF16 = sizeof(T) == 2;
     PageImage pg;
-    if (wave == 0) pg.load(Zp, Sp, (int)(R * ps * sizeof(T) / 16), (int)(ps * RK * sizeof(T) / 16), lane);
-    else wait_vmem();
+    PageSumRegs pr;
+    if (wave == 0) {
+      if constexpr (BF16) pr.load(reinterpret_cast<const uint16_t*>(Zp), reinterpret_cast<const uint16_t*>(Sp), R, RK, ps,
+                                  lane);
+      else pg.load(Zp, Sp, (int)(R * ps * sizeof(T) / 16), (int)(ps * RK * sizeof(T) / 16), lane);
+    } else {
+      wait_vmem();
+    }
     lds_barrier();
     const T* vn = reinterpret_cast<const T*>(base + lay.vk);
     const T* kn = vn + D;
@@ -257,22 +280,33 @@ __global__ __launch_bounds__(SC_T) void score_kernel(ScoreArgs a) {
     lds_barrier();
     if (wave == 0) {
       token_residual_finish(Lt, R, RK, lane);
-      pg.store(img, lane);
+      // the page's operands are in (long since); waiting for them here,
+      // before the token's stores, keeps the sums from waiting for the stores
+      // (vmcnt counts both in issue order)
+      wait_vmem();
       wave_sync();
-      for (int x = lane; x < RR; x += 64) {
-        if (x < R) store_elem(img, (size_t)x * ps + slot, s_st[x]);
-        else store_elem(img, (size_t)R * ps + (size_t)slot * RK + (x - R), s_st[x]);
+      // the token's stores first: they complete while the page is summed
+      T* Kp = static_cast<T*>(a.K) + ((size_t)aphys * H + g) * ps * D;
+      wave_token_store<T, D>(Lt, R, RK, ps, slot, Kp + (size_t)slot * D, Zp, Sp, lane);
+      if constexpr (BF16) {
+        pr.put(slot, s_st, R, RK, ps, lane);
+        pr.sums(R, RK, ps, slot + 1, s_newsum, lane);
+      } else {
+        pg.store(img, lane);
+        wave_sync();
+        for (int x = lane; x < RR; x += 64) {
+          if (x < R) store_elem(img, (size_t)x * ps + slot, s_st[x]);
+          else store_elem(img, (size_t)R * ps + (size_t)slot * RK + (x - R), s_st[x]);
+        }
+        wave_sync();
+        wave_page_sums(img, img + (size_t)R * ps, R, RK, ps, slot + 1, s_newsum, lane);
       }
-      wave_sync();
-      wave_page_sums(img, img + (size_t)R * ps, R, RK, ps, slot + 1, s_newsum, lane);
     } else {
-      project_query<T, D>(sP, sRd, sq, s_qc, R, RK, G, a.s.scale, tid - 64, SC_T - 64);
+      project_query<T, D>(sP, sRd, sq, s_qc, R, RK, G, a.s.scale, 1, SC_NW - 1, wave, lane);
     }
     lds_barrier();
     if (wave == 0) {
-      // the token, then the page's sums, then (quad 0) the page's score
-      T* Kp = static_cast<T*>(a.K) + ((size_t)aphys * H + g) * ps * D;
-      wave_token_store<T, D>(Lt, R, RK, ps, slot, Kp + (size_t)slot * D, Zp, Sp, lane);
+      // the page's sums, then (quad 0) the page's score
       for (int x = lane; x < RR; x += 64) a.summ[((size_t)aphys * H + g) * RR + x] = s_newsum[x];
       if (apage < npg) {
         const float cnt = (float)min(ps, n - apage * ps);
@@ -332,7 +366,7 @@ __global__ __launch_bounds__(SC_T) void score_kernel(ScoreArgs a) {
       for (int u = 0; u < NG; ++u) sv[i][u] = row[min(part + 4 * u, RR / 4 - 1)];
     }
     lds_barrier();  // every wave's direct copies are complete (waited above); the sums stay in flight
-    project_query<T, D>(sP, sRd, sq, s_qc, R, RK, G, a.s.scale, tid, SC_T);
+    project_query<T, D>(sP, sRd, sq, s_qc, R, RK, G, a.s.scale, 0, SC_NW, wave, lane);
     lds_barrier();
 #pragma unroll
     for (int i = 0; i < SC_PPL; ++i)
@@ -361,7 +395,7 @@ __global__ __launch_bounds__(SC_T) void score_kernel(ScoreArgs a) {
   } else {
     // wide sums (r + r_k > 64): a thread per page, 64 channels at a time
     lds_barrier();
-    project_query<T, D>(sP, sRd, sq, s_qc, R, RK, G, a.s.scale, tid, SC_T);
+    project_query<T, D>(sP, sRd, sq, s_qc, R, RK, G, a.s.scale, 0, SC_NW, wave, lane);
     lds_barrier();
     float d[MAX_GROUP];
     for (int j = lo + tid; j < hi; j += SC_T) {

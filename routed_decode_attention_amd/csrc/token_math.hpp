@@ -395,6 +395,101 @@ __device__ __forceinline__ void wave_page_sums(const uint16_t* Zimg, const uint1
   }
 }
 
+// wave_page_sums' operands for a bf16 page read straight from memory into
+// registers (latents [R][ps], residuals [ps][RK]; r, r_k <= 64), so that one
+// slot can take a new token's values before the sums without an LDS copy of
+// the page.  sums() applies wave_page_sums' masks and products to the same
+// operand values, so both give the same bits.
+struct PageSumRegs {
+  bf16x8 a[4][2];       // latents: channel 16 mt + n, slots 32 kc + 8 qd + 0..7
+  u32x4 h[4][2][2];     // residuals: channel 16 nt + n, slot 32 kc + 8 qd + e in h[nt][kc][e / 4][e % 4] (16-bit values)
+  __device__ __forceinline__ void load(const uint16_t* Z, const uint16_t* S, int R, int RK, int ps, int lane) {
+    const int n = lane & 15, qd = lane >> 4;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      if (16 * mt < R)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) a[mt][kc] = load_bf16x8(Z + (16 * mt + n) * ps + min(32 * kc + 8 * qd, ps - 8));
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      if (16 * nt < RK) {
+        const int cc = min(16 * nt + n, RK - 1);
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) h[nt][kc][e >> 2][e & 3] = S[min(32 * kc + 8 * qd + e, ps - 1) * RK + cc];
+      }
+  }
+  // Slot `slot` (< ps) takes st[0, R) (latents) and st[R, R + RK)
+  // (residuals), fp32 values that bf16 represents exactly.
+  __device__ __forceinline__ void put(int slot, const float* st, int R, int RK, int ps, int lane) {
+    const int n = lane & 15, qd = lane >> 4;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const int t0 = 32 * kc + 8 * qd, e = slot - t0;
+      if (t0 >= ps || e < 0 || e >= 8) continue;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        if (16 * mt < R) {
+          const uint32_t v = __float_as_uint(st[16 * mt + n]) >> 16;
+          u32x4 u = __builtin_bit_cast(u32x4, a[mt][kc]);
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            if (w == (e >> 1)) u[w] = (e & 1) ? ((u[w] & 0x0000ffffu) | (v << 16)) : ((u[w] & 0xffff0000u) | v);
+          a[mt][kc] = __builtin_bit_cast(bf16x8, u);
+        }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        if (16 * nt + n < RK) {
+          const uint32_t v = __float_as_uint(st[R + 16 * nt + n]) >> 16;
+#pragma unroll
+          for (int x = 0; x < 8; ++x)
+            if (x == e) h[nt][kc][x >> 2][x & 3] = v;
+        }
+    }
+  }
+  // The sums over slots [0, valid) into out[R + RK] (whole wave).
+  __device__ __forceinline__ void sums(int R, int RK, int ps, int valid, float* out, int lane) const {
+    const int n = lane & 15, qd = lane >> 4;
+    const u32x4 ones_u = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, ones_u);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      if (16 * mt < R) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          const int t0 = 32 * kc + 8 * qd;
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(keep_first_n(a[mt][kc], t0 < ps ? valid - t0 : 0), ones, acc,
+                                                        0, 0, 0);
+        }
+        if (n == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) out[16 * mt + 4 * qd + i] = acc[i];
+        }
+      }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      if (16 * nt < RK) {
+        const int ch = 16 * nt + n;
+        u32x4 u[2];
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int t = 32 * kc + 8 * qd + e;
+            const uint32_t kept = h[nt][kc][e >> 2][e & 3] & (0u - (uint32_t)(ch < RK && t < valid));
+            if (e & 1) u[kc][e >> 1] |= kept << 16;
+            else u[kc][e >> 1] = kept;
+          }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, __builtin_bit_cast(bf16x8, u[0]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, __builtin_bit_cast(bf16x8, u[1]), acc, 0, 0, 0);
+        if (qd == 0 && ch < RK) out[R + ch] = acc[0];
+      }
+  }
+};
+
 __device__ __forceinline__ void wave_page_sums(const float* Zimg, const float* Simg, int R, int RK, int ps,
                                                int valid, float* out, int lane) {
   for (int x = lane; x < R + RK; x += 64) {
