@@ -256,26 +256,27 @@ __device__ inline TopK topk_find(const SelectPages& pg, int nk, int ks, SelectSh
     t.cut = radix_cut(pg.keys, nk, ks, sh);
     return t;
   }
-  // 4. the boundary bin's pages, ranked among themselves by (key, page)
+  // 4. the boundary bin's pages, ranked among themselves by (key, page): as
+  // 64-bit values key << 32 | ~page, of which a larger one ranks higher
   // (the count was cleared by topk_clear)
-  uint32_t* ckey = reinterpret_cast<uint32_t*>(&sh.area[1][0][0]);
-  int* cpage = reinterpret_cast<int*>(ckey + SEL_CAND);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(&sh.area[1][0][0]);
   for (int j = tid; j < nk; j += nt)
     if (pg.bin[j] == t.bstar) {
       const uint32_t c = atomicAdd(&sh.ncand, 1u);
-      ckey[c] = pg.keys[j];
-      cpage[c] = j;
+      cand[c] = (uint64_t)pg.keys[j] << 32 | (uint32_t)~j;
     }
+  if (tid < 2) cand[nb + tid] = 0u;  // pads the list to pairs (the area holds 1024); 0 ranks below every page
   lds_barrier();
   for (int c = tid; c < nb; c += nt) {
-    const uint32_t kc = ckey[c];
-    const int jc = cpage[c];
+    const uint64_t kc = cand[c];
     int rank = 0;
-    for (int d = 0; d < nb; ++d) {
-      const uint32_t kd = ckey[d];
-      rank += kd > kc || (kd == kc && cpage[d] < jc);
+    // two candidates per 16-byte read, several reads in flight
+#pragma unroll 4
+    for (int d = 0; d < nb; d += 2) {
+      const ulonglong2 two = *reinterpret_cast<const ulonglong2*>(cand + d);
+      rank += (two.x > kc) + (two.y > kc);
     }
-    pg.pick[jc] = rank < krem;
+    pg.pick[(int)~(uint32_t)kc] = rank < krem;
   }
   lds_barrier();
   return t;
