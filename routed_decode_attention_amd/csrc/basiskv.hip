@@ -133,12 +133,13 @@ int check_dims(const basiskv_dims* d, bkv::Shape* s) {
 }
 
 struct WsLayout {
-  size_t part_acc, part_ml, z, total;
+  size_t part_acc, part_ml, z, pf_acc, pf_ml, total;
 };
 
 // Workspace: the attention splits' partials (latent sums, then max /
-// denominator pairs), then latent rows (decode batch or prefill chunk).
-// Nothing in it carries over between calls.
+// denominator pairs), then latent rows (decode batch or prefill chunk), then
+// (with prefill tokens) the prefill key ranges' partials.  Nothing in it
+// carries over between calls.
 WsLayout ws_layout(const bkv::Shape& s0, int max_prefill_tokens) {
   const bkv::Shape s = bkv::unit_shape(s0);
   const size_t pairs = (size_t)s.batch * s.n_kv_heads;
@@ -150,7 +151,10 @@ WsLayout ws_layout(const bkv::Shape& s0, int max_prefill_tokens) {
   L.z = L.part_ml + align256(splits * 2 * sizeof(float));
   size_t rows = (size_t)s.batch;
   if (max_prefill_tokens > 0 && (size_t)max_prefill_tokens > rows) rows = max_prefill_tokens;
-  L.total = L.z + align256(rows * s.n_q_heads * s.rank_v * sizeof(float));
+  L.pf_acc = L.z + align256(rows * s.n_q_heads * s.rank_v * sizeof(float));
+  const size_t pf_rows = max_prefill_tokens > 0 ? (size_t)max_prefill_tokens * s.n_q_heads * bkv::PREFILL_KSPLIT_MAX : 0;
+  L.pf_ml = L.pf_acc + align256(pf_rows * s.rank_v * sizeof(float));
+  L.total = L.pf_ml + align256(pf_rows * 2 * sizeof(float));
   return L;
 }
 
@@ -686,6 +690,9 @@ int basiskv_prefill(const basiskv_dims* dims, const basiskv_factors* f, const ba
   a.start = start_pos;
   a.n_tok = n_tok;
   a.scale_log2 = s.scale * 1.4426950408889634f;
+  bkv::plan_prefill(s, start_pos, n_tok, &a.n_ksplit, &a.split_pages);
+  a.part_acc = reinterpret_cast<float*>(static_cast<char*>(ws) + L.pf_acc);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + L.pf_ml);
   const hipError_t e = bkv::launch_prefill_attend(a, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
   return do_project(s, f, z, n_tok, out, stream);

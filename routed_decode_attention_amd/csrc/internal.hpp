@@ -133,7 +133,17 @@ struct PrefillArgs {
   float* z_out;             // [n_tok][n_q_heads][rank_v]
   int seq, start, n_tok;
   float scale_log2;
+  // the key pages split into ranges of split_pages, n_ksplit of them (1: no
+  // split, z written directly); partials [n_tok * n_q_heads][n_ksplit][rank_v]
+  // and [..][n_ksplit][2] (max, denominator), merged into z_out afterwards
+  int n_ksplit, split_pages;
+  float *part_acc, *part_ml;
 };
+constexpr int PREFILL_KSPLIT_MAX = 8;
+// Key-range splits of a prefill chunk: about 16 pages each (or
+// BASISKV_PREFILL_SPLIT_PAGES), at most PREFILL_KSPLIT_MAX; 1 where the
+// matrix-core kernel does not run.
+void plan_prefill(const Shape& s, int start, int n_tok, int* n_ksplit, int* split_pages);
 
 // Raise a kernel's dynamic-LDS limit when a launch needs more than the
 // default allows alongside its static arrays (gfx950 has 160 KiB per CU).
