@@ -517,7 +517,8 @@ def run_extras(args, names):
         extra["prefill_8k"] = pre
         log(f"prefill_8k: {pre['us_per_prompt']:.0f} us per prompt, {pre['TFLOP_per_s']} TFLOP/s "
             f"({100 * pre['frac_of_bf16_mfma_peak']:.1f}% of the bf16 matrix-core peak); attention "
-            f"{pre['attention']['TFLOP_per_s']} TFLOP/s")
+            f"{pre['attention']['TFLOP_per_s']} TFLOP/s; per chunk: writer {pre['writer']['us_per_chunk']} us, "
+            f"projection {pre['projection']['us_per_chunk']} us ({pre['projection']['TFLOP_per_s']} TFLOP/s)")
     return extra
 
 
