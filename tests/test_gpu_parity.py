@@ -553,6 +553,45 @@ def test_prefill_matches_oracle(name, chunks):
     compare_written(sc, gc.cache_host(g), ora)
 
 
+@pytest.mark.parametrize("split_pages", [1, 3])
+def test_prefill_key_range_splits(split_pages, monkeypatch):
+    """Prefill chunks whose key pages are split into many ranges (split_pages
+    pages each, at most eight ranges; ranges past a row block's last page are
+    empty and leave empty partials): against the oracle, as unsplit."""
+    monkeypatch.setenv("BASISKV_PREFILL_SPLIT_PAGES", str(split_pages))
+    print(f"[prefill splits] {split_pages} pages a range", flush=True)
+    test_prefill_matches_oracle("g8_2kv_r48_p32", [0, 77, 513])   # 17 pages of 32
+    test_prefill_matches_oracle("g4_d128_p64", [0, 128, 300])     # 5 pages of 64
+
+
+@pytest.mark.parametrize("rows,nq,r,dm", [(65, 2, 48, 256), (300, 4, 32, 512), (2048, 8, 48, 4096)])
+def test_project_many_rows(rows, nq, r, dm):
+    """The projection over many rows (the prefill chunks' LDS-staged 128 x 256
+    tiles) against the fp64 product of the same bf16 weights: rows past a
+    tile's end, a contraction of an odd number of 32-wide steps (96), the
+    8K prefill's chunk shape.  z enters as bf16 high + low parts (about 16
+    significant bits), so the product is within a few 1e-5 of the exact one."""
+    import routed_decode_attention_amd as rda
+    rng = np.random.default_rng(rows + dm)
+    kdim = nq * r
+    d = rda.Dims(batch=1, n_q_heads=nq, n_kv_heads=1, head_dim=128, rank_v=r, rank_k=16, page_size=64,
+                 d_model=dm, top_k=1, max_pages_per_seq=1, num_phys_pages=1, dtype=BF16)
+    W = synth.to_storage(rng.standard_normal((dm, kdim)) / np.sqrt(kdim), BF16)  # bf16 bits
+    z = rng.standard_normal((rows, kdim)).astype(np.float32)
+    f = rda.Factors(B=torch.zeros(128 * r, device="cuda"), P=torch.zeros(r * 128, device="cuda"),
+                    R_enc=torch.zeros(128 * 16, device="cuda"), R_dec=torch.zeros(16 * 128, device="cuda"),
+                    W_ofT=gc.dev(W, BF16))
+    out = torch.full((rows, dm), float("nan"), device="cuda")
+    print(f"[project] rows {rows} kdim {kdim} d_model {dm}", flush=True)
+    rda.basiskv_project(d, f, torch.from_numpy(z).cuda(), rows, out)
+    torch.cuda.synchronize()
+    Wf = (W.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = z.astype(np.float64) @ Wf.T
+    got = gc.host(out)
+    assert np.all(np.isfinite(got))
+    np.testing.assert_allclose(got, ref, rtol=1e-3, atol=1e-4 * np.abs(ref).max())
+
+
 def test_prefill_interleaved_with_decode_steps():
     """Serving order: sequence 0 is prefilled chunk by chunk while the other
     rows run decode steps (row 0 inactive: length 0, no append) between the
