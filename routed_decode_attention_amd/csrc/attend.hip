@@ -44,8 +44,12 @@ namespace {
 // ranks the pair's pages from the router's scores itself (select.hpp) and
 // keeps the positions [split * waves * ppw, +waves * ppw) of the selection
 // in page order, with their physical ids; split 0 also writes the selection
-// (sel, n_sel) for the caller.  Returns the selection count.
-__device__ int select_prologue(const AttendArgs& a, int pair, int split, const SelLds& L) {
+// (sel, n_sel) for the caller.  Returns the selection count.  after_issue()
+// runs once the first scores and page-table entries are requested: loads it
+// issues complete after them (in issue order), so the selection does not
+// wait for them.
+template <typename AfterIssue>
+__device__ int select_prologue(const AttendArgs& a, int pair, int split, const SelLds& L, AfterIssue&& after_issue) {
   const int b = pair / a.s.n_kv_heads, ps = a.s.page_size, maxp = a.s.max_pages;
   const int tid = threadIdx.x, nt = blockDim.x;
   const float* sc = a.scores + (size_t)pair * maxp;
@@ -65,6 +69,7 @@ __device__ int select_prologue(const AttendArgs& a, int pair, int split, const S
       s_pre[i] = sc[j];
       p_pre[i] = pt[j];
     }
+  after_issue();
   const int n = a.seq_lens[b];
   const int npg = n > 0 ? min((n + ps - 1) / ps, maxp) : 0;
   uint32_t kmax = 0u, kmin = 0xffffffffu;  // the range of the keys of pages that are not forced
@@ -101,23 +106,25 @@ __global__ __launch_bounds__(64 * ATTEND_WAVES_MAX) void attend_mfma_kernel(Atte
   const int first = (split * a.waves + wave) * a.pages_per_wave;
   const int seq_len = a.seq_lens[b];
   bf16x8 qb[KS];
-  {
+  auto load_q = [&] {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
                          ((size_t)b * a.s.n_q_heads + g * G + (n < G ? n : 0)) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s) qb[s] = n < G ? load_bf16x8(qp + 8 * qd + 32 * s) : zero_bf16x8();
-  }
+  };
   int my_j = 0, my_phys = 0, nsel;
   if constexpr (SEL) {
-    // the queries stay in flight while the workgroup selects
+    // the queries are requested after the first scores and stay in flight
+    // while the workgroup selects
     const SelLds L = sel_lds(s_acc, a.waves, G, R, a.s.max_pages, a.pages_per_wave);
-    nsel = select_prologue(a, pair, split, L);
+    nsel = select_prologue(a, pair, split, L, load_q);
     const int u = wave * a.pages_per_wave + lane;
     if (lane < a.pages_per_wave && first + lane < nsel) {
       my_j = L.mine_j[u];
       my_phys = L.mine_p[u];
     }
   } else {
+    load_q();
     // this wave's slice of the selection is read in the same round trip as
     // the sequence length and the selection count (every slot < top_k is in
     // bounds; slots past the count are masked below)
@@ -150,7 +157,19 @@ __global__ __launch_bounds__(64 * ATTEND_WAVES_MAX) void attend_mfma_kernel(Atte
   };
 
   OnlineSoftmax<D, PS, R> os;
-  if (PIPE) {  // several pages per wave: the next page's loads overlap this page's math
+  if (PIPE && np == 2) {
+    // two pages (the usual case of the plans with two pages a wave): both
+    // requested at once, in straight-line code, so that the first page's
+    // math waits only for its own loads (a conditional second request would
+    // make the compiler's waits count the second page's loads in)
+    PageFrags<D, PS, R> fa, fb;
+    fa.load(kpage(0), zpage(0), n, qd);
+    fb.load(kpage(1), zpage(1), n, qd);
+    __builtin_amdgcn_sched_barrier(0);
+    os.page(fa, qb, __builtin_amdgcn_readlane(my_cnt, 0), qd, a.scale_log2);
+    __builtin_amdgcn_sched_barrier(0);
+    os.page(fb, qb, __builtin_amdgcn_readlane(my_cnt, 1), qd, a.scale_log2);
+  } else if (PIPE) {  // several pages per wave: the next page's loads overlap this page's math
     PageFrags<D, PS, R> fa, fb;
     if (np > 0) fa.load(kpage(0), zpage(0), n, qd);
     for (int u = 0; u < np; u += 2) {
@@ -216,7 +235,7 @@ __global__ __launch_bounds__(64 * ATTEND_WAVES_MAX) void attend_valu_kernel(Atte
   int nsel;
   if constexpr (SEL) {
     L = sel_lds(s_acc, a.waves, G, R, a.s.max_pages, a.pages_per_wave);
-    nsel = select_prologue(a, pair, split, L);
+    nsel = select_prologue(a, pair, split, L, [] {});
   } else {
     nsel = seq_len > 0 ? a.n_sel[pair] : 0;
   }
