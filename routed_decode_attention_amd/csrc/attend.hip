@@ -56,19 +56,18 @@ __device__ int select_prologue(const AttendArgs& a, int pair, int split, const S
   const int32_t* pt = a.page_table + (size_t)b * maxp;
   // the first SEL_PRE strides of scores and page-table entries are requested
   // before the sequence length is known (clamped and unconditional, so that
-  // they are in flight together with it; entries past the sequence are
-  // read but not used)
+  // they are in flight together with it, and so that the compiler's waits
+  // for each stride count exactly the loads issued after it; entries past
+  // the sequence or the table are read but not used)
   constexpr int SEL_PRE = SEL_SB;
-  const int npre = min(SEL_PRE, (maxp + nt - 1) / nt);  // strides the table has (uniform)
   float s_pre[SEL_PRE];
   int32_t p_pre[SEL_PRE];
 #pragma unroll
-  for (int i = 0; i < SEL_PRE; ++i)
-    if (i < npre) {
-      const int j = min(tid + i * nt, maxp - 1);
-      s_pre[i] = sc[j];
-      p_pre[i] = pt[j];
-    }
+  for (int i = 0; i < SEL_PRE; ++i) {
+    const int j = min(tid + i * nt, maxp - 1);
+    s_pre[i] = sc[j];
+    p_pre[i] = pt[j];
+  }
   after_issue();
   const int n = a.seq_lens[b];
   const int npg = n > 0 ? min((n + ps - 1) / ps, maxp) : 0;
@@ -84,7 +83,7 @@ __device__ int select_prologue(const AttendArgs& a, int pair, int split, const S
   };
 #pragma unroll
   for (int i = 0; i < SEL_PRE; ++i)
-    if (i < npre && tid + i * nt < npg) take(tid + i * nt, s_pre[i], p_pre[i]);
+    if (tid + i * nt < npg) take(tid + i * nt, s_pre[i], p_pre[i]);
   for (int j = tid + SEL_PRE * nt; j < npg; j += nt) take(j, sc[j], pt[j]);
   return select_tail(a, pair, split, L, npg, kmax, kmin);
 }
@@ -106,11 +105,14 @@ __global__ __launch_bounds__(64 * ATTEND_WAVES_MAX) void attend_mfma_kernel(Atte
   const int first = (split * a.waves + wave) * a.pages_per_wave;
   const int seq_len = a.seq_lens[b];
   bf16x8 qb[KS];
+  // lanes of tile columns n >= G load head 0's query (unconditional loads:
+  // exact waits); the products keep every column apart and those columns
+  // are never stored
   auto load_q = [&] {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
                          ((size_t)b * a.s.n_q_heads + g * G + (n < G ? n : 0)) * D;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qb[s] = n < G ? load_bf16x8(qp + 8 * qd + 32 * s) : zero_bf16x8();
+    for (int s = 0; s < KS; ++s) qb[s] = load_bf16x8(qp + 8 * qd + 32 * s);
   };
   int my_j = 0, my_phys = 0, nsel;
   if constexpr (SEL) {
