@@ -177,6 +177,7 @@ __global__ __launch_bounds__(SC_T) void score_kernel(ScoreArgs a) {
   __shared__ __attribute__((aligned(16))) float s_st[SC_XMAX];    // the appended token's stored values
   __shared__ __attribute__((aligned(16))) float s_e[128];          // its Key remainder
   __shared__ __attribute__((aligned(16))) float s_newsum[SC_XMAX]; // its page's new sums
+  __shared__ __attribute__((aligned(16))) float s_pre[SC_XMAX];    // the sums of its page's earlier slots
   __shared__ __attribute__((aligned(16))) float s_parts[TP * (64 + 128 + 64)];  // its products' parts
 
   const int H = a.s.n_kv_heads, G = a.s.group, C = a.cluster;
@@ -253,9 +254,16 @@ __global__ __launch_bounds__(SC_T) void score_kernel(ScoreArgs a) {
     PageImage pg;
     PageSumRegs pr;
     if (wave == 0) {
-      if constexpr (BF16) pr.load(reinterpret_cast<const uint16_t*>(Zp), reinterpret_cast<const uint16_t*>(Sp), R, RK, ps,
-                                  lane);
-      else pg.load(Zp, Sp, (int)(R * ps * sizeof(T) / 16), (int)(ps * RK * sizeof(T) / 16), lane);
+      if constexpr (BF16) {
+        pr.load(reinterpret_cast<const uint16_t*>(Zp), reinterpret_cast<const uint16_t*>(Sp), R, RK, ps, lane);
+        // the page arrives before waves 1-3's copies: the sums of the slots
+        // before the token are taken meanwhile (the token's own values are
+        // added once it exists: wave_page_sums' order)
+        wait_vmem();
+        pr.prefix(R, RK, ps, slot, s_pre, lane);
+      } else {
+        pg.load(Zp, Sp, (int)(R * ps * sizeof(T) / 16), (int)(ps * RK * sizeof(T) / 16), lane);
+      }
     } else {
       wait_vmem();
     }
@@ -280,17 +288,16 @@ __global__ __launch_bounds__(SC_T) void score_kernel(ScoreArgs a) {
     lds_barrier();
     if (wave == 0) {
       token_residual_finish(Lt, R, RK, lane);
-      // the page's operands are in (long since); waiting for them here,
-      // before the token's stores, keeps the sums from waiting for the stores
-      // (vmcnt counts both in issue order)
+      // (fp32) the page image, long since in: waiting for it here, before
+      // the token's stores, keeps its use below from waiting for the stores
+      // (vmcnt counts both in issue order); bf16 waited for it above
       wait_vmem();
       wave_sync();
-      // the token's stores first: they complete while the page is summed
+      // the token's stores first: they complete while the sums are formed
       T* Kp = static_cast<T*>(a.K) + ((size_t)aphys * H + g) * ps * D;
       wave_token_store<T, D>(Lt, R, RK, ps, slot, Kp + (size_t)slot * D, Zp, Sp, lane);
       if constexpr (BF16) {
-        pr.put(slot, s_st, R, RK, ps, lane);
-        pr.sums(R, RK, ps, slot + 1, s_newsum, lane);
+        for (int x = lane; x < RR; x += 64) s_newsum[x] = s_pre[x] + s_st[x];
       } else {
         pg.store(img, lane);
         wave_sync();

@@ -322,12 +322,15 @@ __device__ __forceinline__ void wave_token_store(const TokenLds<T>& L, int R, in
   }
 }
 
-// Page sums over slots [0, valid) of a page image in LDS (storage dtype,
-// latents channel-major [R][ps], residuals [ps][RK]) into out[R + RK]
-// (whole wave).  bf16: matrix-core products with a ones operand, the page's
-// slots >= valid zeroed; latents as the A operand (16 channels x 32 slots,
-// 16 contiguous bytes per lane), residuals as the B operand (32 slots x 16
-// channels).  fp32: one lane per channel, in slot order.
+// Page sums over slots [0, valid) of a page image (storage dtype, latents
+// channel-major [R][ps], residuals [ps][RK]) into out[R + RK] (whole wave).
+// bf16: the sums of slots [0, valid - 1) as matrix-core products with a ones
+// operand (the page's slots >= valid - 1 zeroed; latents as the A operand,
+// 16 channels x 32 slots, 16 contiguous bytes per lane; residuals as the B
+// operand, 32 slots x 16 channels), then slot valid - 1 added in fp32.  So a
+// decode-step append at slot s gets the same bits from the sums of the
+// slots before it, which it can take before its own token exists, plus the
+// token.  fp32: one lane per channel, in slot order.
 __device__ __forceinline__ bf16x8 keep_first_n(bf16x8 v, int valid) {
   u32x4 u = __builtin_bit_cast(u32x4, v);
 #pragma unroll
@@ -344,6 +347,7 @@ __device__ __forceinline__ void wave_page_sums(const uint16_t* Zimg, const uint1
   const int n = lane & 15, qd = lane >> 4;
   const u32x4 ones_u = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
   const bf16x8 ones = __builtin_bit_cast(bf16x8, ones_u);
+  const int last = max(valid - 1, 0);  // slot added after the products
   // latents: every fragment of up to 4 channel tiles x 2 slot halves is read
   // first (addresses clamped into the page, out-of-range parts zeroed)
   bf16x8 a[4][2];
@@ -353,7 +357,7 @@ __device__ __forceinline__ void wave_page_sums(const uint16_t* Zimg, const uint1
     for (int kc = 0; kc < 2; ++kc) {
       const int t0 = 32 * kc + 8 * qd;
       const int row = min(16 * mt + n, R - 1), tt = min(t0, ps - 8);
-      const int keep = (16 * mt < R && t0 < ps) ? valid - t0 : 0;
+      const int keep = (16 * mt < R && t0 < ps) ? last - t0 : 0;
       a[mt][kc] = keep_first_n(*reinterpret_cast<const bf16x8*>(Zimg + row * ps + tt), keep);
     }
 #pragma unroll
@@ -365,7 +369,10 @@ __device__ __forceinline__ void wave_page_sums(const uint16_t* Zimg, const uint1
       // lane (n, qd) holds rows 4 qd + i of column n; column 0 is taken
       if (n == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) out[16 * mt + 4 * qd + i] = acc[i];
+        for (int i = 0; i < 4; ++i) {
+          const int ch = 16 * mt + 4 * qd + i;
+          out[ch] = valid > 0 ? acc[i] + bf16_to_f32(Zimg[ch * ps + last]) : acc[i];
+        }
       }
     }
   // residuals: 16-channel tiles as the B operand (32 slots x 16 channels)
@@ -382,7 +389,7 @@ __device__ __forceinline__ void wave_page_sums(const uint16_t* Zimg, const uint1
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int t = 32 * kc + 8 * qd + e;
-        const uint32_t kept = h[e] & (0u - (uint32_t)(ch < RK && t < valid));
+        const uint32_t kept = h[e] & (0u - (uint32_t)(ch < RK && t < last));
         if (e & 1) u[kc][e >> 1] |= kept << 16;
         else u[kc][e >> 1] = kept;
       }
@@ -391,15 +398,15 @@ __device__ __forceinline__ void wave_page_sums(const uint16_t* Zimg, const uint1
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, __builtin_bit_cast(bf16x8, u[0]), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, __builtin_bit_cast(bf16x8, u[1]), acc, 0, 0, 0);
     // every row of the product is the column sum; row 4 qd of column n
-    if (qd == 0 && ch < RK) out[R + ch] = acc[0];
+    if (qd == 0 && ch < RK) out[R + ch] = valid > 0 ? acc[0] + bf16_to_f32(Simg[last * RK + ch]) : acc[0];
   }
 }
 
 // wave_page_sums' operands for a bf16 page read straight from memory into
-// registers (latents [R][ps], residuals [ps][RK]; r, r_k <= 64), so that one
-// slot can take a new token's values before the sums without an LDS copy of
-// the page.  sums() applies wave_page_sums' masks and products to the same
-// operand values, so both give the same bits.
+// registers (latents [R][ps], residuals [ps][RK]; r, r_k <= 64), so that the
+// sums of the slots before a new token's slot need no LDS copy of the page.
+// prefix() applies wave_page_sums' masks and products to the same operand
+// values, so both give the same bits.
 struct PageSumRegs {
   bf16x8 a[4][2];       // latents: channel 16 mt + n, slots 32 kc + 8 qd + 0..7
   u32x4 h[4][2][2];     // residuals: channel 16 nt + n, slot 32 kc + 8 qd + e in h[nt][kc][e / 4][e % 4] (16-bit values)
@@ -420,36 +427,10 @@ struct PageSumRegs {
           for (int e = 0; e < 8; ++e) h[nt][kc][e >> 2][e & 3] = S[min(32 * kc + 8 * qd + e, ps - 1) * RK + cc];
       }
   }
-  // Slot `slot` (< ps) takes st[0, R) (latents) and st[R, R + RK)
-  // (residuals), fp32 values that bf16 represents exactly.
-  __device__ __forceinline__ void put(int slot, const float* st, int R, int RK, int ps, int lane) {
-    const int n = lane & 15, qd = lane >> 4;
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const int t0 = 32 * kc + 8 * qd, e = slot - t0;
-      if (t0 >= ps || e < 0 || e >= 8) continue;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        if (16 * mt < R) {
-          const uint32_t v = __float_as_uint(st[16 * mt + n]) >> 16;
-          u32x4 u = __builtin_bit_cast(u32x4, a[mt][kc]);
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            if (w == (e >> 1)) u[w] = (e & 1) ? ((u[w] & 0x0000ffffu) | (v << 16)) : ((u[w] & 0xffff0000u) | v);
-          a[mt][kc] = __builtin_bit_cast(bf16x8, u);
-        }
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        if (16 * nt + n < RK) {
-          const uint32_t v = __float_as_uint(st[R + 16 * nt + n]) >> 16;
-#pragma unroll
-          for (int x = 0; x < 8; ++x)
-            if (x == e) h[nt][kc][x >> 2][x & 3] = v;
-        }
-    }
-  }
-  // The sums over slots [0, valid) into out[R + RK] (whole wave).
-  __device__ __forceinline__ void sums(int R, int RK, int ps, int valid, float* out, int lane) const {
+  // The matrix-core part of wave_page_sums for a page whose slot `slot` is
+  // its last: the sums over slots [0, slot) into out[R + RK] (whole wave);
+  // the slot's own values are added to them afterwards.
+  __device__ __forceinline__ void prefix(int R, int RK, int ps, int slot, float* out, int lane) const {
     const int n = lane & 15, qd = lane >> 4;
     const u32x4 ones_u = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
     const bf16x8 ones = __builtin_bit_cast(bf16x8, ones_u);
@@ -460,7 +441,7 @@ struct PageSumRegs {
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
           const int t0 = 32 * kc + 8 * qd;
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(keep_first_n(a[mt][kc], t0 < ps ? valid - t0 : 0), ones, acc,
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(keep_first_n(a[mt][kc], t0 < ps ? slot - t0 : 0), ones, acc,
                                                         0, 0, 0);
         }
         if (n == 0) {
@@ -478,7 +459,7 @@ struct PageSumRegs {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int t = 32 * kc + 8 * qd + e;
-            const uint32_t kept = h[nt][kc][e >> 2][e & 3] & (0u - (uint32_t)(ch < RK && t < valid));
+            const uint32_t kept = h[nt][kc][e >> 2][e & 3] & (0u - (uint32_t)(ch < RK && t < slot));
             if (e & 1) u[kc][e >> 1] |= kept << 16;
             else u[kc][e >> 1] = kept;
           }
