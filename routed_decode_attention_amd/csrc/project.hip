@@ -225,10 +225,14 @@ __global__ __launch_bounds__(64 * PT_WAVES) void project_tiled_kernel(ProjectArg
 
 // Decode: the attention splits' merge and the projection in one launch.  A
 // workgroup of MP_WAVES waves owns MP_ROWS batch rows and 16 * MP_WN *
-// MP_WAVES output columns: it requests its weight fragments for the whole
-// contraction first, then merges the splits of its rows into LDS (one
-// 4-channel task per thread), then each wave multiplies its 16 x 16 tiles as
-// project_mfma_kernel does, the A operand padded to 16 rows with zeros.  The
+// MP_WAVES output columns.  The threads that merge (one 4-channel task of a
+// row each) request their rows' partials first, then every thread requests
+// its weight fragments for the whole contraction (KB steps of 32), so the
+// merge waits only for the partials while the weights are in flight; the
+// merged rows go to LDS (row stride kdim + 4 floats, so the lanes reading
+// one column of different rows hit different banks), then each wave
+// multiplies its 16 x 16 tiles as project_mfma_kernel does, the A operand
+// padded to 16 rows with zeros (lanes past MP_ROWS read nothing).  The
 // partials are re-read by every column group and the weights by every row
 // group (from L2); small tiles keep both per workgroup small.
 constexpr int MP_WAVES = 8;
@@ -237,48 +241,68 @@ constexpr int MP_WN = 1;  // 16-column tiles per wave
 constexpr int MP_COLS = 16 * MP_WN * MP_WAVES;
 constexpr int MP_KMAX = 512;  // contraction length held in registers and LDS
 
+template <int KB>
 __global__ __launch_bounds__(64 * MP_WAVES) void merge_project_kernel(MergeProjectArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float zs[];  // [16][kdim], rows past MP_ROWS zero
+  extern __shared__ __attribute__((aligned(16))) float zs[];  // [MP_ROWS][kdim + 4]
+  constexpr int KDIM = 32 * KB, ZST = KDIM + 4, QUADS = KDIM / 4;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, qd = lane >> 4;
-  const int G = a.s.group, R = a.s.rank_v, H = a.s.n_kv_heads, kdim = a.kdim;
+  const int G = a.s.group, R = a.s.rank_v, H = a.s.n_kv_heads;
   const int row0 = blockIdx.y * MP_ROWS;
   const int col = blockIdx.x * MP_COLS + wave * 16 * MP_WN + n;  // and col + 16 j
   const uint16_t* W = static_cast<const uint16_t*>(a.W);
 
-  bf16x8 bfr[MP_KMAX / 32][MP_WN];
-#pragma unroll
-  for (int kb = 0; kb < MP_KMAX / 32; ++kb)
-    if (32 * kb < kdim) {
-#pragma unroll
-      for (int j = 0; j < MP_WN; ++j) bfr[kb][j] = load_bf16x8(W + (size_t)(col + 16 * j) * kdim + 32 * kb + 8 * qd);
-    }
-
-  // z rows: z[b][hq * R + r] is head h = hq % G of pair (b, hq / G)
-  const int quads = kdim / 4;
-  for (int t = threadIdx.x; t < 16 * quads; t += blockDim.x) {
-    const int row = t / quads, k = 4 * (t % quads);
-    const int b = row0 + row, hq = k / R, r0 = k % R;
-    f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    if (row < MP_ROWS && b < a.rows) {
-      const size_t pair = (size_t)b * H + hq / G;
-      z = merge_splits4(a.part_acc + pair * a.n_wsplit * G * R, a.part_ml + pair * a.n_wsplit * G * 2,
-                        a.n_wsplit, G, R, hq % G, r0);
-      if (a.z_out && blockIdx.x == 0) *reinterpret_cast<f32x4*>(a.z_out + (size_t)b * kdim + k) = z;
-    }
-    *reinterpret_cast<f32x4*>(zs + row * kdim + k) = z;
+  // z rows: z[b][hq * R + r] is head h = hq % G of pair (b, hq / G); thread t
+  // < MP_ROWS * QUADS merges row t / QUADS, channels 4 (t % QUADS) ..
+  const int t = threadIdx.x, row = t / QUADS, k = 4 * (t % QUADS);
+  const int b = row0 + row;
+  const bool merger = t < MP_ROWS * QUADS && b < a.rows;
+  SplitMerge m{nullptr, nullptr, a.n_wsplit, G, R, 0, 0};
+  if (merger) {
+    const int hq = k / R;
+    const size_t pair = (size_t)b * H + hq / G;
+    m.acc = a.part_acc + pair * a.n_wsplit * G * R;
+    m.ml = a.part_ml + pair * a.n_wsplit * G * 2;
+    m.h = hq % G;
+    m.r0 = k % R;
+    m.load(0);
   }
-  __syncthreads();
+  bf16x8 bfr[KB][MP_WN];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int j = 0; j < MP_WN; ++j) bfr[kb][j] = load_bf16x8(W + (size_t)(col + 16 * j) * KDIM + 32 * kb + 8 * qd);
+  if (merger) {
+    __builtin_amdgcn_sched_barrier(0);
+    m.fold(0);
+    for (int s0 = MERGE_CHUNK; s0 < a.n_wsplit; s0 += MERGE_CHUNK) {
+      m.load(s0);
+      __builtin_amdgcn_sched_barrier(0);
+      m.fold(s0);
+    }
+    const f32x4 z = m.finish();
+    if (a.z_out && blockIdx.x == 0) *reinterpret_cast<f32x4*>(a.z_out + (size_t)b * KDIM + k) = z;
+    *reinterpret_cast<f32x4*>(zs + row * ZST + k) = z;
+  } else if (t < MP_ROWS * QUADS) {
+    *reinterpret_cast<f32x4*>(zs + row * ZST + k) = f32x4{0.f, 0.f, 0.f, 0.f};  // rows past the batch
+  }
+  lds_barrier();
 
   f32x4 acc[MP_WN];
 #pragma unroll
   for (int j = 0; j < MP_WN; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kb = 0; kb < MP_KMAX / 32; ++kb) {
-    if (32 * kb >= kdim) break;
-    const float* zp = zs + n * kdim + 32 * kb + 8 * qd;
-    const f32x4 lo4 = *reinterpret_cast<const f32x4*>(zp), hi4 = *reinterpret_cast<const f32x4*>(zp + 4);
-    const float x[8] = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+  for (int kb = 0; kb < KB; ++kb) {
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (n < MP_ROWS) {
+      const float* zp = zs + n * ZST + 32 * kb + 8 * qd;
+      const f32x4 lo4 = *reinterpret_cast<const f32x4*>(zp), hi4 = *reinterpret_cast<const f32x4*>(zp + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = lo4[e];
+        x[4 + e] = hi4[e];
+      }
+    }
     bf16x8 af, al;
     split_bf16x8(x, af, al);
 #pragma unroll
@@ -291,10 +315,10 @@ __global__ __launch_bounds__(64 * MP_WAVES) void merge_project_kernel(MergeProje
   if (4 * qd < MP_ROWS) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int row = row0 + 4 * qd + e;
-      if (4 * qd + e < MP_ROWS && row < a.rows) {
+      const int r = row0 + 4 * qd + e;
+      if (4 * qd + e < MP_ROWS && r < a.rows) {
 #pragma unroll
-        for (int j = 0; j < MP_WN; ++j) a.out[(size_t)row * a.n + col + 16 * j] = acc[j][e];
+        for (int j = 0; j < MP_WN; ++j) a.out[(size_t)r * a.n + col + 16 * j] = acc[j][e];
       }
     }
   }
@@ -325,10 +349,34 @@ bool merge_project_supported(const Shape& s) {
   return !off && s.dtype == 1 && kdim % 32 == 0 && kdim <= MP_KMAX && s.d_model % MP_COLS == 0;
 }
 
+template <int KB>
+void launch_mp(const MergeProjectArgs& a, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL(merge_project_kernel<KB>, grid, dim3(64 * MP_WAVES), (size_t)MP_ROWS * (32 * KB + 4) * sizeof(float),
+                     st, a);
+}
+
 hipError_t launch_merge_project(const MergeProjectArgs& a, hipStream_t st) {
   if (a.rows <= 0) return hipSuccess;
   const dim3 grid(a.n / MP_COLS, (a.rows + MP_ROWS - 1) / MP_ROWS);
-  hipLaunchKernelGGL(merge_project_kernel, grid, dim3(64 * MP_WAVES), (size_t)16 * a.kdim * sizeof(float), st, a);
+  switch (a.kdim / 32) {  // merge_project_supported: kdim % 32 == 0, kdim <= MP_KMAX
+    case 1: launch_mp<1>(a, grid, st); break;
+    case 2: launch_mp<2>(a, grid, st); break;
+    case 3: launch_mp<3>(a, grid, st); break;
+    case 4: launch_mp<4>(a, grid, st); break;
+    case 5: launch_mp<5>(a, grid, st); break;
+    case 6: launch_mp<6>(a, grid, st); break;
+    case 7: launch_mp<7>(a, grid, st); break;
+    case 8: launch_mp<8>(a, grid, st); break;
+    case 9: launch_mp<9>(a, grid, st); break;
+    case 10: launch_mp<10>(a, grid, st); break;
+    case 11: launch_mp<11>(a, grid, st); break;
+    case 12: launch_mp<12>(a, grid, st); break;
+    case 13: launch_mp<13>(a, grid, st); break;
+    case 14: launch_mp<14>(a, grid, st); break;
+    case 15: launch_mp<15>(a, grid, st); break;
+    case 16: launch_mp<16>(a, grid, st); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
