@@ -172,7 +172,8 @@ int basiskv_fold_output(const basiskv_dims *dims, const float *B, const void *W_
  * k, z~ and s~ go to slot p % page_size of page page_table[seq][p / page_size].
  * Then each touched page's sums are set to the fp32 sums of its stored
  * latents and residuals over slots [0, last written slot] (fp32 storage: in
- * slot order; bf16: on the matrix cores, the same way for appends and chunks).
+ * slot order; bf16: the slots before the last on the matrix cores, then the
+ * last slot added, the same way for appends and chunks).
  * The caller maps the pages first.  k, v: [n_tok][n_kv_heads][head_dim] dtype.
  */
 int basiskv_write(const basiskv_dims *dims, const basiskv_factors *f,
