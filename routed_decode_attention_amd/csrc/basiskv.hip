@@ -247,7 +247,9 @@ int do_project(const bkv::Shape& s, const basiskv_factors* f, const float* z, in
 int merge_project(const bkv::Shape& s, const basiskv_factors* f, void* ws, const WsLayout& L, int n_wsplit,
                   float* z, float* z_out, float* out, void* stream) {
   char* w = static_cast<char*>(ws);
-  const bool fused = n_wsplit > 1 && s.batch <= 16 && bkv::merge_project_supported(s);
+  const bool small = s.batch <= 16 && bkv::merge_project_supported(s);
+  const bool rows16 = !small && bkv::merge_project_rows_supported(s);  // 16-row tiles
+  const bool fused = n_wsplit > 1 && (small || rows16);
   if (!fused) {
     if (n_wsplit > 1) {
       bkv::MergeArgs m;
@@ -272,7 +274,8 @@ int merge_project(const bkv::Shape& s, const basiskv_factors* f, void* ws, const
   m.rows = s.batch;
   m.kdim = s.n_q_heads * s.rank_v;
   m.n = s.d_model;
-  const hipError_t e = bkv::launch_merge_project(m, as_stream(stream));
+  const hipError_t e = rows16 ? bkv::launch_merge_project_rows(m, as_stream(stream))
+                              : bkv::launch_merge_project(m, as_stream(stream));
   return e == hipSuccess ? BASISKV_OK : hip_fail(e, "merge-projection launch");
 }
 

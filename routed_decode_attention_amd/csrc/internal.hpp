@@ -173,6 +173,8 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
 bool merge_project_supported(const Shape& s);
 hipError_t launch_merge_project(const MergeProjectArgs& a, hipStream_t st);
+bool merge_project_rows_supported(const Shape& s);  // beyond 16 rows: 16-row tiles
+hipError_t launch_merge_project_rows(const MergeProjectArgs& a, hipStream_t st);
 hipError_t launch_project(const ProjectArgs& a, hipStream_t st);
 hipError_t launch_prefill_attend(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_zero_u32(unsigned* p, size_t n, hipStream_t st);

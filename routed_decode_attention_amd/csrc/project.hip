@@ -349,10 +349,124 @@ bool merge_project_supported(const Shape& s) {
   return !off && s.dtype == 1 && kdim % 32 == 0 && kdim <= MP_KMAX && s.d_model % MP_COLS == 0;
 }
 
+// Beyond 16 rows: the same with a whole 16-row tile of real rows per
+// workgroup (16 rows x 128 columns), so the weights are read by every row
+// tile and the partials re-merged by every column group; each thread merges
+// TPT 4-channel tasks, all their partials requested before the weights.
+constexpr int MR_ROWS = 16;
+constexpr int MR_KMAX = 256;  // the merged rows' registers: two tasks a thread at most
+
+template <int KB>
+__global__ __launch_bounds__(64 * MP_WAVES) void merge_project_rows_kernel(MergeProjectArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float zs[];  // [MR_ROWS][kdim + 4]
+  constexpr int KDIM = 32 * KB, ZST = KDIM + 4, QUADS = KDIM / 4;
+  constexpr int TASKS = MR_ROWS * QUADS, TPT = (TASKS + 64 * MP_WAVES - 1) / (64 * MP_WAVES);
+  static_assert(TPT <= 2, "contraction too long for the row-tile merge");
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, qd = lane >> 4;
+  const int G = a.s.group, R = a.s.rank_v, H = a.s.n_kv_heads;
+  const int row0 = blockIdx.y * MR_ROWS;
+  const int col = blockIdx.x * MP_COLS + wave * 16 * MP_WN + n;
+  const uint16_t* W = static_cast<const uint16_t*>(a.W);
+
+  // task u = threadIdx.x + 512 i: row u / QUADS, channels 4 (u % QUADS) ..;
+  // eight splits requested together (the long-context plans' split counts)
+  using SM = SplitMergeT<8>;
+  SM m[TPT];
+  bool merger[TPT];
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    const int u = threadIdx.x + 64 * MP_WAVES * i, row = u / QUADS, k = 4 * (u % QUADS), b = row0 + row;
+    merger[i] = u < TASKS && b < a.rows;
+    m[i] = SM{nullptr, nullptr, a.n_wsplit, G, R, 0, 0};
+    if (merger[i]) {
+      const int hq = k / R;
+      const size_t pair = (size_t)b * H + hq / G;
+      m[i].acc = a.part_acc + pair * a.n_wsplit * G * R;
+      m[i].ml = a.part_ml + pair * a.n_wsplit * G * 2;
+      m[i].h = hq % G;
+      m[i].r0 = k % R;
+      m[i].load(0);
+    }
+  }
+  bf16x8 bfr[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) bfr[kb] = load_bf16x8(W + (size_t)col * KDIM + 32 * kb + 8 * qd);
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    const int u = threadIdx.x + 64 * MP_WAVES * i, row = u / QUADS, k = 4 * (u % QUADS), b = row0 + row;
+    if (merger[i]) {
+      __builtin_amdgcn_sched_barrier(0);
+      m[i].fold(0);
+      for (int s0 = SM::MERGE_CHUNK; s0 < a.n_wsplit; s0 += SM::MERGE_CHUNK) {
+        m[i].load(s0);
+        __builtin_amdgcn_sched_barrier(0);
+        m[i].fold(s0);
+      }
+      const f32x4 z = m[i].finish();
+      if (a.z_out && blockIdx.x == 0) *reinterpret_cast<f32x4*>(a.z_out + (size_t)b * KDIM + k) = z;
+      *reinterpret_cast<f32x4*>(zs + row * ZST + k) = z;
+    } else if (u < TASKS) {
+      *reinterpret_cast<f32x4*>(zs + row * ZST + k) = f32x4{0.f, 0.f, 0.f, 0.f};  // rows past the batch
+    }
+  }
+  lds_barrier();
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const float* zp = zs + n * ZST + 32 * kb + 8 * qd;
+    const f32x4 lo4 = *reinterpret_cast<const f32x4*>(zp), hi4 = *reinterpret_cast<const f32x4*>(zp + 4);
+    const float x[8] = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    bf16x8 af, al;
+    split_bf16x8(x, af, al);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[kb], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bfr[kb], acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = row0 + 4 * qd + e;
+    if (r < a.rows) a.out[(size_t)r * a.n + col] = acc[e];
+  }
+}
+
+template <int KB>
+void launch_mr(const MergeProjectArgs& a, hipStream_t st) {
+  const dim3 grid(a.n / MP_COLS, (a.rows + MR_ROWS - 1) / MR_ROWS);
+  hipLaunchKernelGGL(merge_project_rows_kernel<KB>, grid, dim3(64 * MP_WAVES),
+                     (size_t)MR_ROWS * (32 * KB + 4) * sizeof(float), st, a);
+}
+
 template <int KB>
 void launch_mp(const MergeProjectArgs& a, dim3 grid, hipStream_t st) {
   hipLaunchKernelGGL(merge_project_kernel<KB>, grid, dim3(64 * MP_WAVES), (size_t)MP_ROWS * (32 * KB + 4) * sizeof(float),
                      st, a);
+}
+
+bool merge_project_rows_supported(const Shape& s) {
+  // BASISKV_MERGE_PROJECT_ROWS=0: beyond 16 rows the separate merge and
+  // projection instead (a tuning override)
+  static const bool off = [] {
+    const char* e = getenv("BASISKV_MERGE_PROJECT_ROWS");
+    return e && e[0] == '0';
+  }();
+  return !off && merge_project_supported(s) && s.n_q_heads * s.rank_v <= MR_KMAX;
+}
+
+hipError_t launch_merge_project_rows(const MergeProjectArgs& a, hipStream_t st) {
+  if (a.rows <= 0) return hipSuccess;
+  switch (a.kdim / 32) {  // merge_project_rows_supported: kdim % 32 == 0, kdim <= MR_KMAX
+    case 1: launch_mr<1>(a, st); break;
+    case 2: launch_mr<2>(a, st); break;
+    case 3: launch_mr<3>(a, st); break;
+    case 4: launch_mr<4>(a, st); break;
+    case 5: launch_mr<5>(a, st); break;
+    case 6: launch_mr<6>(a, st); break;
+    case 7: launch_mr<7>(a, st); break;
+    case 8: launch_mr<8>(a, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_merge_project(const MergeProjectArgs& a, hipStream_t st) {

@@ -20,7 +20,11 @@ constexpr int MERGE_CHUNK = 16;  // splits whose partials are requested together
 // splits are taken in chunks of MERGE_CHUNK whose loads are issued together
 // (load), then folded into a running (M, L, A) rescaled to each chunk's new
 // max, splits in order within a chunk (fold); finish() normalises.
-struct SplitMerge {
+// (CH: splits requested together, MERGE_CHUNK unless a kernel needs fewer
+// registers for it.)
+template <int CH>
+struct SplitMergeT {
+  static constexpr int MERGE_CHUNK = CH;
   const float *acc, *ml;
   int nws, G, R, h, r0;
   float M = -__builtin_huge_valf(), L = 0.f;
@@ -67,6 +71,8 @@ struct SplitMerge {
     return z;
   }
 };
+
+using SplitMerge = SplitMergeT<MERGE_CHUNK>;
 
 __device__ __forceinline__ f32x4 merge_splits4(const float* acc, const float* ml, int nws, int G, int R, int h,
                                                int r0) {
