@@ -236,10 +236,13 @@ def time_launches(fn, n):
 
 
 def mp_kernels(w) -> str:
-    """The kernel(s) of the split merge and the projection: fused at one MFMA
-    row tile (16 rows, the library's rule), the merge kernel and the
-    projection kernel beyond."""
-    return "merge_project_kernel" if w.batch <= 16 else "merge_kernel+project_mfma_kernel"
+    """The kernel(s) of the split merge and the projection, by the library's
+    rule: fused with 2-row groups up to one MFMA row tile (16 rows), fused with
+    16-row tiles beyond while the contraction (query heads x r) is at most
+    256, else the merge kernel and the projection kernel."""
+    if w.batch <= 16:
+        return "merge_project_kernel"
+    return "merge_project_rows_kernel" if w.n_q_heads * w.rank_v <= 256 else "merge_kernel+project_mfma_kernel"
 
 
 def decode_kernels(st, launches):
