@@ -240,10 +240,11 @@ int do_project(const bkv::Shape& s, const basiskv_factors* f, const float* z, in
 // After the attention (n_wsplit splits per unit, partials at L in ws, or
 // with one split the latents already in z): the merge of the splits and the
 // output projection.  The fused merge-projection re-merges a row's splits in
-// every column group and re-reads the weights in every row group: it wins at
-// one MFMA row tile (16 rows), the separate merge and projection beyond
-// (measured: 70B 128K share 62.8 against 75.7 us per step, ragged mix 48.0
-// against 54.9).  s: the unit shape.
+// every column group and re-reads the weights in every row group: up to one
+// MFMA row tile (16 rows) in groups of 2 rows, beyond in whole 16-row tiles
+// (measured against the separate merge and projection: 70B 128K share 41.2
+// against 42.2 us per step, ragged mix 35.7 against 38.2), which contractions
+// over 256 still take.  s: the unit shape.
 int merge_project(const bkv::Shape& s, const basiskv_factors* f, void* ws, const WsLayout& L, int n_wsplit,
                   float* z, float* z_out, float* out, void* stream) {
   char* w = static_cast<char*>(ws);
