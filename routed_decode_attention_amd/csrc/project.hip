@@ -351,16 +351,17 @@ bool merge_project_supported(const Shape& s) {
 
 // Beyond 16 rows: the same with a whole 16-row tile of real rows per
 // workgroup (16 rows x 128 columns), so the weights are read by every row
-// tile and the partials re-merged by every column group; each thread merges
-// TPT 4-channel tasks, all their partials requested before the weights.
+// tile and the partials re-merged by every column group; NW waves, each
+// thread merging TPT 4-channel tasks with all their partials requested before
+// the weights, the first MP_WAVES waves then multiplying.
 constexpr int MR_ROWS = 16;
 constexpr int MR_KMAX = 256;  // the merged rows' registers: two tasks a thread at most
 
-template <int KB>
-__global__ __launch_bounds__(64 * MP_WAVES) void merge_project_rows_kernel(MergeProjectArgs a) {
+template <int KB, int NW>
+__global__ __launch_bounds__(64 * NW) void merge_project_rows_kernel(MergeProjectArgs a) {
   extern __shared__ __attribute__((aligned(16))) float zs[];  // [MR_ROWS][kdim + 4]
   constexpr int KDIM = 32 * KB, ZST = KDIM + 4, QUADS = KDIM / 4;
-  constexpr int TASKS = MR_ROWS * QUADS, TPT = (TASKS + 64 * MP_WAVES - 1) / (64 * MP_WAVES);
+  constexpr int TASKS = MR_ROWS * QUADS, TPT = (TASKS + 64 * NW - 1) / (64 * NW);
   static_assert(TPT <= 2, "contraction too long for the row-tile merge");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, qd = lane >> 4;
@@ -376,7 +377,7 @@ __global__ __launch_bounds__(64 * MP_WAVES) void merge_project_rows_kernel(Merge
   bool merger[TPT];
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {
-    const int u = threadIdx.x + 64 * MP_WAVES * i, row = u / QUADS, k = 4 * (u % QUADS), b = row0 + row;
+    const int u = threadIdx.x + 64 * NW * i, row = u / QUADS, k = 4 * (u % QUADS), b = row0 + row;
     merger[i] = u < TASKS && b < a.rows;
     m[i] = SM{nullptr, nullptr, a.n_wsplit, G, R, 0, 0};
     if (merger[i]) {
@@ -389,12 +390,15 @@ __global__ __launch_bounds__(64 * MP_WAVES) void merge_project_rows_kernel(Merge
       m[i].load(0);
     }
   }
+  // (waves past MP_WAVES only merge)
   bf16x8 bfr[KB];
+  if (wave < MP_WAVES) {
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) bfr[kb] = load_bf16x8(W + (size_t)col * KDIM + 32 * kb + 8 * qd);
+    for (int kb = 0; kb < KB; ++kb) bfr[kb] = load_bf16x8(W + (size_t)col * KDIM + 32 * kb + 8 * qd);
+  }
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {
-    const int u = threadIdx.x + 64 * MP_WAVES * i, row = u / QUADS, k = 4 * (u % QUADS), b = row0 + row;
+    const int u = threadIdx.x + 64 * NW * i, row = u / QUADS, k = 4 * (u % QUADS), b = row0 + row;
     if (merger[i]) {
       __builtin_amdgcn_sched_barrier(0);
       m[i].fold(0);
@@ -411,6 +415,7 @@ __global__ __launch_bounds__(64 * MP_WAVES) void merge_project_rows_kernel(Merge
     }
   }
   lds_barrier();
+  if (wave >= MP_WAVES) return;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -433,8 +438,17 @@ __global__ __launch_bounds__(64 * MP_WAVES) void merge_project_rows_kernel(Merge
 template <int KB>
 void launch_mr(const MergeProjectArgs& a, hipStream_t st) {
   const dim3 grid(a.n / MP_COLS, (a.rows + MR_ROWS - 1) / MR_ROWS);
-  hipLaunchKernelGGL(merge_project_rows_kernel<KB>, grid, dim3(64 * MP_WAVES),
-                     (size_t)MR_ROWS * (32 * KB + 4) * sizeof(float), st, a);
+  // sixteen waves: one merge task a thread at contractions up to 256 (the
+  // last eight waves only merge); measured 7.8-8.0 against 8.25 us at the
+  // 70B 128K share, 5.3-5.5 against 5.6 at the ragged mix.
+  // BASISKV_MR_WAVES=8 overrides (a tuning override)
+  static const int nw = [] {
+    const char* e = getenv("BASISKV_MR_WAVES");
+    return e && atoi(e) == 8 ? 8 : 16;
+  }();
+  const size_t lds = (size_t)MR_ROWS * (32 * KB + 4) * sizeof(float);
+  if (nw == 16) hipLaunchKernelGGL((merge_project_rows_kernel<KB, 16>), grid, dim3(64 * 16), lds, st, a);
+  else hipLaunchKernelGGL((merge_project_rows_kernel<KB, 8>), grid, dim3(64 * 8), lds, st, a);
 }
 
 template <int KB>
