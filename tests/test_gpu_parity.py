@@ -74,14 +74,19 @@ CASES = {
     "g4_2kv_r48_k384": (small("k384", 213, batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, page_size=64,
                               rank_v=48, rank_k=16, top_k=12, d_model=256, dtype=BF16, ctx=1500),
                         [1500, 700]),
-    # batches past one MFMA row tile: the separate split merge and the decode
-    # projection holding two and three row tiles per wave
+    # batches past one MFMA row tile: the merge-projection in 16-row tiles,
+    # the last tile partly filled (24 and 40 rows)
     "b24_rows": (small("b24", 214, batch=24, n_q_heads=8, n_kv_heads=2, head_dim=128, page_size=64, rank_v=32,
                        rank_k=16, top_k=6, d_model=256, dtype=BF16, ctx=700),
                  [(53 * i + 17) % 700 + 1 for i in range(24)]),
     "b40_rows": (small("b40", 215, batch=40, n_q_heads=4, n_kv_heads=1, head_dim=128, page_size=32, rank_v=32,
                        rank_k=16, top_k=9, d_model=128, dtype=BF16, ctx=900),
                  [(71 * i + 5) % 900 + 1 for i in range(40)]),
+    # 16-row tiles with more attention splits (10) than the row-tile merge
+    # requests together (8), and ragged lengths below top_k pages
+    "b20_k40": (small("b20", 216, batch=20, n_q_heads=4, n_kv_heads=1, head_dim=128, page_size=64, rank_v=32,
+                      rank_k=16, top_k=40, d_model=128, dtype=BF16, ctx=3000),
+                [(97 * i + 13) % 3000 + 1 for i in range(20)]),
     "ragged_permuted": (configs.get("ragged_mix").with_(name="rg", cfg_id=206, batch=5,
                                                         length_range=(1, 3000), top_k=16,
                                                         d_model=256),
