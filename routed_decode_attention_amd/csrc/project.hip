@@ -357,6 +357,8 @@ bool merge_project_supported(const Shape& s) {
 constexpr int MR_ROWS = 16;
 constexpr int MR_KMAX = 256;  // the merged rows' registers: two tasks a thread at most
 
+namespace {
+
 template <int KB, int NW>
 __global__ __launch_bounds__(64 * NW) void merge_project_rows_kernel(MergeProjectArgs a) {
   extern __shared__ __attribute__((aligned(16))) float zs[];  // [MR_ROWS][kdim + 4]
@@ -434,6 +436,8 @@ __global__ __launch_bounds__(64 * NW) void merge_project_rows_kernel(MergeProjec
     if (r < a.rows) a.out[(size_t)r * a.n + col] = acc[e];
   }
 }
+
+}  // namespace
 
 template <int KB>
 void launch_mr(const MergeProjectArgs& a, hipStream_t st) {
